@@ -1,0 +1,281 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each pin takes the loaded oracle library and raises AssertionError on a
+mismatch.  The pytest file runs every pin on the real oracle, and runs the
+whole battery on deliberately broken copies of oracle.c to show that each
+plausible mistake is caught by at least one pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from tests import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def _close(a, b, rtol=1e-10, atol=1e-12, what=""):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    if a.shape != b.shape or not np.allclose(a, b, rtol=rtol, atol=atol):
+        err = np.max(np.abs(a - b)) if a.shape == b.shape else "shape"
+        raise AssertionError(f"{what}: mismatch (max abs err {err})")
+
+
+def _bits(x) -> np.ndarray:
+    x = np.asarray(x, np.float32)
+    b = W.f32_to_bf16_bits(x).reshape(x.shape)
+    assert np.array_equal(W.bf16_bits_to_f32(b).reshape(x.shape), x), "fixture value not exact in bf16"
+    return b
+
+
+# --------------------------------------------------------------------- golden closed forms
+def pin_golden_closed_forms(lib):
+    with open(GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    env = {"e": math.e, "__builtins__": {}}
+    for c in cases:
+        q = _bits(c["q"])[None]                # [1, Hq, D]
+        k = _bits(c["k"])[None]                # [1, Hkv, S, D]
+        v = _bits(c["v"])[None]
+        lens = np.array([c["len"]], np.int32)
+        out = oracle.decode(q, k, v, lens, c["scale"], lib=lib)[0]
+        exp = np.array([[eval(s, env) for s in row] for row in c["expected"]], np.float64)
+        _close(out, exp, what=c["name"])
+
+
+# --------------------------------------------------------------------- library special case
+def _sdpa_reference(case: W.Case) -> np.ndarray:
+    """torch scaled_dot_product_attention (CPU, float64), heads repeated per kv head."""
+    q = torch.from_numpy(W.bf16_bits_to_f32(case.q).reshape(case.q.shape).astype(np.float64))
+    k = torch.from_numpy(W.bf16_bits_to_f32(case.k).reshape(case.k.shape).astype(np.float64))
+    v = torch.from_numpy(W.bf16_bits_to_f32(case.v).reshape(case.v.shape).astype(np.float64))
+    out = np.zeros((case.B, case.Hq, case.D))
+    for b in range(case.B):
+        n = int(case.seq_lens[b])
+        if n == 0:
+            continue
+        kb = k[b, :, :n].repeat_interleave(case.G, dim=0)[None]   # [1, Hq, n, D]
+        vb = v[b, :, :n].repeat_interleave(case.G, dim=0)[None]
+        qb = q[b][None, :, None, :]                               # [1, Hq, 1, D]
+        o = torch.nn.functional.scaled_dot_product_attention(qb, kb, vb, scale=case.scale)
+        out[b] = o[0, :, 0, :].numpy()
+    return out
+
+
+def pin_torch_sdpa(lib):
+    cases = [
+        W.contig_case(1, 8, 2, 64, 96, seed=1),
+        W.contig_case(2, 6, 1, 128, 77, seq_lens=[77, 40], seed=2),
+        W.contig_case(3, 12, 3, 32, 33, seq_lens=[1, 33, 17], seed=3),
+        W.contig_case(1, 24, 4, 256, 64, seed=4, scale=1.0 / 16),
+        W.contig_case(2, 4, 4, 16, 20, seq_lens=[20, 0], seed=5),
+    ]
+    for c in cases:
+        _close(oracle.decode(c.q, c.k, c.v, c.seq_lens, c.scale, lib=lib), _sdpa_reference(c),
+               what=f"sdpa B={c.B} Hq={c.Hq} Hkv={c.Hkv} D={c.D}")
+
+
+# --------------------------------------------------------------------- brute force
+def pin_brute_force(lib):
+    """Pure-Python softmax with correctly rounded sums (math.fsum) on tiny inputs."""
+    c = W.contig_case(2, 4, 2, 8, 6, seq_lens=[6, 3], seed=7, scale=0.37)
+    q = W.bf16_bits_to_f32(c.q).reshape(c.q.shape).astype(float)
+    k = W.bf16_bits_to_f32(c.k).reshape(c.k.shape).astype(float)
+    v = W.bf16_bits_to_f32(c.v).reshape(c.v.shape).astype(float)
+    exp = np.zeros((c.B, c.Hq, c.D))
+    for b in range(c.B):
+        n = int(c.seq_lens[b])
+        for h in range(c.Hq):
+            kv = h // c.G
+            s = [c.scale * math.fsum(q[b, h, d] * k[b, kv, t, d] for d in range(c.D))
+                 for t in range(n)]
+            z = [math.exp(x) for x in s]
+            Z = math.fsum(z)
+            for d in range(c.D):
+                exp[b, h, d] = math.fsum(z[t] * v[b, kv, t, d] for t in range(n)) / Z
+    _close(oracle.decode(c.q, c.k, c.v, c.seq_lens, c.scale, lib=lib), exp, what="brute force")
+
+
+# --------------------------------------------------------------------- closed-form invariants
+def pin_len_one_is_v0(lib):
+    c = W.contig_case(2, 8, 2, 64, 5, seq_lens=[1, 1], seed=8)
+    out = oracle.decode(c.q, c.k, c.v, c.seq_lens, c.scale, lib=lib)
+    v0 = W.bf16_bits_to_f32(c.v[:, :, 0, :]).reshape(c.B, c.Hkv, c.D).astype(np.float64)
+    exp = np.repeat(v0, c.G, axis=1)
+    if not np.array_equal(out, exp):
+        raise AssertionError("len=1 must return V[0] exactly")
+
+
+def pin_uniform_weights_give_mean(lib):
+    """Identical keys, q = 0 or scale = 0 all give the plain mean of V[0:len]."""
+    base = W.contig_case(1, 4, 2, 32, 40, seq_lens=[37], seed=9)
+    vf = W.bf16_bits_to_f32(base.v).reshape(base.v.shape).astype(np.float64)
+    mean = np.repeat(vf[0, :, :37, :].mean(axis=1), base.G, axis=0)[None]
+    same_k = base.k.copy()
+    same_k[:, :, :, :] = base.k[:, :, :1, :]
+    _close(oracle.decode(base.q, same_k, base.v, base.seq_lens, base.scale, lib=lib), mean,
+           what="identical keys")
+    _close(oracle.decode(np.zeros_like(base.q), base.k, base.v, base.seq_lens, base.scale, lib=lib),
+           mean, what="q = 0")
+    _close(oracle.decode(base.q, base.k, base.v, base.seq_lens, 0.0, lib=lib), mean,
+           what="scale = 0")
+
+
+def pin_dominant_key(lib):
+    """One score above every other by >= 60 returns that row of V (within n e^-60)."""
+    c = W.contig_case(1, 2, 1, 16, 50, seed=10, scale=1.0)
+    q = np.zeros_like(c.q)
+    q[0, :, 0] = _bits([4.0])[0]
+    k = np.zeros_like(c.k)
+    k[0, 0, :, 0] = _bits((np.arange(50) % 9 - 4).astype(np.float32) / 4)
+    k[0, 0, 23, 0] = _bits([16.0])[0]            # score 64, others <= 4
+    out = oracle.decode(q, k, c.v, c.seq_lens, c.scale, lib=lib)
+    v23 = W.bf16_bits_to_f32(c.v[0, 0, 23]).astype(np.float64)
+    _close(out[0, 0], v23, rtol=0, atol=50 * math.exp(-60) * 10, what="dominant key")
+    _close(out[0, 1], v23, rtol=0, atol=50 * math.exp(-60) * 10, what="dominant key")
+
+
+def pin_scale_moves_into_q(lib):
+    """(2q, scale/2) equals (q, scale) exactly: the scale multiplies the dot product."""
+    c = W.contig_case(1, 8, 2, 64, 64, seed=11)
+    qf = W.bf16_bits_to_f32(c.q).reshape(c.q.shape)
+    q2 = W.f32_to_bf16_bits(qf * np.float32(2)).reshape(c.q.shape)
+    a = oracle.decode(c.q, c.k, c.v, c.seq_lens, c.scale, lib=lib)
+    b = oracle.decode(q2, c.k, c.v, c.seq_lens, c.scale / 2, lib=lib)
+    if not np.array_equal(a, b):
+        raise AssertionError("(2q, scale/2) must equal (q, scale)")
+    c3 = oracle.decode(c.q, c.k, c.v, c.seq_lens, c.scale * 2, lib=lib)
+    if np.allclose(a, c3, rtol=1e-6, atol=1e-9):
+        raise AssertionError("the scale must change the result")
+
+
+def pin_v_is_linear(lib):
+    """Doubling V (exact in bf16) doubles the output exactly."""
+    c = W.contig_case(1, 4, 1, 32, 30, seed=12)
+    v2 = W.f32_to_bf16_bits(W.bf16_bits_to_f32(c.v) * np.float32(2)).reshape(c.v.shape)
+    a = oracle.decode(c.q, c.k, c.v, c.seq_lens, c.scale, lib=lib)
+    b = oracle.decode(c.q, c.k, v2, c.seq_lens, c.scale, lib=lib)
+    if not np.array_equal(2 * a, b):
+        raise AssertionError("out(2V) must equal 2 out(V)")
+
+
+def pin_token_permutation(lib):
+    """Reordering the tokens (K and V rows together) does not change the output."""
+    c = W.contig_case(2, 6, 3, 64, 48, seq_lens=[48, 31], seed=13)
+    rng = np.random.default_rng(99)
+    k2, v2 = c.k.copy(), c.v.copy()
+    for b in range(c.B):
+        n = int(c.seq_lens[b])
+        p = rng.permutation(n)
+        k2[b, :, :n] = c.k[b][:, p]
+        v2[b, :, :n] = c.v[b][:, p]
+    _close(oracle.decode(c.q, c.k, c.v, c.seq_lens, c.scale, lib=lib),
+           oracle.decode(c.q, k2, v2, c.seq_lens, c.scale, lib=lib), what="token permutation")
+
+
+def pin_head_mapping(lib):
+    """Swapping the data of kv heads i and j swaps the output head groups."""
+    c = W.contig_case(1, 12, 3, 32, 40, seed=14)
+    G = c.G
+    k2, v2 = c.k.copy(), c.v.copy()
+    k2[:, [0, 2]] = c.k[:, [2, 0]]
+    v2[:, [0, 2]] = c.v[:, [2, 0]]
+    q2 = c.q.copy()
+    q2[:, 0:G], q2[:, 2 * G:3 * G] = c.q[:, 2 * G:3 * G], c.q[:, 0:G]
+    a = oracle.decode(c.q, c.k, c.v, c.seq_lens, c.scale, lib=lib)
+    b = oracle.decode(q2, k2, v2, c.seq_lens, c.scale, lib=lib)
+    exp = a.copy()
+    exp[:, 0:G], exp[:, 2 * G:3 * G] = a[:, 2 * G:3 * G], a[:, 0:G]
+    if not np.array_equal(b, exp):
+        raise AssertionError("head groups must follow their kv head")
+
+
+def pin_nan_tail_ignored(lib):
+    """Rows at or beyond len (here NaN or inf) never reach the output."""
+    lens = [5, 17, 0]
+    a = W.contig_case(3, 4, 2, 64, 24, seq_lens=lens, seed=15)
+    for tail in ("nan", "inf"):
+        b = W.contig_case(3, 4, 2, 64, 24, seq_lens=lens, seed=15, tail=tail)
+        oa = oracle.decode(a.q, a.k, a.v, a.seq_lens, a.scale, lib=lib)
+        ob = oracle.decode(b.q, b.k, b.v, b.seq_lens, b.scale, lib=lib)
+        if not np.array_equal(oa, ob):
+            raise AssertionError(f"{tail} tail changed the output")
+        if not np.all(ob[2] == 0):
+            raise AssertionError("len = 0 must give a zero row")
+
+
+def pin_split_invariance(lib):
+    """Split partials folded by the log-sum-exp rescale equal the one-pass result."""
+    c = W.contig_case(2, 8, 2, 64, 150, seq_lens=[150, 61], seed=16)
+    full = oracle.decode(c.q, c.k, c.v, c.seq_lens, c.scale, lib=lib)
+    for chunk in (1, 2, 3, 7, 64, 150, 1000):
+        part = oracle.decode(c.q, c.k, c.v, c.seq_lens, c.scale, chunk=chunk, lib=lib)
+        _close(part, full, rtol=1e-12, atol=1e-14, what=f"split chunk={chunk}")
+    # scores of several hundred: every exponent must be taken relative to a running max
+    big = W.contig_case(1, 4, 1, 64, 90, seed=20, scale=100.0)
+    full = oracle.decode(big.q, big.k, big.v, big.seq_lens, big.scale, lib=lib)
+    if not np.all(np.isfinite(full)):
+        raise AssertionError("large scores must not overflow")
+    for chunk in (4, 30):
+        part = oracle.decode(big.q, big.k, big.v, big.seq_lens, big.scale, chunk=chunk, lib=lib)
+        _close(part, full, rtol=1e-12, atol=1e-14, what=f"large-score split chunk={chunk}")
+    p = W.paged_case(3, 8, 2, 32, 16, 40, seq_lens=[150, 1, 77], seed=17)
+    full = oracle.paged_decode(p.q, p.k, p.v, p.seq_lens, p.page_table, p.scale, lib=lib)
+    for chunk in (1, 5, 16, 33):
+        part = oracle.paged_decode(p.q, p.k, p.v, p.seq_lens, p.page_table, p.scale, chunk=chunk,
+                                   lib=lib)
+        _close(part, full, rtol=1e-12, atol=1e-14, what=f"paged split chunk={chunk}")
+
+
+def gather_pages(p: W.Case):
+    """Copy a paged cache into a contiguous [B, Hkv, max_pages*ps, D] cache (data movement only)."""
+    S = p.max_pages * p.page_size
+    k = np.zeros((p.B, p.Hkv, S, p.D), np.uint16)
+    v = np.zeros_like(k)
+    for b in range(p.B):
+        for i in range(p.max_pages):
+            pg = int(p.page_table[b, i])
+            if pg < 0:
+                continue
+            k[b, :, i * p.page_size:(i + 1) * p.page_size] = p.k[pg]
+            v[b, :, i * p.page_size:(i + 1) * p.page_size] = p.v[pg]
+    return k, v
+
+
+def pin_paged_equals_gathered(lib):
+    p = W.paged_case(4, 8, 2, 64, 16, 64, seq_lens=[1, 16, 17, 200], max_len=256, seed=18)
+    k, v = gather_pages(p)
+    a = oracle.paged_decode(p.q, p.k, p.v, p.seq_lens, p.page_table, p.scale, lib=lib)
+    b = oracle.decode(p.q, k, v, p.seq_lens, p.scale, lib=lib)
+    if not np.array_equal(a, b):
+        raise AssertionError("paged must equal the gathered contiguous cache")
+
+
+def pin_page_permutation(lib):
+    """Moving pages to other pool slots (table updated to match) gives identical output."""
+    p = W.paged_case(3, 8, 4, 32, 8, 60, seq_lens=[100, 7, 64], max_len=128, seed=19)
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(p.num_pages)           # new slot of old page i
+    k2 = np.empty_like(p.k)
+    v2 = np.empty_like(p.v)
+    k2[perm] = p.k
+    v2[perm] = p.v
+    t2 = np.where(p.page_table >= 0, perm[np.maximum(p.page_table, 0)], -1).astype(np.int32)
+    a = oracle.paged_decode(p.q, p.k, p.v, p.seq_lens, p.page_table, p.scale, lib=lib)
+    b = oracle.paged_decode(p.q, k2, v2, p.seq_lens, t2, p.scale, lib=lib)
+    if not np.array_equal(a, b):
+        raise AssertionError("page permutation changed the output")
+
+
+ALL_PINS = [
+    pin_golden_closed_forms, pin_torch_sdpa, pin_brute_force, pin_len_one_is_v0,
+    pin_uniform_weights_give_mean, pin_dominant_key, pin_scale_moves_into_q, pin_v_is_linear,
+    pin_token_permutation, pin_head_mapping, pin_nan_tail_ignored, pin_split_invariance,
+    pin_paged_equals_gathered, pin_page_permutation,
+]
