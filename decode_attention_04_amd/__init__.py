@@ -1,0 +1,183 @@
+"""MI355X (gfx950) GQA flash-decode attention: Python binding over libgqa_decode.so.
+
+The binding only marshals arguments: torch tensors supply device memory and
+the current HIP stream, every step of the computation runs in the HIP
+kernels of the shared library, and there is no fallback.  If the library is
+not built, importing the binding succeeds but every call raises.
+
+Entry points mirror include/gqa_decode.h:
+    gqa_decode(q, k_cache, v_cache, seq_lens, scale, ...)
+    gqa_paged_decode(q, k_pool, v_pool, seq_lens, page_table, scale, ...)
+    gqa_decode_workspace_bytes(B, Hq, Hkv, head_dim, max_seq_len, page_size, num_splits)
+    gqa_decode_plan(B, Hq, Hkv, head_dim, max_seq_len, page_size, num_splits, cu_count)
+    gqa_status_string(code)
+bf16 tensors may be torch.bfloat16 or int16/uint16 views of the bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgqa_decode.so")
+
+GQA_OK = 0
+STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_UNSUPPORTED",
+                4: "GQA_ERR_ALIGN", 5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_HIP"}
+
+# every symbol include/gqa_decode.h declares
+EXPORTED = ("gqa_decode_plan", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_paged_decode",
+            "gqa_status_string")
+
+
+class GqaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS_NAMES.get(code, code)} ({gqa_status_string(code)})")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int), ("split_tokens", ctypes.c_int),
+                ("tile_tokens", ctypes.c_int), ("waves", ctypes.c_int), ("grid", ctypes.c_int),
+                ("direct", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run decode_attention_04_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.gqa_decode_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(Plan)]
+    lib.gqa_decode_plan.restype = ci
+    lib.gqa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci, ci]
+    lib.gqa_decode_workspace_bytes.restype = sz
+    lib.gqa_decode.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp, vp, sz, ci, vp]
+    lib.gqa_decode.restype = ci
+    lib.gqa_paged_decode.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, vp,
+                                     sz, ci, vp]
+    lib.gqa_paged_decode.restype = ci
+    lib.gqa_status_string.argtypes = [ci]
+    lib.gqa_status_string.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def gqa_status_string(code: int) -> str:
+    try:
+        return load().gqa_status_string(int(code)).decode()
+    except RuntimeError:
+        return STATUS_NAMES.get(code, str(code))
+
+
+def gqa_decode_plan(B, Hq, Hkv, head_dim, max_seq_len, page_size=0, num_splits=0, cu_count=256):
+    p = Plan()
+    rc = load().gqa_decode_plan(B, Hq, Hkv, head_dim, max_seq_len, page_size, num_splits,
+                                cu_count, ctypes.byref(p))
+    if rc != GQA_OK:
+        raise GqaError(rc, "gqa_decode_plan")
+    return p
+
+
+def gqa_decode_workspace_bytes(B, Hq, Hkv, head_dim, max_seq_len, page_size=0, num_splits=0):
+    n = load().gqa_decode_workspace_bytes(B, Hq, Hkv, head_dim, max_seq_len, page_size,
+                                          num_splits)
+    if n == ctypes.c_size_t(-1).value:
+        raise GqaError(2, "gqa_decode_workspace_bytes")
+    return n
+
+
+# ------------------------------------------------------------------ tensor marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, name, dtypes):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _bf16_types():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _stream_ptr(stream, device):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def _workspace(workspace, need, device):
+    torch = _torch()
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def gqa_decode(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None, num_splits=0,
+               stream=None):
+    """Contiguous cache: q [B,Hq,D], k/v [B,Hkv,S_max,D] bf16, seq_lens int32 [B].
+
+    Returns out (fp32 [B,Hq,D]).  `workspace` (a uint8 device tensor) is
+    allocated when not given; pass one to keep the call allocation-free."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    _, Hkv, S_max, _ = k_cache.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, S_max, 0, num_splits)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    bf = _bf16_types()
+    rc = load().gqa_decode(
+        _dev_ptr(q, "q", bf), _dev_ptr(k_cache, "k_cache", bf), _dev_ptr(v_cache, "v_cache", bf),
+        _dev_ptr(seq_lens, "seq_lens", (torch.int32,)), B, Hq, Hkv, D, S_max, float(scale),
+        _dev_ptr(out, "out", (torch.float32,)),
+        None if workspace is None else workspace.data_ptr(), ws_bytes, int(num_splits),
+        _stream_ptr(stream, q.device))
+    if rc != GQA_OK:
+        raise GqaError(rc, "gqa_decode")
+    return out
+
+
+def gqa_paged_decode(q, k_pool, v_pool, seq_lens, page_table, scale, out=None, workspace=None,
+                     num_splits=0, stream=None):
+    """Paged cache: k/v pools [P,Hkv,page_size,D] bf16, page_table int32 [B,max_pages]."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    P, Hkv, page_size, _ = k_pool.shape
+    max_pages = page_table.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, max_pages * page_size, page_size, num_splits)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    bf = _bf16_types()
+    rc = load().gqa_paged_decode(
+        _dev_ptr(q, "q", bf), _dev_ptr(k_pool, "k_pool", bf), _dev_ptr(v_pool, "v_pool", bf),
+        _dev_ptr(seq_lens, "seq_lens", (torch.int32,)),
+        _dev_ptr(page_table, "page_table", (torch.int32,)), B, Hq, Hkv, D, page_size, P,
+        max_pages, float(scale), _dev_ptr(out, "out", (torch.float32,)),
+        None if workspace is None else workspace.data_ptr(), ws_bytes, int(num_splits),
+        _stream_ptr(stream, q.device))
+    if rc != GQA_OK:
+        raise GqaError(rc, "gqa_paged_decode")
+    return out

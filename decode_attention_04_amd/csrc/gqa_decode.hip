@@ -1,0 +1,640 @@
+// Single-token GQA flash-decode attention over a bf16 KV cache, gfx950 only.
+//
+// Two kernels (the split-KV scheme of the AstrAI csrc commit log and the
+// partial/combine structure of sparkinfer PR #877, section Mechanism):
+//
+//   gqa_split_kernel   one workgroup per (sequence b, kv head, split s).  Its
+//                      NW waves stripe the split's tiles (tile i goes to wave
+//                      i % NW), each keeping its own running (m, l, acc); the
+//                      waves are folded in LDS in ascending wave order and the
+//                      workgroup emits one unnormalised partial per query head
+//                      (or the final output when there is a single split).
+//   gqa_combine_kernel folds the S partials of each (b, h) with the
+//                      log-sum-exp rescale, splits in ascending order.
+//
+// Layout of the work inside one wave (64 lanes, r = lane % 16, grp = lane / 16):
+//
+//   QK^T  v_mfma_f32_16x16x32_bf16 with A = 16 keys x 32 dims and
+//         B = 32 dims x 16 query heads (the G heads of the kv head, zero
+//         padded to 16).  Lane (r, grp) loads 16 contiguous bytes of key row r
+//         straight from HBM into the A operand, so K never passes through LDS.
+//         Q is exact bf16 and stays resident in the B operand registers.  The
+//         result gives lane (r, grp) the scores of query head r for keys
+//         4*grp .. 4*grp+3 of each 16-key block.
+//   softmax the scale (times log2 e) is applied to the fp32 scores; the
+//         running max of head r is shared by the four lanes r, r+16, r+32,
+//         r+48 (two xor shuffles per tile); l is kept per lane and summed
+//         once at the end.
+//   PV    v_mfma_f32_16x16x4_f32 computing O^T[d][g] += V^T[d][t] P^T[t][g].
+//         The B operand is the lane's own probability (no data movement), the
+//         A operand one fp32 value of V for the lane's key; lane (r, grp)
+//         loads 16 contiguous bytes of V row (4*grp + j), so P is never
+//         rounded to bf16 and V never needs a transpose.  The accumulator
+//         rows are head dims, its columns query heads: lane (r, grp) owns
+//         head r, so the softmax rescale of acc is lane-local.
+//
+// K/V tiles are double-buffered in VGPRs: the loads of the wave's next tile
+// are issued before the current tile's QK / softmax / PV, so HBM latency
+// overlaps compute (the role of the two shared-memory buffers of sparkinfer
+// PR #874, section Summary).  Loads use buffer resources whose size ends at
+// the sequence length, so rows past the end read as zero (the zero-filling
+// predicated copy of the AstrAI csrc commit log) and a NaN in the unused tail
+// of a cache can never reach the sums.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "gqa_decode.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;           // waves per workgroup
+constexpr int kMaxHeadsPerKv = 16;  // G is padded to the MFMA's 16 columns
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords (gfx9 family)
+
+struct SplitArgs {
+    const uint16_t *q;
+    const uint16_t *k;
+    const uint16_t *v;
+    const int32_t *seq_lens;
+    const int32_t *page_table;  // paged only
+    float *part_acc;            // [B][Hq][S][D]
+    float *part_ml;             // [B][Hq][S][2]  (m in log2 units, l)
+    float *out;                 // [B][Hq][D]     (direct mode)
+    int B, Hq, Hkv, G;
+    int S_max;                  // contiguous capacity
+    int page_size, max_pages;   // paged
+    int num_pages;              // paged
+    int num_splits, split_tokens;
+    float qk_scale_log2;        // scale * log2(e)
+};
+
+struct CombineArgs {
+    const float *part_acc;
+    const float *part_ml;
+    float *out;
+    int Hq, num_splits;
+};
+
+__device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float xor_max(float x, int mask) {
+    return fmaxf(x, __shfl_xor(x, mask, 64));
+}
+
+// Element e (0..2*N-1) of a vector of N dwords holding 2*N bf16 values.
+template <int N>
+__device__ __forceinline__ float bf16_elem(const unsigned int (&w)[N], int e) {
+    return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+}
+
+template <int D>
+struct Shape {
+    static constexpr int KB = D / 32;                  // 32-dim blocks of the QK contraction
+    static constexpr int DPL = D >= 128 ? 8 : D / 16;  // V values per lane per chunk
+    static constexpr int VC = D / (16 * DPL);          // V chunks per key per lane
+    static constexpr int NACC = D / 16;                // PV accumulators (f32x4) per lane
+    static constexpr int VW = DPL / 2;                 // dwords per V chunk
+};
+
+// One wave's staged tile: NB blocks of 16 keys.
+template <int D, int NB>
+struct Tile {
+    u32x4_t k[NB][Shape<D>::KB];                       // key 16*blk + r, dims 32*kb + 8*grp ..
+    unsigned int v[NB][4][Shape<D>::VC][Shape<D>::VW]; // key 16*blk + 4*grp + j, dims 16*DPL*c + DPL*r ..
+};
+
+// Issue the loads of one tile.  `rk` / `rv` cover the rows of this tile's
+// (sequence, kv head) or page, ending at the last valid row; `row0` is the
+// tile's first row inside that range.
+template <int D, int NB>
+__device__ __forceinline__ void load_tile(Tile<D, NB> &t, __amdgpu_buffer_rsrc_t rk,
+                                          __amdgpu_buffer_rsrc_t rv, int row0, int r, int grp) {
+    using S = Shape<D>;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+        const int krow = row0 + 16 * blk + r;
+#pragma unroll
+        for (int kb = 0; kb < S::KB; ++kb) {
+            const int off = (krow * D + 32 * kb + 8 * grp) * 2;
+            t.k[blk][kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int vrow = row0 + 16 * blk + 4 * grp + j;
+#pragma unroll
+            for (int c = 0; c < S::VC; ++c) {
+                const int off = (vrow * D + 16 * S::DPL * c + S::DPL * r) * 2;
+                if constexpr (S::VW == 4) {
+                    u32x4_t x = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+                    t.v[blk][j][c][0] = x[0];
+                    t.v[blk][j][c][1] = x[1];
+                    t.v[blk][j][c][2] = x[2];
+                    t.v[blk][j][c][3] = x[3];
+                } else {
+                    u32x2_t x = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0));
+                    t.v[blk][j][c][0] = x[0];
+                    t.v[blk][j][c][1] = x[1];
+                }
+            }
+        }
+    }
+}
+
+// Running online-softmax state of one wave (lane (r, grp) holds query head r).
+template <int D>
+struct WaveState {
+    f32x4_t acc[Shape<D>::NACC];  // acc[c*DPL + e][i] = O[r][16*DPL*c + DPL*(4*grp+i) + e]
+    float m;                      // running max (log2 units), identical in the 4 lanes of head r
+    float l;                      // this lane's share of the running sum
+};
+
+// QK^T, online softmax and PV for one staged tile whose first key has index
+// `t0` in the sequence; keys at or beyond `t_end` are masked.
+template <int D, int NB>
+__device__ __forceinline__ void compute_tile(const Tile<D, NB> &t, const bf16x8_t (&qb)[Shape<D>::KB],
+                                             WaveState<D> &st, int t0, int t_end, int grp,
+                                             float qk_scale_log2) {
+    using S = Shape<D>;
+    f32x4_t sc[NB];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < S::KB; ++kb)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[blk][kb]),
+                                                        qb[kb], c, 0, 0, 0);
+        sc[blk] = c;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = t0 + 16 * blk + 4 * grp + i;
+            const float x = tok < t_end ? sc[blk][i] * qk_scale_log2 : -INFINITY;
+            sc[blk][i] = x;
+            mx = fmaxf(mx, x);
+        }
+    }
+    mx = xor_max(mx, 16);
+    mx = xor_max(mx, 32);
+    // The tile holds at least one unmasked key, so m_new is finite.
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 on the first tile
+    float psum = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(sc[blk][i] - m_new);
+            sc[blk][i] = p;
+            psum += p;
+        }
+    }
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+#pragma unroll
+    for (int a = 0; a < S::NACC; ++a) st.acc[a] *= alpha;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float p = sc[blk][j];
+#pragma unroll
+            for (int c = 0; c < S::VC; ++c) {
+#pragma unroll
+                for (int e = 0; e < S::DPL; ++e) {
+                    const float vf = bf16_elem(t.v[blk][j][c], e);
+                    st.acc[c * S::DPL + e] =
+                        __builtin_amdgcn_mfma_f32_16x16x4f32(vf, p, st.acc[c * S::DPL + e], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+template <int D>
+struct FoldLds {
+    float m[kWaves][kMaxHeadsPerKv];
+    float l[kWaves][kMaxHeadsPerKv];
+    float acc[kWaves][kMaxHeadsPerKv][D];
+};
+
+template <int D, int NB, bool PAGED>
+__global__ __launch_bounds__(64 * kWaves) void gqa_split_kernel(const SplitArgs a) {
+    using S = Shape<D>;
+    constexpr int TT = 16 * NB;  // keys per wave tile
+    __shared__ FoldLds<D> lds;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r = lane & 15;
+    const int grp = lane >> 4;
+
+    const int split = blockIdx.x % a.num_splits;
+    const int bk = blockIdx.x / a.num_splits;
+    const int kvh = bk % a.Hkv;
+    const int b = bk / a.Hkv;
+    // Out-of-range lengths / page ids are clamped so that no access can leave
+    // the caller's buffers (the results for such inputs are unspecified).
+    const int cap = PAGED ? a.max_pages * a.page_size : a.S_max;
+    const int len = min(max(a.seq_lens[b], 0), cap);
+    const int t_begin = split * a.split_tokens;
+    const int t_end = min(len, t_begin + a.split_tokens);
+    const int ntiles = t_end > t_begin ? (t_end - t_begin + TT - 1) / TT : 0;
+    const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+
+    // Q of the G heads of this kv head, exact bf16, in the QK B operand layout.
+    bf16x8_t qb[S::KB];
+    {
+        const uint16_t *qrow = a.q + ((size_t)b * a.Hq + (size_t)kvh * a.G + r) * D;
+#pragma unroll
+        for (int kb = 0; kb < S::KB; ++kb) {
+            u32x4_t x = {0u, 0u, 0u, 0u};
+            if (r < a.G) x = *reinterpret_cast<const u32x4_t *>(qrow + 32 * kb + 8 * grp);
+            qb[kb] = __builtin_bit_cast(bf16x8_t, x);
+        }
+    }
+
+    WaveState<D> st;
+#pragma unroll
+    for (int i = 0; i < S::NACC; ++i) st.acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    st.m = -INFINITY;
+    st.l = 0.f;
+
+    // Resources of the rows a tile reads.  Contiguous: the whole (b, kvh)
+    // slab up to len.  Paged: the tile's page up to len (one table read).
+    const size_t slab = (size_t)D;
+    auto issue = [&](Tile<D, NB> &tile, int it) {
+        const int t0 = t_begin + (wave + kWaves * it) * TT;
+        if constexpr (PAGED) {
+            const int pidx = t0 / a.page_size;
+            const int row0 = t0 - pidx * a.page_size;
+            const int page = min(max(__builtin_amdgcn_readfirstlane(a.page_table[(size_t)b * a.max_pages + pidx]), 0),
+                                 a.num_pages - 1);
+            const int rows = min(a.page_size, len - pidx * a.page_size);
+            const size_t base = ((size_t)page * a.Hkv + kvh) * (size_t)a.page_size * slab;
+            __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, rows * D * 2, kRsrcWord3);
+            __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, rows * D * 2, kRsrcWord3);
+            load_tile<D, NB>(tile, rk, rv, row0, r, grp);
+        } else {
+            const size_t base = ((size_t)b * a.Hkv + kvh) * (size_t)a.S_max * slab;
+            __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, len * D * 2, kRsrcWord3);
+            __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, len * D * 2, kRsrcWord3);
+            load_tile<D, NB>(tile, rk, rv, t0, r, grp);
+        }
+    };
+    auto tile_start = [&](int it) { return t_begin + (wave + kWaves * it) * TT; };
+
+    Tile<D, NB> buf0, buf1;
+    if (my_tiles > 0) issue(buf0, 0);
+    for (int it = 0; it < my_tiles; it += 2) {
+        if (it + 1 < my_tiles) issue(buf1, it + 1);
+        compute_tile<D, NB>(buf0, qb, st, tile_start(it), t_end, grp, a.qk_scale_log2);
+        if (it + 1 < my_tiles) {
+            if (it + 2 < my_tiles) issue(buf0, it + 2);
+            compute_tile<D, NB>(buf1, qb, st, tile_start(it + 1), t_end, grp, a.qk_scale_log2);
+        }
+    }
+
+    // This wave's sum for head r: the four lanes r, r+16, r+32, r+48.
+    float lsum = st.l;
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+
+    // Publish the wave's state; rows g >= G are never read.
+    if (r < a.G) {
+        if (grp == 0) {
+            lds.m[wave][r] = st.m;
+            lds.l[wave][r] = lsum;
+        }
+#pragma unroll
+        for (int c = 0; c < S::VC; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < S::DPL; ++e)
+                    lds.acc[wave][r][16 * S::DPL * c + S::DPL * (4 * grp + i) + e] = st.acc[c * S::DPL + e][i];
+    }
+    __syncthreads();
+
+    // Fold the waves in ascending order and emit this split's result.
+    const int G = a.G;
+    const bool direct = a.num_splits == 1;
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
+        const int g = idx / D, d = idx - (idx / D) * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds.m[w][g]);
+        float L = 0.f, ACC = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float sw = __builtin_amdgcn_exp2f(lds.m[w][g] - M);
+                L += sw * lds.l[w][g];
+                ACC += sw * lds.acc[w][g][d];
+            }
+        }
+        const size_t h = (size_t)kvh * G + g;
+        if (direct) {
+            a.out[((size_t)b * a.Hq + h) * D + d] = L > 0.f ? ACC / L : 0.f;
+        } else {
+            const size_t row = ((size_t)b * a.Hq + h) * a.num_splits + split;
+            a.part_acc[row * D + d] = ACC;
+            if (d == 0) {
+                a.part_ml[row * 2 + 0] = M;
+                a.part_ml[row * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+// One workgroup of D threads per (b, h): thread d folds acc[., d] over the
+// splits in ascending order.
+template <int D>
+__global__ __launch_bounds__(D) void gqa_combine_kernel(const CombineArgs a) {
+    const size_t bh = blockIdx.x;
+    const int d = threadIdx.x;
+    const int S = a.num_splits;
+    const float *ml = a.part_ml + bh * S * 2;
+    const float *acc = a.part_acc + bh * S * D + d;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+    float L = 0.f, ACC = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < S; ++s) {
+            const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
+            L += w * ml[2 * s + 1];
+            ACC += w * acc[(size_t)s * D];
+        }
+    }
+    a.out[bh * D + d] = L > 0.f ? ACC / L : 0.f;
+}
+
+// ------------------------------------------------------------------ host side
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int tile_tokens_for(int D) { return D == 64 ? 64 : (D == 128 ? 32 : 16); }
+
+bool supported_dim(int D) { return D == 64 || D == 128 || D == 256; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+gqa_status_t device_cu_count(int *out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GQA_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) {
+        int c = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return GQA_OK;
+        }
+    }
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+        return GQA_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(c, std::memory_order_relaxed);
+    *out = c;
+    return GQA_OK;
+}
+
+int env_splits() {
+    const char *s = getenv("GQA_DECODE_SPLITS");
+    if (s == nullptr || *s == '\0') return 0;
+    const int v = atoi(s);
+    return v > 0 ? v : 0;
+}
+
+bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+template <int D>
+hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const float *part_ml,
+                          float *out, int B, int Hq, hipStream_t stream) {
+    CombineArgs ca{part_acc, part_ml, out, Hq, plan.num_splits};
+    hipLaunchKernelGGL(gqa_combine_kernel<D>, dim3((unsigned)(B * Hq)), dim3(D), 0, stream, ca);
+    return hipGetLastError();
+}
+
+template <int D, int NB, bool PAGED>
+hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
+    if constexpr (NB * D > 256) {  // at most 16 KB of K+V (64 * NB * D bytes) per wave tile
+        return hipErrorInvalidValue;
+    } else {
+        hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED>), dim3((unsigned)plan.grid),
+                           dim3(64 * kWaves), 0, stream, a);
+        return hipGetLastError();
+    }
+}
+
+template <int D, bool PAGED>
+hipError_t launch_split(const gqa_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
+    switch (plan.tile_tokens) {
+        case 16: return launch_split_nb<D, 1, PAGED>(plan, a, stream);
+        case 32: return launch_split_nb<D, 2, PAGED>(plan, a, stream);
+        case 64: return launch_split_nb<D, 4, PAGED>(plan, a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, void *workspace,
+                 hipStream_t stream) {
+    if (!plan.direct) {
+        const size_t acc_bytes = align_up((size_t)a.B * a.Hq * plan.num_splits * D * sizeof(float), 256);
+        a.part_acc = static_cast<float *>(workspace);
+        a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + acc_bytes);
+    }
+    hipError_t e = hipSuccess;
+    switch (D) {
+        case 64: e = paged ? launch_split<64, true>(plan, a, stream) : launch_split<64, false>(plan, a, stream); break;
+        case 128: e = paged ? launch_split<128, true>(plan, a, stream) : launch_split<128, false>(plan, a, stream); break;
+        case 256: e = paged ? launch_split<256, true>(plan, a, stream) : launch_split<256, false>(plan, a, stream); break;
+        default: return GQA_ERR_UNSUPPORTED;
+    }
+    if (e != hipSuccess) return GQA_ERR_HIP;
+    if (plan.direct) return GQA_OK;
+    switch (D) {
+        case 64: e = launch_combine<64>(plan, a.part_acc, a.part_ml, a.out, a.B, a.Hq, stream); break;
+        case 128: e = launch_combine<128>(plan, a.part_acc, a.part_ml, a.out, a.B, a.Hq, stream); break;
+        default: e = launch_combine<256>(plan, a.part_acc, a.part_ml, a.out, a.B, a.Hq, stream); break;
+    }
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+gqa_status_t check_common(const void *q, const void *k, const void *v, const int32_t *seq_lens,
+                          const float *out, int B, int Hq, int Hkv, int D, float scale) {
+    if (!q || !k || !v || !seq_lens || !out) return GQA_ERR_NULL;
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !isfinite(scale)) return GQA_ERR_SHAPE;
+    if (!supported_dim(D) || Hq / Hkv > kMaxHeadsPerKv) return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hq * D > INT32_MAX) return GQA_ERR_SHAPE;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
+        misaligned(seq_lens, 4))
+        return GQA_ERR_ALIGN;
+    return GQA_OK;
+}
+
+gqa_status_t plan_for_call(int B, int Hq, int Hkv, int D, int cap, int page_size, int num_splits,
+                           gqa_plan_t *plan) {
+    if (num_splits == 0) num_splits = env_splits();
+    int cu = 256;
+    if (num_splits == 0) {
+        gqa_status_t s = device_cu_count(&cu);
+        if (s != GQA_OK) return s;
+    }
+    return gqa_decode_plan(B, Hq, Hkv, D, cap, page_size, num_splits, cu, plan);
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int page_size,
+                             int num_splits, int cu_count, gqa_plan_t *plan) {
+    if (plan == nullptr) return GQA_ERR_NULL;
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_seq_len < 0 || page_size < 0 ||
+        num_splits < 0 || cu_count <= 0)
+        return GQA_ERR_SHAPE;
+    if (!supported_dim(D) || Hq / Hkv > kMaxHeadsPerKv) return GQA_ERR_UNSUPPORTED;
+    if (page_size > 0 && page_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
+
+    int tt = tile_tokens_for(D);
+    if (page_size > 0) {
+        while (page_size % tt != 0) tt /= 2;  // a tile never straddles a page (tt >= 16)
+    }
+    const int tiles_total = max_seq_len > 0 ? (max_seq_len + tt - 1) / tt : 1;
+    // Splits: enough workgroups to give every CU two of them, and no split
+    // longer than kMaxSplitTokens keys (so one long sequence in a ragged
+    // batch cannot serialise behind a single workgroup), but at least one
+    // tile per wave.
+    constexpr int kMaxSplitTokens = 1024;
+    const int base = B > 0 ? B * Hkv : 1;
+    int S = num_splits;
+    if (S == 0) {
+        const int fill = (2 * cu_count + base - 1) / base;
+        const int len_cap = (max_seq_len + kMaxSplitTokens - 1) / kMaxSplitTokens;
+        S = fill > len_cap ? fill : len_cap;
+        const int most = (tiles_total + kWaves - 1) / kWaves;
+        if (S > most) S = most;
+    }
+    if (S > tiles_total) S = tiles_total;
+    if (S < 1) S = 1;
+    int split_tiles = (tiles_total + S - 1) / S;
+    S = (tiles_total + split_tiles - 1) / split_tiles;  // drop splits that would be empty
+
+    plan->num_splits = S;
+    plan->split_tokens = split_tiles * tt;
+    plan->tile_tokens = tt;
+    plan->waves = kWaves;
+    const int64_t grid = (int64_t)(B > 0 ? B : 0) * Hkv * S;
+    if (grid > INT32_MAX) return GQA_ERR_SHAPE;
+    plan->grid = (int)grid;
+    plan->direct = S == 1 ? 1 : 0;
+    plan->workspace_bytes = 0;
+    if (!plan->direct) {
+        const size_t rows = (size_t)B * Hq * S;
+        plan->workspace_bytes = align_up(rows * D * sizeof(float), 256) + align_up(rows * 2 * sizeof(float), 256);
+    }
+    return GQA_OK;
+}
+
+size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_seq_len, int page_size,
+                                  int num_splits) {
+    gqa_plan_t plan;
+    if (plan_for_call(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, &plan) != GQA_OK) return SIZE_MAX;
+    return plan.workspace_bytes;
+}
+
+gqa_status_t gqa_decode(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
+                        float scale, float *out, void *workspace, size_t workspace_bytes,
+                        int num_splits, hipStream_t stream) {
+    gqa_status_t s = check_common(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, scale);
+    if (s != GQA_OK) return s;
+    if (S_max < 0 || num_splits < 0) return GQA_ERR_SHAPE;
+    if (((int64_t)S_max + 64) * D * 2 > INT32_MAX) return GQA_ERR_SHAPE;  // 32-bit buffer offsets
+    if (workspace != nullptr && misaligned(workspace, 16)) return GQA_ERR_ALIGN;
+    gqa_plan_t plan;
+    s = plan_for_call(B, Hq, Hkv, D, S_max, 0, num_splits, &plan);
+    if (s != GQA_OK) return s;
+    if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+        return workspace == nullptr ? GQA_ERR_NULL : GQA_ERR_WORKSPACE;
+    if (B == 0) return GQA_OK;
+    SplitArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k_cache);
+    a.v = static_cast<const uint16_t *>(v_cache);
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+    a.S_max = S_max;
+    a.num_splits = plan.num_splits;
+    a.split_tokens = plan.split_tokens;
+    a.qk_scale_log2 = scale * 1.4426950408889634f;
+    return run(plan, a, D, false, workspace, stream);
+}
+
+gqa_status_t gqa_paged_decode(const void *q, const void *k_pool, const void *v_pool,
+                              const int32_t *seq_lens, const int32_t *page_table, int B, int Hq,
+                              int Hkv, int D, int page_size, int num_pages, int max_pages,
+                              float scale, float *out, void *workspace, size_t workspace_bytes,
+                              int num_splits, hipStream_t stream) {
+    gqa_status_t s = check_common(q, k_pool, v_pool, seq_lens, out, B, Hq, Hkv, D, scale);
+    if (s != GQA_OK) return s;
+    if (page_table == nullptr) return GQA_ERR_NULL;
+    if (misaligned(page_table, 4)) return GQA_ERR_ALIGN;
+    if (page_size <= 0 || num_pages <= 0 || max_pages <= 0 || num_splits < 0) return GQA_ERR_SHAPE;
+    if (page_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)max_pages * page_size > INT32_MAX || (int64_t)page_size * D * 2 > INT32_MAX)
+        return GQA_ERR_SHAPE;
+    if (workspace != nullptr && misaligned(workspace, 16)) return GQA_ERR_ALIGN;
+    gqa_plan_t plan;
+    s = plan_for_call(B, Hq, Hkv, D, max_pages * page_size, page_size, num_splits, &plan);
+    if (s != GQA_OK) return s;
+    if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+        return workspace == nullptr ? GQA_ERR_NULL : GQA_ERR_WORKSPACE;
+    if (B == 0) return GQA_OK;
+    SplitArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k_pool);
+    a.v = static_cast<const uint16_t *>(v_pool);
+    a.seq_lens = seq_lens;
+    a.page_table = page_table;
+    a.out = out;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+    a.page_size = page_size;
+    a.max_pages = max_pages;
+    a.num_pages = num_pages;
+    a.num_splits = plan.num_splits;
+    a.split_tokens = plan.split_tokens;
+    a.qk_scale_log2 = scale * 1.4426950408889634f;
+    return run(plan, a, D, true, workspace, stream);
+}
+
+const char *gqa_status_string(gqa_status_t status) {
+    switch (status) {
+        case GQA_OK: return "ok";
+        case GQA_ERR_NULL: return "a required pointer is NULL";
+        case GQA_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case GQA_ERR_UNSUPPORTED: return "unsupported head_dim, group size or page size";
+        case GQA_ERR_ALIGN: return "a pointer is not aligned as required";
+        case GQA_ERR_WORKSPACE: return "workspace smaller than the plan needs";
+        case GQA_ERR_HIP: return "a HIP runtime call or launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+/*
+ * gqa_decode.h -- single-token GQA flash-decode attention over a bf16 KV cache
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Computes, for every sequence b and query head h,
+ *
+ *     out[b,h,:] = softmax(scale * q[b,h,:] . K[b,h/G,0:len,:]^T) . V[b,h/G,0:len,:]
+ *
+ * with G = Hq / Hkv query heads per kv head (grouped consecutively: query
+ * head h reads kv head h / G) and len = seq_lens[b].  The KV range of every
+ * (sequence, kv head) is cut into splits; each split emits unnormalised
+ * partials (m, l, acc) that a combine step folds with the log-sum-exp rescale
+ * in ascending split order (sparkinfer PR #877 "split the flash-decode KV range
+ * across warp-groups", section Mechanism; AstrAI csrc commit log, the split-KV
+ * decode bullets: partials over gridDim.z blocks reduced by a combine kernel,
+ * split count chosen to fill the device).  All G query heads of a kv head are
+ * computed by one workgroup, so each K/V byte is read from HBM once (AstrAI
+ * csrc commit log, the decode MMA head-packing bullets).
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are caller-owned DEVICE memory.  q, k, v, out and
+ *     workspace must be 16-byte aligned; seq_lens and page_table 4-byte
+ *     aligned.  bf16 tensors are passed as raw 16-bit patterns.
+ *   - Calls only enqueue work on `stream` (0 = the null stream): they never
+ *     synchronise, never allocate and keep no state besides a cached CU count
+ *     per device.  Outputs are ready when the stream reaches them.
+ *   - Every argument check runs on the host before any launch; a rejected call
+ *     launches nothing and returns the status below.  A failed launch returns
+ *     GQA_ERR_HIP.  Nothing throws across this interface.
+ *   - Device-resident preconditions that the host cannot check:
+ *     0 <= seq_lens[b] <= capacity, and (paged) page_table[b][i] in
+ *     [0, num_pages) for i < ceil(seq_lens[b] / page_size).  Entries past that
+ *     are never read.  A sequence of length 0 yields a zero output row.
+ *   - Results are bit-identical from run to run for the same inputs, device
+ *     and plan (fixed fold orders, no atomics in the arithmetic).  Different
+ *     split counts re-associate the sums and may differ in the last bits.
+ */
+#ifndef GQA_DECODE_H
+#define GQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gqa_status {
+    GQA_OK = 0,
+    GQA_ERR_NULL = 1,        /* a required pointer is NULL */
+    GQA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+    GQA_ERR_UNSUPPORTED = 3, /* head_dim not in {64,128,256}, G > 16, page_size % 16 != 0 */
+    GQA_ERR_ALIGN = 4,       /* a pointer violates the alignment above */
+    GQA_ERR_WORKSPACE = 5,   /* workspace smaller than the plan needs */
+    GQA_ERR_HIP = 6          /* a HIP runtime call or launch failed */
+} gqa_status_t;
+
+/* How a call is laid out on the device (host-side, deterministic). */
+typedef struct gqa_plan {
+    int num_splits;         /* S: KV partitions per (sequence, kv head) */
+    int split_tokens;       /* tokens per split, a multiple of tile_tokens */
+    int tile_tokens;        /* tokens one wave stages per pipeline step */
+    int waves;              /* waves (of 64 lanes) per workgroup */
+    int grid;               /* workgroups of the split kernel: B * Hkv * S */
+    int direct;             /* 1: S == 1, the split kernel writes `out` itself */
+    size_t workspace_bytes; /* scratch the call needs (0 when direct) */
+} gqa_plan_t;
+
+/*
+ * The split plan for a call (the split-count rule of the AstrAI csrc commit
+ * log: fill the device, bounded by the tile count).  max_seq_len is the cache
+ * capacity (contiguous S_max, or max_pages * page_size when paged);
+ * page_size = 0 means a contiguous cache.  num_splits = 0 picks the count from
+ * cu_count; num_splits > 0 forces it (clamped to the tile count).  Pure host
+ * code: needs no GPU.
+ */
+gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int head_dim, int max_seq_len, int page_size,
+                             int num_splits, int cu_count, gqa_plan_t *plan);
+
+/*
+ * Workspace bytes gqa_decode / gqa_paged_decode need for the same arguments
+ * on the current device.  With num_splits = 0 this queries the current
+ * device's CU count; returns SIZE_MAX if the arguments are invalid or the
+ * device cannot be queried.
+ */
+size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int max_seq_len,
+                                  int page_size, int num_splits);
+
+/*
+ * Contiguous cache.
+ *   q        bf16 [B][Hq][head_dim]
+ *   k_cache  bf16 [B][Hkv][S_max][head_dim]
+ *   v_cache  bf16 [B][Hkv][S_max][head_dim]
+ *   seq_lens int32 [B], each in [0, S_max]
+ *   out      fp32 [B][Hq][head_dim]  (written)
+ *   workspace: at least gqa_decode_workspace_bytes(B, Hq, Hkv, head_dim,
+ *              S_max, 0, num_splits) bytes; may be NULL when that is 0.
+ *   num_splits: 0 = heuristic, > 0 = forced.
+ */
+gqa_status_t gqa_decode(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *seq_lens, int B, int Hq, int Hkv, int head_dim, int S_max,
+                        float scale, float *out, void *workspace, size_t workspace_bytes,
+                        int num_splits, hipStream_t stream);
+
+/*
+ * Paged cache (AstrAI csrc/tests commit log, the paged decode bullets: one
+ * page-table lookup per tile, a tile never straddling a page).
+ *   k_pool, v_pool bf16 [num_pages][Hkv][page_size][head_dim]
+ *   page_table     int32 [B][max_pages]; token t of sequence b is row
+ *                  t % page_size of page page_table[b][t / page_size]
+ *   page_size      a positive multiple of 16
+ *   seq_lens[b] <= max_pages * page_size
+ *   Other arguments as gqa_decode; the workspace size uses
+ *   max_seq_len = max_pages * page_size and page_size.
+ */
+gqa_status_t gqa_paged_decode(const void *q, const void *k_pool, const void *v_pool,
+                              const int32_t *seq_lens, const int32_t *page_table, int B, int Hq,
+                              int Hkv, int head_dim, int page_size, int num_pages, int max_pages,
+                              float scale, float *out, void *workspace, size_t workspace_bytes,
+                              int num_splits, hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char *gqa_status_string(gqa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_DECODE_H */

@@ -1,0 +1,172 @@
+"""HIP path against the CPU oracle, through the C ABI (needs an MI355X).
+
+Tolerance (elementwise): |gpu - oracle| <= 2e-3 + 2e-3 |oracle|, the fp32
+output against the fp64 oracle on unit-normal bf16 inputs.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_04_amd as gd
+from tests import workloads as W
+from tests.gpu_util import DeviceCase, compare, oracle_out, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+# ------------------------------------------------------------------ the five workloads, full size
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_workload_full_size(name):
+    say(f"[parity] workload {name}: generating")
+    case = W.make(name)
+    dc = DeviceCase(case)
+    plan = gd.gqa_decode_plan(case.B, case.Hq, case.Hkv, case.D, case.capacity, case.page_size)
+    say(f"[parity] workload {name}: plan {plan.as_dict()}")
+    outs = [dc.run_host() for _ in range(3)]
+    say(f"[parity] workload {name}: oracle")
+    ref = oracle_out(case)
+    stats = compare(outs[0], ref, name)
+    say(f"[parity] workload {name}: {stats}")
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), "not bit-exact across runs"
+
+
+# ------------------------------------------------------------------ shape matrix
+MATRIX = []
+for D in (64, 128, 256):
+    for (Hq, Hkv) in ((8, 8), (8, 2), (12, 2), (16, 2), (16, 1)):
+        MATRIX.append((D, Hq, Hkv))
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", MATRIX)
+def test_matrix_ragged_with_nan_tail(D, Hq, Hkv):
+    tt = {64: 64, 128: 32, 256: 16}[D]
+    lens = [1, tt - 1, tt + 1, 3 * tt + 5, 517]
+    S_max = 600
+    say(f"[parity] matrix D={D} Hq={Hq} Hkv={Hkv} lens={lens}")
+    case = W.contig_case(len(lens), Hq, Hkv, D, S_max, seq_lens=lens, seed=D + Hq + Hkv,
+                         tail="nan")
+    dc = DeviceCase(case)
+    ref = oracle_out(case)
+    for splits in (0, 1, 3):
+        compare(dc.run_host(splits), ref, f"D={D} G={Hq // Hkv} splits={splits}")
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 7, 64, 10000])
+def test_forced_split_counts(splits):
+    say(f"[parity] forced splits {splits}")
+    case = W.contig_case(2, 24, 4, 256, 2048, seq_lens=[2048, 1500], seed=21, scale=1 / 16)
+    compare(DeviceCase(case).run_host(splits), oracle_out(case), f"splits={splits}")
+
+
+def test_length_zero_and_one():
+    say("[parity] len 0 / len 1")
+    case = W.contig_case(3, 8, 2, 128, 64, seq_lens=[0, 1, 0], seed=22, tail="nan")
+    dc = DeviceCase(case)
+    for splits in (0, 1, 2):
+        out = dc.run_host(splits)
+        assert np.all(out[0] == 0) and np.all(out[2] == 0)
+        v0 = W.bf16_bits_to_f32(case.v[1, :, 0, :]).reshape(2, 128)
+        assert np.array_equal(out[1], np.repeat(v0, 4, axis=0)), "len 1 must return V[0] exactly"
+
+
+def test_large_scores():
+    say("[parity] large scores")
+    case = W.contig_case(1, 8, 1, 128, 700, seed=23, scale=2.0)
+    compare(DeviceCase(case).run_host(), oracle_out(case), "scale=2")
+
+
+def test_peaky_small():
+    say("[parity] peaky small")
+    case = W.peaky_case(2, 16, 2, 128, 3000, frac=0.01, mul=8, seed=24)
+    compare(DeviceCase(case).run_host(), oracle_out(case), "peaky")
+
+
+def test_batch_zero():
+    case = W.contig_case(1, 8, 2, 64, 16, seed=25)
+    dc = DeviceCase(case)
+    out = torch.empty((0, 8, 64), dtype=torch.float32, device="cuda")
+    q0 = dc.q[:0]
+    gd.gqa_decode(q0, dc.k[:0], dc.v[:0], dc.seq_lens[:0], case.scale, out=out)
+    torch.cuda.synchronize()
+
+
+def test_side_stream_and_reused_workspace():
+    say("[parity] side stream")
+    case = W.contig_case(2, 8, 2, 128, 900, seq_lens=[900, 333], seed=26)
+    dc = DeviceCase(case)
+    ref = oracle_out(case)
+    need = gd.gqa_decode_workspace_bytes(2, 8, 2, 128, 900, 0, 0)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        outs = [dc.run(0, workspace=ws, stream=s) for _ in range(2)]
+    s.synchronize()
+    for o in outs:
+        compare(o.cpu().numpy(), ref, "side stream")
+
+
+# ------------------------------------------------------------------ paged
+@pytest.mark.parametrize("ps", [16, 32, 64, 48])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_paged_matrix(ps, D):
+    say(f"[parity] paged ps={ps} D={D}")
+    lens = [1, ps - 1, ps, ps + 1, 5 * ps + 3, 700]
+    case = W.paged_case(len(lens), 16, 4, D, ps, 200, seq_lens=lens, max_len=704, seed=ps + D)
+    dc = DeviceCase(case)
+    ref = oracle_out(case)
+    for splits in (0, 1, 5):
+        compare(dc.run_host(splits), ref, f"paged ps={ps} D={D} splits={splits}")
+
+
+def test_paged_equals_contiguous_bitwise():
+    """Pages holding the same rows as a contiguous cache give the same bits (same plan)."""
+    say("[parity] paged == contiguous")
+    B, Hq, Hkv, D, ps, S = 3, 32, 8, 128, 32, 1024
+    c = W.contig_case(B, Hq, Hkv, D, S, seq_lens=[1024, 77, 500], seed=27)
+    pages = S // ps
+    k_pool = np.zeros((B * pages, Hkv, ps, D), np.uint16)
+    v_pool = np.zeros_like(k_pool)
+    table = np.zeros((B, pages), np.int32)
+    for b in range(B):
+        for i in range(pages):
+            pg = b * pages + i
+            k_pool[pg] = c.k[b, :, i * ps:(i + 1) * ps]
+            v_pool[pg] = c.v[b, :, i * ps:(i + 1) * ps]
+            table[b, i] = pg
+    p = W.Case("paged_copy", B, Hq, Hkv, D, c.scale, c.q, k_pool, v_pool, c.seq_lens, table, ps)
+    a = DeviceCase(c).run_host()
+    b = DeviceCase(p).run_host()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_paged_page_permutation_bitwise():
+    say("[parity] page permutation")
+    p = W.paged_case(4, 32, 8, 128, 32, 300, seq_lens=[2000, 31, 1000, 33], max_len=2048,
+                     seed=28)
+    rng = np.random.default_rng(6)
+    perm = rng.permutation(p.num_pages)
+    k2 = np.empty_like(p.k)
+    v2 = np.empty_like(p.v)
+    k2[perm] = p.k
+    v2[perm] = p.v
+    t2 = np.where(p.page_table >= 0, perm[np.maximum(p.page_table, 0)], -1).astype(np.int32)
+    q = W.Case("perm", p.B, p.Hq, p.Hkv, p.D, p.scale, p.q, k2, v2, p.seq_lens, t2, p.page_size)
+    a = DeviceCase(p).run_host()
+    b = DeviceCase(q).run_host()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    compare(a, oracle_out(p), "paged permutation")

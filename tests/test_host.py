@@ -1,0 +1,166 @@
+"""Host-side logic of the C-ABI library, on the CPU (no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_04_amd as gd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_decode.h")
+
+WORKLOAD_SHAPES = [  # (B, Hq, Hkv, D, capacity, page_size)
+    (1, 8, 2, 64, 512, 0),
+    (1, 24, 4, 256, 4096, 0),
+    (16, 32, 4, 128, 16384, 0),
+    (32, 32, 8, 128, 8192, 32),
+    (1, 8, 1, 128, 131072, 0),
+]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gd.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_\w+)\s*\(", text)))
+
+
+def test_header_declares_what_the_binding_exports():
+    assert declared_functions() == sorted(gd.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.gqa_status_string(code)
+    assert b"unknown" in lib.gqa_status_string(99)
+
+
+@pytest.mark.parametrize("shape", WORKLOAD_SHAPES)
+@pytest.mark.parametrize("cu", [256, 304, 80, 1])
+def test_plan_invariants(shape, cu):
+    B, Hq, Hkv, D, cap, ps = shape
+    p = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, 0, cu)
+    assert p.split_tokens % p.tile_tokens == 0
+    assert p.tile_tokens % 16 == 0
+    if ps:
+        assert ps % p.tile_tokens == 0        # one page-table lookup per tile
+    assert p.num_splits * p.split_tokens >= cap
+    assert (p.num_splits - 1) * p.split_tokens < cap  # no split starts past the capacity
+    assert p.grid == B * Hkv * p.num_splits
+    assert p.direct == (p.num_splits == 1)
+    rows = B * Hq * p.num_splits
+    align = lambda x: (x + 255) // 256 * 256
+    exp_ws = 0 if p.direct else align(rows * D * 4) + align(rows * 2 * 4)
+    assert p.workspace_bytes == exp_ws
+    again = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, 0, cu)
+    assert again.as_dict() == p.as_dict()
+
+
+def test_plan_fills_the_device():
+    # one kv head, 131072 keys: enough splits for two workgroups per CU
+    p = gd.gqa_decode_plan(1, 8, 1, 128, 131072, 0, 0, 256)
+    assert p.grid >= 512
+    # the GQA-6 layer (4 kv heads, 4096 keys) cannot give every wave more than one tile
+    p = gd.gqa_decode_plan(1, 24, 4, 256, 4096, 0, 0, 256)
+    assert p.grid == 256 and p.split_tokens == 4 * p.tile_tokens
+    # ragged paged batch: no split longer than 1024 keys
+    p = gd.gqa_decode_plan(32, 32, 8, 128, 8192, 32, 0, 256)
+    assert p.split_tokens <= 1024
+
+
+def test_forced_splits_are_clamped_to_tiles():
+    p = gd.gqa_decode_plan(1, 8, 2, 64, 512, 0, 1000, 256)
+    assert p.num_splits == 512 // p.tile_tokens
+    p = gd.gqa_decode_plan(1, 8, 2, 64, 512, 0, 1, 256)
+    assert p.num_splits == 1 and p.direct == 1 and p.workspace_bytes == 0
+    p = gd.gqa_decode_plan(2, 8, 2, 128, 1000, 0, 7, 256)
+    assert p.num_splits == 7
+
+
+def test_paged_tile_never_straddles_a_page():
+    for ps in (16, 32, 48, 64, 80, 128):
+        for D in (64, 128, 256):
+            p = gd.gqa_decode_plan(4, 8, 2, D, ps * 10, ps, 0, 256)
+            assert ps % p.tile_tokens == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 8, 3, 128, 100, 0, 0, 256), 2),     # Hq % Hkv != 0
+    ((1, 8, 2, 96, 100, 0, 0, 256), 3),      # head_dim 96
+    ((1, 34, 2, 128, 100, 0, 0, 256), 3),    # G = 17
+    ((1, 8, 2, 128, 100, 24, 0, 256), 3),    # page size not a multiple of 16
+    ((1, 8, 2, 128, -1, 0, 0, 256), 2),
+    ((1, 8, 2, 128, 100, 0, -1, 256), 2),
+    ((1, 8, 2, 128, 100, 0, 0, 0), 2),       # no CUs
+])
+def test_plan_rejects(args, code):
+    with pytest.raises(gd.GqaError) as e:
+        gd.gqa_decode_plan(*args)
+    assert e.value.code == code
+
+
+# ---- gqa_decode / gqa_paged_decode argument checks (all fail before any HIP call)
+A = 0x10000  # an aligned fake device address; never dereferenced
+
+
+def call_decode(lib, q=A, k=A, v=A, lens=A, B=1, Hq=8, Hkv=2, D=128, S=64, scale=0.1, out=A,
+                ws=A, ws_bytes=1 << 30, splits=2):
+    return lib.gqa_decode(q, k, v, lens, B, Hq, Hkv, D, S, scale, out, ws, ws_bytes, splits, None)
+
+
+def call_paged(lib, q=A, k=A, v=A, lens=A, table=A, B=1, Hq=8, Hkv=2, D=128, ps=32, P=10, mp=4,
+               scale=0.1, out=A, ws=A, ws_bytes=1 << 30, splits=2):
+    return lib.gqa_paged_decode(q, k, v, lens, table, B, Hq, Hkv, D, ps, P, mp, scale, out, ws,
+                                ws_bytes, splits, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(lens=None), 1),
+    (dict(out=None), 1), (dict(ws=None), 1),
+    (dict(Hq=9), 2), (dict(Hkv=0), 2), (dict(B=-1), 2), (dict(S=-1), 2), (dict(splits=-1), 2),
+    (dict(scale=float("nan")), 2), (dict(scale=float("inf")), 2), (dict(S=1 << 30), 2),
+    (dict(D=32), 3), (dict(D=80), 3), (dict(Hq=64, Hkv=2), 3),
+    (dict(q=A + 8), 4), (dict(k=A + 2), 4), (dict(v=A + 4), 4), (dict(out=A + 4), 4),
+    (dict(lens=A + 2), 4), (dict(ws=A + 8), 4),
+    (dict(ws_bytes=16), 5),
+])
+def test_decode_rejects(lib, kw, code):
+    assert call_decode(lib, **kw) == code
+
+
+def test_decode_workspace_exact_size_accepted_without_launch(lib):
+    need = gd.gqa_decode_plan(1, 8, 2, 128, 64, 0, 2, 256).workspace_bytes
+    assert call_decode(lib, ws_bytes=need - 1) == 5
+    # B = 0 passes every check and launches nothing
+    assert call_decode(lib, B=0, ws_bytes=need) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(table=None), 1), (dict(q=None), 1),
+    (dict(ps=0), 2), (dict(P=0), 2), (dict(mp=0), 2), (dict(Hq=7), 2),
+    (dict(ps=24), 3), (dict(D=48), 3),
+    (dict(table=A + 2), 4), (dict(k=A + 8), 4),
+    (dict(ws_bytes=0), 5),
+])
+def test_paged_rejects(lib, kw, code):
+    assert call_paged(lib, **kw) == code
+
+
+def test_workspace_bytes_matches_plan_when_forced(lib):
+    for shape in WORKLOAD_SHAPES:
+        B, Hq, Hkv, D, cap, ps = shape
+        for s in (1, 3, 16):
+            assert gd.gqa_decode_workspace_bytes(B, Hq, Hkv, D, cap, ps, s) == \
+                gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, s, 256).workspace_bytes
+    with pytest.raises(gd.GqaError):
+        gd.gqa_decode_workspace_bytes(1, 8, 3, 128, 100, 0, 2)
