@@ -39,7 +39,8 @@ class GqaError(RuntimeError):
 class Plan(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int), ("split_tokens", ctypes.c_int),
                 ("tile_tokens", ctypes.c_int), ("waves", ctypes.c_int), ("grid", ctypes.c_int),
-                ("direct", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+                ("direct", ctypes.c_int), ("fused", ctypes.c_int), ("fold_group", ctypes.c_int),
+                ("fold_groups", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -130,7 +131,8 @@ def _workspace(workspace, need, device):
     if need == 0:
         return None, 0
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        # zero-filled: the library's arrival counters start at zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=device)
     return workspace, workspace.numel() * workspace.element_size()
 
 

@@ -10,7 +10,7 @@
 //                      workgroup emits one unnormalised partial per query head
 //                      (or the final output when there is a single split).
 //   gqa_combine_kernel folds the S partials of each (b, h) with the
-//                      log-sum-exp rescale, splits in ascending order.
+//                      log-sum-exp rescale in a fixed order.
 //
 // Layout of the work inside one wave (64 lanes, r = lane % 16, grp = lane / 16):
 //
@@ -63,20 +63,29 @@ constexpr int kWaves = 4;           // waves per workgroup
 constexpr int kMaxHeadsPerKv = 16;  // G is padded to the MFMA's 16 columns
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords (gfx9 family)
 
+// Partials of one (sequence, kv head) are blocks of [G][D] (acc) and [G][2]
+// (m in log2 units, l): the split partials at part_acc/part_ml, indexed
+// [b*Hkv + kvh][split], and the group partials of the two-level fold at
+// grp_acc/grp_ml, indexed [b*Hkv + kvh][group].
 struct SplitArgs {
     const uint16_t *q;
     const uint16_t *k;
     const uint16_t *v;
     const int32_t *seq_lens;
     const int32_t *page_table;  // paged only
-    float *part_acc;            // [B][Hq][S][D]
-    float *part_ml;             // [B][Hq][S][2]  (m in log2 units, l)
-    float *out;                 // [B][Hq][D]     (direct mode)
+    float *part_acc;
+    float *part_ml;
+    float *grp_acc;
+    float *grp_ml;
+    unsigned int *counters;     // [B*Hkv][fold_groups + 1], zero between calls
+    float *out;                 // [B][Hq][D]
     int B, Hq, Hkv, G;
     int S_max;                  // contiguous capacity
     int page_size, max_pages;   // paged
     int num_pages;              // paged
     int num_splits, split_tokens;
+    int fused;                  // 1: the last workgroups fold the partials in this kernel
+    int fold_group, fold_groups;
     float qk_scale_log2;        // scale * log2(e)
 };
 
@@ -84,7 +93,7 @@ struct CombineArgs {
     const float *part_acc;
     const float *part_ml;
     float *out;
-    int Hq, num_splits;
+    int D, G, Hq, num_splits;
 };
 
 __device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
@@ -230,8 +239,64 @@ template <int D>
 struct FoldLds {
     float m[kWaves][kMaxHeadsPerKv];
     float l[kWaves][kMaxHeadsPerKv];
-    float acc[kWaves][kMaxHeadsPerKv][D];
+    float acc[kWaves][kMaxHeadsPerKv][D + 4];  // +4 floats: consecutive rows start on other banks
+    int last;
 };
+
+// Fold n partial blocks ([G][D] acc, [G][2] ml, block i at acc + i*G*D and
+// ml + i*G*2) with the log-sum-exp rescale, blocks in ascending order.  The
+// result goes to out rows out[g*D ..] normalised (final) or, if out is null,
+// to the partial block dst_acc / dst_ml.  All threads of the workgroup take
+// part; each owns 4 consecutive dims of one head.
+template <int D>
+__device__ __forceinline__ void fold_blocks(const float *acc, const float *ml, int n, int G,
+                                            float *dst_acc, float *dst_ml, float *out) {
+    for (int col = threadIdx.x; col < G * (D / 4); col += 64 * kWaves) {
+        const int g = col / (D / 4);
+        const int d = 4 * (col - g * (D / 4));
+        float M = -INFINITY;
+        for (int i = 0; i < n; ++i) M = fmaxf(M, ml[(i * G + g) * 2]);
+        f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+        float L = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll 8
+            for (int i = 0; i < n; ++i) {
+                const float w = __builtin_amdgcn_exp2f(ml[(i * G + g) * 2] - M);
+                L += w * ml[(i * G + g) * 2 + 1];
+                sum += w * *reinterpret_cast<const f32x4_t *>(acc + ((size_t)i * G + g) * D + d);
+            }
+        }
+        if (out != nullptr) {
+            *reinterpret_cast<f32x4_t *>(out + (size_t)g * D + d) =
+                L > 0.f ? sum / L : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        } else {
+            *reinterpret_cast<f32x4_t *>(dst_acc + (size_t)g * D + d) = sum;
+            if (d == 0) {
+                dst_ml[g * 2] = M;
+                dst_ml[g * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+// Cross-workgroup arrival: returns true (in every thread) for the last of
+// `expected` workgroups to reach `counter`, after making this workgroup's
+// stores visible and, for the last one, acquiring everyone else's.  The last
+// arrival resets the counter to zero for the next call.
+template <int D>
+__device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int expected, FoldLds<D> &lds) {
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned int t = atomicAdd(counter, 1u);
+        lds.last = t + 1 == expected;
+        if (t + 1 == expected) *counter = 0u;
+    }
+    __syncthreads();
+    const bool last = lds.last;
+    if (last) __threadfence();
+    return last;
+}
 
 template <int D, int NB, bool PAGED>
 __global__ __launch_bounds__(64 * kWaves) void gqa_split_kernel(const SplitArgs a) {
@@ -326,62 +391,154 @@ __global__ __launch_bounds__(64 * kWaves) void gqa_split_kernel(const SplitArgs 
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int e = 0; e < S::DPL; ++e)
-                    lds.acc[wave][r][16 * S::DPL * c + S::DPL * (4 * grp + i) + e] = st.acc[c * S::DPL + e][i];
+                for (int e = 0; e < S::DPL; e += 4) {
+                    const f32x4_t x = {st.acc[c * S::DPL + e][i], st.acc[c * S::DPL + e + 1][i],
+                                       st.acc[c * S::DPL + e + 2][i], st.acc[c * S::DPL + e + 3][i]};
+                    *reinterpret_cast<f32x4_t *>(&lds.acc[wave][r][16 * S::DPL * c + S::DPL * (4 * grp + i) + e]) = x;
+                }
     }
     __syncthreads();
 
-    // Fold the waves in ascending order and emit this split's result.
+    // Fold the waves in ascending order: this split's partial (or the output).
     const int G = a.G;
-    const bool direct = a.num_splits == 1;
-    for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
-        const int g = idx / D, d = idx - (idx / D) * D;
+    const int nsplit = a.num_splits;
+    const bool direct = nsplit == 1;
+    float *out_rows = a.out + ((size_t)b * a.Hq + (size_t)kvh * G) * D;
+    float *my_acc = a.part_acc + ((size_t)bk * nsplit + split) * G * D;
+    float *my_ml = a.part_ml + ((size_t)bk * nsplit + split) * G * 2;
+    for (int col = threadIdx.x; col < G * (D / 4); col += 64 * kWaves) {
+        const int g = col / (D / 4);
+        const int d = 4 * (col - g * (D / 4));
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds.m[w][g]);
-        float L = 0.f, ACC = 0.f;
+        float L = 0.f;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         if (M != -INFINITY) {
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
                 const float sw = __builtin_amdgcn_exp2f(lds.m[w][g] - M);
                 L += sw * lds.l[w][g];
-                ACC += sw * lds.acc[w][g][d];
+                acc += sw * *reinterpret_cast<const f32x4_t *>(&lds.acc[w][g][d]);
             }
         }
-        const size_t h = (size_t)kvh * G + g;
         if (direct) {
-            a.out[((size_t)b * a.Hq + h) * D + d] = L > 0.f ? ACC / L : 0.f;
+            *reinterpret_cast<f32x4_t *>(out_rows + (size_t)g * D + d) =
+                L > 0.f ? acc / L : f32x4_t{0.f, 0.f, 0.f, 0.f};
         } else {
-            const size_t row = ((size_t)b * a.Hq + h) * a.num_splits + split;
-            a.part_acc[row * D + d] = ACC;
+            *reinterpret_cast<f32x4_t *>(my_acc + (size_t)g * D + d) = acc;
             if (d == 0) {
-                a.part_ml[row * 2 + 0] = M;
-                a.part_ml[row * 2 + 1] = L;
+                my_ml[g * 2] = M;
+                my_ml[g * 2 + 1] = L;
             }
         }
     }
+    if (direct || !a.fused) return;
+
+    // Two-level fold across workgroups: the last split to finish in each group
+    // of fold_group splits folds that group; the last group to finish folds the
+    // groups into the output (one level when there is a single group).
+    const int ngroups = a.fold_groups;
+    const int grp_id = split / a.fold_group;
+    const int g0 = grp_id * a.fold_group;
+    const int gn = min(a.fold_group, nsplit - g0);
+    unsigned int *ctr = a.counters + (size_t)bk * (ngroups + 1);
+    if (!arrive_last<D>(ctr + grp_id, (unsigned)gn, lds)) return;
+    const float *src_acc = a.part_acc + ((size_t)bk * nsplit + g0) * G * D;
+    const float *src_ml = a.part_ml + ((size_t)bk * nsplit + g0) * G * 2;
+    if (ngroups == 1) {
+        fold_blocks<D>(src_acc, src_ml, gn, G, nullptr, nullptr, out_rows);
+        return;
+    }
+    fold_blocks<D>(src_acc, src_ml, gn, G, a.grp_acc + ((size_t)bk * ngroups + grp_id) * G * D,
+                   a.grp_ml + ((size_t)bk * ngroups + grp_id) * G * 2, nullptr);
+    if (!arrive_last<D>(ctr + ngroups, (unsigned)ngroups, lds)) return;
+    fold_blocks<D>(a.grp_acc + (size_t)bk * ngroups * G * D, a.grp_ml + (size_t)bk * ngroups * G * 2,
+                   ngroups, G, nullptr, nullptr, out_rows);
 }
 
-// One workgroup of D threads per (b, h): thread d folds acc[., d] over the
-// splits in ascending order.
-template <int D>
-__global__ __launch_bounds__(D) void gqa_combine_kernel(const CombineArgs a) {
-    const size_t bh = blockIdx.x;
-    const int d = threadIdx.x;
+// Combine: one workgroup of 256 threads per (b, h, chunk of 4*NCOL dims).
+// Thread (sg, c) owns dims 4c .. 4c+3 of the chunk and the splits s with
+// s % NSG == sg (NSG = 256 / NCOL).  It issues the loads of all its splits
+// before using any (one memory round trip), folds them in ascending s with a
+// running max, and the NSG groups are then folded through LDS in ascending
+// order: a fixed summation order, so the result is bit-reproducible.
+constexpr int kCombineThreads = 256;
+
+template <int NCOL>
+__global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const CombineArgs a) {
+    constexpr int NSG = kCombineThreads / NCOL;
+    constexpr int U = 4;  // splits per thread per round of loads
+    const int D = a.D;
+    const int chunks = D / (4 * NCOL);
+    const size_t bh = blockIdx.x / chunks;
+    const int d0 = (blockIdx.x % chunks) * 4 * NCOL;
+    const int c = threadIdx.x % NCOL;
+    const int sg = threadIdx.x / NCOL;
     const int S = a.num_splits;
-    const float *ml = a.part_ml + bh * S * 2;
-    const float *acc = a.part_acc + bh * S * D + d;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.f, ACC = 0.f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < S; ++s) {
-            const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-            L += w * ml[2 * s + 1];
-            ACC += w * acc[(size_t)s * D];
+    const int G = a.G;
+    const size_t b = bh / a.Hq;
+    const int h = (int)(bh % a.Hq);
+    const size_t bk = b * (a.Hq / G) + h / G;   // b * Hkv + kvh
+    const int g = h % G;
+    // split s of head g: acc at ((bk*S + s)*G + g)*D, ml at ((bk*S + s)*G + g)*2
+    const float *ml = a.part_ml + (bk * S * G + g) * 2;
+    const float *acc = a.part_acc + (bk * S * G + g) * D + d0 + 4 * c;
+    const size_t ml_stride = (size_t)G * 2, acc_stride = (size_t)G * D;
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4_t o_run = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = sg; s0 < S; s0 += U * NSG) {
+        float mv[U], lv[U];
+        f32x4_t av[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u * NSG;
+            mv[u] = -INFINITY;
+            lv[u] = 0.f;
+            av[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (s < S) {
+                mv[u] = ml[s * ml_stride];
+                lv[u] = ml[s * ml_stride + 1];
+                av[u] = *reinterpret_cast<const f32x4_t *>(acc + s * acc_stride);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float m_new = fmaxf(m_run, mv[u]);
+            if (m_new != -INFINITY) {
+                const float wa = __builtin_amdgcn_exp2f(m_run - m_new);
+                const float wb = __builtin_amdgcn_exp2f(mv[u] - m_new);
+                l_run = l_run * wa + lv[u] * wb;
+                o_run = o_run * wa + av[u] * wb;
+                m_run = m_new;
+            }
         }
     }
-    a.out[bh * D + d] = L > 0.f ? ACC / L : 0.f;
+
+    __shared__ f32x4_t part[NSG][NCOL];
+    __shared__ float mpart[NSG], lpart[NSG];
+    part[sg][c] = o_run;
+    if (c == 0) {
+        mpart[sg] = m_run;
+        lpart[sg] = l_run;
+    }
+    __syncthreads();
+    if (sg == 0) {
+        float M = -INFINITY;
+        for (int i = 0; i < NSG; ++i) M = fmaxf(M, mpart[i]);
+        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+        float L = 0.f;
+        if (M != -INFINITY) {
+            for (int i = 0; i < NSG; ++i) {
+                const float w = __builtin_amdgcn_exp2f(mpart[i] - M);
+                L += w * lpart[i];
+                o += w * part[i][c];
+            }
+        }
+        *reinterpret_cast<f32x4_t *>(a.out + bh * D + d0 + 4 * c) =
+            L > 0.f ? o / L : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 }
 
 // ------------------------------------------------------------------ host side
@@ -413,6 +570,50 @@ gqa_status_t device_cu_count(int *out) {
     return GQA_OK;
 }
 
+struct WorkspaceLayout {
+    size_t part_acc, part_ml, grp_acc, grp_ml, counters, total;
+};
+
+// The arrival counters of the fused fold live in a fixed area at the start of
+// every workspace that no other region ever overlaps, so a zero-filled
+// workspace stays valid across calls with different shapes: each call leaves
+// the counters it used at zero.
+constexpr size_t kCounterBytes = 65536;
+constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(unsigned int));
+
+// Byte offsets of the workspace regions (all 256-byte aligned).
+WorkspaceLayout workspace_layout(int B, int Hq, int Hkv, int D, int S, int fused, int groups) {
+    (void)Hkv;
+    WorkspaceLayout w{};
+    const size_t rows = (size_t)B * Hq;
+    size_t off = 0;
+    w.counters = 0;
+    if (fused) off += kCounterBytes;
+    w.part_acc = off;
+    off += align_up(rows * S * D * sizeof(float), 256);
+    w.part_ml = off;
+    off += align_up(rows * S * 2 * sizeof(float), 256);
+    w.grp_acc = off;
+    w.grp_ml = off;
+    if (fused && groups > 1) {
+        off += align_up(rows * groups * D * sizeof(float), 256);
+        w.grp_ml = off;
+        off += align_up(rows * groups * 2 * sizeof(float), 256);
+    }
+    w.total = off;
+    return w;
+}
+
+// The in-kernel fold is off unless GQA_DECODE_FUSED=1: on gfx950 each
+// workgroup's device-scope release/acquire is an L2 writeback/invalidate of
+// its XCD, costing microseconds that serialise per XCD, which is far more
+// than the separate combine launch it saves.
+int env_fused() {
+    const char *s = getenv("GQA_DECODE_FUSED");
+    if (s == nullptr || *s == '\0') return 0;
+    return atoi(s) != 0 ? 1 : 0;
+}
+
 int env_splits() {
     const char *s = getenv("GQA_DECODE_SPLITS");
     if (s == nullptr || *s == '\0') return 0;
@@ -422,11 +623,19 @@ int env_splits() {
 
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
-template <int D>
 hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const float *part_ml,
-                          float *out, int B, int Hq, hipStream_t stream) {
-    CombineArgs ca{part_acc, part_ml, out, Hq, plan.num_splits};
-    hipLaunchKernelGGL(gqa_combine_kernel<D>, dim3((unsigned)(B * Hq)), dim3(D), 0, stream, ca);
+                          float *out, int B, int Hq, int Hkv, int D, hipStream_t stream) {
+    CombineArgs ca{part_acc, part_ml, out, D, Hq / Hkv, Hq, plan.num_splits};
+    // Narrow dim chunks (more workgroups, fewer splits per thread) when there
+    // are few heads and many splits.
+    const int64_t heads = (int64_t)B * Hq;
+    if (heads * (D / 64) >= 256 || plan.num_splits <= 64) {
+        hipLaunchKernelGGL(gqa_combine_kernel<16>, dim3((unsigned)(heads * (D / 64))), dim3(kCombineThreads), 0, stream, ca);
+    } else if (heads * (D / 32) >= 256 || plan.num_splits <= 256) {
+        hipLaunchKernelGGL(gqa_combine_kernel<8>, dim3((unsigned)(heads * (D / 32))), dim3(kCombineThreads), 0, stream, ca);
+    } else {
+        hipLaunchKernelGGL(gqa_combine_kernel<4>, dim3((unsigned)(heads * (D / 16))), dim3(kCombineThreads), 0, stream, ca);
+    }
     return hipGetLastError();
 }
 
@@ -454,9 +663,17 @@ hipError_t launch_split(const gqa_plan_t &plan, const SplitArgs &a, hipStream_t 
 gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, void *workspace,
                  hipStream_t stream) {
     if (!plan.direct) {
-        const size_t acc_bytes = align_up((size_t)a.B * a.Hq * plan.num_splits * D * sizeof(float), 256);
-        a.part_acc = static_cast<float *>(workspace);
-        a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + acc_bytes);
+        WorkspaceLayout w = workspace_layout(a.B, a.Hq, a.Hkv, D, plan.num_splits, plan.fused,
+                                             plan.fold_groups);
+        char *base = static_cast<char *>(workspace);
+        a.part_acc = reinterpret_cast<float *>(base + w.part_acc);
+        a.part_ml = reinterpret_cast<float *>(base + w.part_ml);
+        a.grp_acc = reinterpret_cast<float *>(base + w.grp_acc);
+        a.grp_ml = reinterpret_cast<float *>(base + w.grp_ml);
+        a.counters = reinterpret_cast<unsigned int *>(base + w.counters);
+        a.fused = plan.fused;
+        a.fold_group = plan.fold_group;
+        a.fold_groups = plan.fold_groups;
     }
     hipError_t e = hipSuccess;
     switch (D) {
@@ -466,20 +683,17 @@ gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, void *
         default: return GQA_ERR_UNSUPPORTED;
     }
     if (e != hipSuccess) return GQA_ERR_HIP;
-    if (plan.direct) return GQA_OK;
-    switch (D) {
-        case 64: e = launch_combine<64>(plan, a.part_acc, a.part_ml, a.out, a.B, a.Hq, stream); break;
-        case 128: e = launch_combine<128>(plan, a.part_acc, a.part_ml, a.out, a.B, a.Hq, stream); break;
-        default: e = launch_combine<256>(plan, a.part_acc, a.part_ml, a.out, a.B, a.Hq, stream); break;
-    }
+    if (plan.direct || plan.fused) return GQA_OK;
+    e = launch_combine(plan, a.part_acc, a.part_ml, a.out, a.B, a.Hq, a.Hkv, D, stream);
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
 gqa_status_t check_common(const void *q, const void *k, const void *v, const int32_t *seq_lens,
                           const float *out, int B, int Hq, int Hkv, int D, float scale) {
-    if (!q || !k || !v || !seq_lens || !out) return GQA_ERR_NULL;
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !isfinite(scale)) return GQA_ERR_SHAPE;
     if (!supported_dim(D) || Hq / Hkv > kMaxHeadsPerKv) return GQA_ERR_UNSUPPORTED;
+    if (B == 0) return GQA_OK;  // nothing is read or written
+    if (!q || !k || !v || !seq_lens || !out) return GQA_ERR_NULL;
     if ((int64_t)B * Hq * D > INT32_MAX) return GQA_ERR_SHAPE;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
         misaligned(seq_lens, 4))
@@ -543,11 +757,21 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
     if (grid > INT32_MAX) return GQA_ERR_SHAPE;
     plan->grid = (int)grid;
     plan->direct = S == 1 ? 1 : 0;
-    plan->workspace_bytes = 0;
-    if (!plan->direct) {
-        const size_t rows = (size_t)B * Hq * S;
-        plan->workspace_bytes = align_up(rows * D * sizeof(float), 256) + align_up(rows * 2 * sizeof(float), 256);
+    plan->fused = plan->direct ? 0 : env_fused();
+    // Fold groups: one level up to 8 splits, else about sqrt(S) splits per
+    // group and about sqrt(S) groups, so no workgroup folds many blocks.
+    int fg = S;
+    if (S > 8) {
+        fg = 1;
+        while (fg * fg < S) ++fg;
     }
+    plan->fold_group = fg;
+    plan->fold_groups = (S + fg - 1) / fg;
+    if (plan->fused && (int64_t)B * Hkv * (plan->fold_groups + 1) > kMaxCounters)
+        plan->fused = 0;  // too many (sequence, kv head) pairs for the counter area
+    plan->workspace_bytes = 0;
+    if (!plan->direct)
+        plan->workspace_bytes = workspace_layout(B, Hq, Hkv, D, S, plan->fused, plan->fold_groups).total;
     return GQA_OK;
 }
 
@@ -565,6 +789,7 @@ gqa_status_t gqa_decode(const void *q, const void *k_cache, const void *v_cache,
     gqa_status_t s = check_common(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, scale);
     if (s != GQA_OK) return s;
     if (S_max < 0 || num_splits < 0) return GQA_ERR_SHAPE;
+    if (B == 0) return GQA_OK;
     if (((int64_t)S_max + 64) * D * 2 > INT32_MAX) return GQA_ERR_SHAPE;  // 32-bit buffer offsets
     if (workspace != nullptr && misaligned(workspace, 16)) return GQA_ERR_ALIGN;
     gqa_plan_t plan;
@@ -594,6 +819,7 @@ gqa_status_t gqa_paged_decode(const void *q, const void *k_pool, const void *v_p
                               int num_splits, hipStream_t stream) {
     gqa_status_t s = check_common(q, k_pool, v_pool, seq_lens, out, B, Hq, Hkv, D, scale);
     if (s != GQA_OK) return s;
+    if (B == 0) return (page_size > 0 && page_size % 16 == 0) ? GQA_OK : GQA_ERR_UNSUPPORTED;
     if (page_table == nullptr) return GQA_ERR_NULL;
     if (misaligned(page_table, 4)) return GQA_ERR_ALIGN;
     if (page_size <= 0 || num_pages <= 0 || max_pages <= 0 || num_splits < 0) return GQA_ERR_SHAPE;

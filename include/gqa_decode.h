@@ -31,6 +31,9 @@
  *     0 <= seq_lens[b] <= capacity, and (paged) page_table[b][i] in
  *     [0, num_pages) for i < ceil(seq_lens[b] / page_size).  Entries past that
  *     are never read.  A sequence of length 0 yields a zero output row.
+ *     Out-of-range lengths and page ids are clamped on the device so that no
+ *     access leaves the buffers; the output for such inputs is unspecified.
+ *   - B = 0 is a no-op that reads no pointer (they may be NULL).
  *   - Results are bit-identical from run to run for the same inputs, device
  *     and plan (fixed fold orders, no atomics in the arithmetic).  Different
  *     split counts re-associate the sums and may differ in the last bits.
@@ -65,6 +68,9 @@ typedef struct gqa_plan {
     int waves;              /* waves (of 64 lanes) per workgroup */
     int grid;               /* workgroups of the split kernel: B * Hkv * S */
     int direct;             /* 1: S == 1, the split kernel writes `out` itself */
+    int fused;              /* 1: the split kernel also folds the partials (one launch) */
+    int fold_group;         /* splits folded together at the first fold level */
+    int fold_groups;        /* first-level groups (1 = a single fold level) */
     size_t workspace_bytes; /* scratch the call needs (0 when direct) */
 } gqa_plan_t;
 
@@ -97,6 +103,10 @@ size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int max_
  *   out      fp32 [B][Hq][head_dim]  (written)
  *   workspace: at least gqa_decode_workspace_bytes(B, Hq, Hkv, head_dim,
  *              S_max, 0, num_splits) bytes; may be NULL when that is 0.
+ *              It must be zero-filled before its first use; every call
+ *              leaves it in a state fit for the next call (its arrival
+ *              counters back at zero), so calls that share one workspace
+ *              must not overlap in time.
  *   num_splits: 0 = heuristic, > 0 = forced.
  */
 gqa_status_t gqa_decode(const void *q, const void *k_cache, const void *v_cache,

@@ -66,7 +66,7 @@ def test_matrix_ragged_with_nan_tail(D, Hq, Hkv):
         compare(dc.run_host(splits), ref, f"D={D} G={Hq // Hkv} splits={splits}")
 
 
-@pytest.mark.parametrize("splits", [0, 1, 2, 7, 64, 10000])
+@pytest.mark.parametrize("splits", [0, 1, 2, 7, 9, 64, 100, 10000])
 def test_forced_split_counts(splits):
     say(f"[parity] forced splits {splits}")
     case = W.contig_case(2, 24, 4, 256, 2048, seq_lens=[2048, 1500], seed=21, scale=1 / 16)
@@ -111,7 +111,7 @@ def test_side_stream_and_reused_workspace():
     dc = DeviceCase(case)
     ref = oracle_out(case)
     need = gd.gqa_decode_workspace_bytes(2, 8, 2, 128, 900, 0, 0)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         outs = [dc.run(0, workspace=ws, stream=s) for _ in range(2)]
@@ -170,3 +170,42 @@ def test_paged_page_permutation_bitwise():
     b = DeviceCase(q).run_host()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     compare(a, oracle_out(p), "paged permutation")
+
+
+# ------------------------------------------------------------------ fold paths and workspace reuse
+@pytest.mark.parametrize("splits", [0, 9, 100])
+def test_in_kernel_fold_path(monkeypatch, splits):
+    """GQA_DECODE_FUSED=1 folds the partials inside the split kernel (one or two levels);
+    both paths match the oracle and each is bit-exact across runs."""
+    say(f"[parity] in-kernel fold, splits={splits}")
+    case = W.contig_case(2, 24, 4, 256, 2048, seq_lens=[2048, 999], seed=29, scale=1 / 16)
+    dc = DeviceCase(case)
+    ref = oracle_out(case)
+    two_kernel = dc.run_host(splits)
+    monkeypatch.setenv("GQA_DECODE_FUSED", "1")
+    assert gd.gqa_decode_plan(2, 24, 4, 256, 2048, 0, splits).fused == 1
+    fused = [dc.run_host(splits) for _ in range(2)]
+    monkeypatch.delenv("GQA_DECODE_FUSED")
+    compare(two_kernel, ref, "two kernels")
+    compare(fused[0], ref, "fused")
+    assert np.array_equal(fused[0].view(np.uint32), fused[1].view(np.uint32))
+
+
+def test_shared_workspace_across_plans(monkeypatch):
+    """One zero-filled workspace serves in-kernel-fold calls with different plans back to back."""
+    say("[parity] shared workspace")
+    monkeypatch.setenv("GQA_DECODE_FUSED", "1")
+    a = W.contig_case(1, 8, 1, 128, 20000, seed=30)          # many splits, two fold levels
+    b = W.contig_case(3, 16, 4, 64, 700, seq_lens=[700, 5, 300], seed=31)
+    ws = torch.zeros(1 << 24, dtype=torch.uint8, device="cuda")
+    da, db = DeviceCase(a), DeviceCase(b)
+    ra, rb = oracle_out(a), oracle_out(b)
+    for _ in range(3):
+        oa = da.run(0, workspace=ws)
+        ob = db.run(3, workspace=ws)
+        oc = da.run(37, workspace=ws)
+        torch.cuda.synchronize()
+        compare(oa.cpu().numpy(), ra, "plan A")
+        compare(ob.cpu().numpy(), rb, "plan B")
+        compare(oc.cpu().numpy(), ra, "plan A, 37 splits")
+    assert not torch.any(ws[:65536]), "the counter area must be back at zero after each call"

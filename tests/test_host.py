@@ -24,6 +24,22 @@ def lib():
     return gd.load()
 
 
+def expected_workspace(B, Hq, Hkv, D, p):
+    """Split partials [B*Hq*S] x (D + 2) floats, group partials [B*Hq*groups] x (D + 2) floats
+    when there are two fold levels, and a fixed 64 KiB counter area in front when fused;
+    every region rounded up to 256 bytes."""
+    if p.direct:
+        return 0
+    align = lambda x: (x + 255) // 256 * 256
+    rows = B * Hq
+    total = align(rows * p.num_splits * D * 4) + align(rows * p.num_splits * 2 * 4)
+    if p.fused:
+        total += 65536  # fixed counter area at the front
+        if p.fold_groups > 1:
+            total += align(rows * p.fold_groups * D * 4) + align(rows * p.fold_groups * 2 * 4)
+    return total
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -58,10 +74,14 @@ def test_plan_invariants(shape, cu):
     assert (p.num_splits - 1) * p.split_tokens < cap  # no split starts past the capacity
     assert p.grid == B * Hkv * p.num_splits
     assert p.direct == (p.num_splits == 1)
-    rows = B * Hq * p.num_splits
-    align = lambda x: (x + 255) // 256 * 256
-    exp_ws = 0 if p.direct else align(rows * D * 4) + align(rows * 2 * 4)
-    assert p.workspace_bytes == exp_ws
+    assert p.fused == 0   # the in-kernel fold is opt-in (GQA_DECODE_FUSED=1)
+    assert p.fold_group * p.fold_groups >= p.num_splits
+    assert (p.fold_groups - 1) * p.fold_group < p.num_splits
+    if p.num_splits <= 8:
+        assert p.fold_groups == 1
+    else:
+        assert p.fold_group * p.fold_group >= p.num_splits
+    assert p.workspace_bytes == expected_workspace(B, Hq, Hkv, D, p)
     again = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, 0, cu)
     assert again.as_dict() == p.as_dict()
 
@@ -141,8 +161,10 @@ def test_decode_rejects(lib, kw, code):
 def test_decode_workspace_exact_size_accepted_without_launch(lib):
     need = gd.gqa_decode_plan(1, 8, 2, 128, 64, 0, 2, 256).workspace_bytes
     assert call_decode(lib, ws_bytes=need - 1) == 5
-    # B = 0 passes every check and launches nothing
+    # B = 0 passes every check and launches nothing, whatever the pointers
     assert call_decode(lib, B=0, ws_bytes=need) == 0
+    assert call_decode(lib, B=0, q=None, k=None, v=None, lens=None, out=None, ws=None) == 0
+    assert call_paged(lib, B=0, q=None, table=None, ws=None) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -164,3 +186,20 @@ def test_workspace_bytes_matches_plan_when_forced(lib):
                 gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, s, 256).workspace_bytes
     with pytest.raises(gd.GqaError):
         gd.gqa_decode_workspace_bytes(1, 8, 3, 128, 100, 0, 2)
+
+
+def test_fused_falls_back_when_counters_do_not_fit(monkeypatch):
+    monkeypatch.setenv("GQA_DECODE_FUSED", "1")
+    p = gd.gqa_decode_plan(4096, 32, 8, 128, 8192, 0, 4, 256)
+    assert p.fold_groups == 1 and p.fused == 0          # 4096*8*2 counters > 16384
+    p = gd.gqa_decode_plan(64, 32, 8, 128, 8192, 0, 4, 256)
+    assert p.fused == 1
+
+
+def test_fused_plan_workspace(monkeypatch):
+    monkeypatch.setenv("GQA_DECODE_FUSED", "1")
+    for shape in WORKLOAD_SHAPES:
+        B, Hq, Hkv, D, cap, ps = shape
+        p = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, 0, 256)
+        assert p.fused == 1
+        assert p.workspace_bytes == expected_workspace(B, Hq, Hkv, D, p)
