@@ -27,6 +27,25 @@ METRIC = "decode-attention µs/call + achieved HBM GB/s (% of peak), GQA-6 hd256
 HBM_PEAK_GBS = 8000.0
 
 
+def measured_traffic(workload):
+    """HBM bytes per split-kernel launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "decode_attention_04_amd", "csrc", "gqa_decode.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != digest:
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    return None if w is None else w.get("hbm_bytes_per_launch")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -37,11 +56,99 @@ def parse():
     ap.add_argument("--rotate-bytes", type=float, default=2.0 * 2**30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the benchmark, copy a 256 MiB buffer 5 times (a plain copy "
+                         "kernel of known size, to scale rocprofv3 byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) "
+                         "of a --copy-calibration run into profiles/traffic.json")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 * 2**20
+
+
+def copy_calibration():
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _counter_rows(directory):
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _per_dispatch(rows, counter, match):
+    vals = [float(r["Counter_Value"]) for r in rows
+            if r.get("Counter_Name") == counter and match(r.get("Kernel_Name", ""))]
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def summarize_pmc(fetch_dir, write_dir, workload):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the split kernel, scaled by what the
+    same counters read for the plain copy kernel of COPY_BYTES, into profiles/traffic.json."""
+    import hashlib
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    is_split = lambda n: "gqa_split_kernel" in n
+    f_split, nf = _per_dispatch(fr, "FETCH_SIZE", is_split)
+    w_split, nw = _per_dispatch(wr, "WRITE_SIZE", is_split)
+
+    # the calibration copies: the last five device-to-device copy dispatches of the run
+    def calib(rows, counter):
+        copies = [r for r in rows if "copyBuffer" in r.get("Kernel_Name", "")
+                  and r.get("Counter_Name") == counter]
+        copies.sort(key=lambda r: int(r["Dispatch_Id"]))
+        vals = [float(r["Counter_Value"]) for r in copies[-5:]]
+        return sum(vals) / len(vals) if vals else None
+    f_copy, w_copy = calib(fr, "FETCH_SIZE"), calib(wr, "WRITE_SIZE")
+    if None in (f_split, w_split, f_copy, w_copy):
+        raise SystemExit("counter rows missing for the split or the copy kernel")
+    f_scale = COPY_BYTES / (f_copy * 1024)   # true bytes per counted byte
+    w_scale = COPY_BYTES / (w_copy * 1024)
+    fetch_b = f_split * 1024 * f_scale
+    write_b = w_split * 1024 * w_scale
+    src = os.path.join(ROOT, "decode_attention_04_amd", "csrc", "gqa_decode.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    if rec.get("kernel_source_sha256") != digest:
+        rec = {"kernel_source_sha256": digest, "workloads": {}}
+    rec["note"] = ("HBM bytes per gqa_split_kernel launch: rocprofv3 FETCH_SIZE and WRITE_SIZE "
+                   "(KiB per dispatch, one counter run each) scaled by the same counters read for "
+                   f"a plain {COPY_BYTES} B device-to-device copy kernel")
+    rec["workloads"][workload] = {
+        "fetch_kib_per_dispatch": round(f_split, 1), "write_kib_per_dispatch": round(w_split, 1),
+        "copy_fetch_kib": round(f_copy, 1), "copy_write_kib": round(w_copy, 1),
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "dispatches": [nf, nw],
+        "hbm_bytes_per_launch": int(round(fetch_b + write_b)),
+        "fetch_bytes_per_launch": int(round(fetch_b)), "write_bytes_per_launch": int(round(write_b)),
+    }
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps(rec["workloads"][workload]))
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        from tests import workloads as W
+        summarize_pmc(*args.summarize_pmc, args.workload or W.HEADLINE)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
@@ -77,46 +184,69 @@ def main():
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
     outs = [torch.empty((case.B, case.Hq, case.D), dtype=torch.float32, device="cuda")
             for _ in range(R)]
-    def step(i, stream):
+    def full(i, stream):
         sets[i % R].run(args.splits, out=outs[i % R], workspace=ws, stream=stream)
 
-    # eager calls: W untimed warm-up steps, then a short timed eager run (reported, not the value)
+    def split_only(i, stream):
+        d = sets[i % R]
+        if case.paged:
+            gd.gqa_paged_decode_partials(d.q, d.k, d.v, d.seq_lens, d.page_table, case.scale,
+                                         out=outs[i % R], workspace=ws, num_splits=args.splits,
+                                         stream=stream)
+        else:
+            gd.gqa_decode_partials(d.q, d.k, d.v, d.seq_lens, case.scale, out=outs[i % R],
+                                   workspace=ws, num_splits=args.splits, stream=stream)
+
+    def combine_only(i, stream):
+        gd.gqa_decode_combine(ws, outs[i % R], case.B, case.Hq, case.Hkv, case.D, cap,
+                              case.page_size, args.splits, stream=stream)
+
     cur = torch.cuda.current_stream()
+
+    def graph_time(fn, k):
+        """ms per call of `fn` over k calls captured in one HIP graph (one untimed replay first)."""
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            fn(0, side)
+        cur.wait_stream(side)
+        with torch.cuda.graph(graph):
+            gs = torch.cuda.current_stream()
+            for i in range(k):
+                fn(i, gs)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        graph.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    # W untimed warm-up steps, then a short timed eager run (reported beside the value)
     for i in range(args.warmup):
-        step(i, cur)
+        full(i, cur)
     torch.cuda.synchronize()
     n_eager = min(args.steps, 500)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(cur)
     for i in range(n_eager):
-        step(i, cur)
+        full(i, cur)
     e1.record(cur)
     torch.cuda.synchronize()
     eager_us = e0.elapsed_time(e1) * 1e3 / n_eager
 
-    # the timed region: exactly K calls, captured once into a HIP graph and replayed, so the
-    # host's per-call launch cost does not throttle the GPU
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(cur)
-    with torch.cuda.stream(side):
-        step(0, side)
-    cur.wait_stream(side)
-    with torch.cuda.graph(graph):
-        gs = torch.cuda.current_stream()
-        for i in range(args.steps):
-            step(i, gs)
-    graph.replay()  # graph warm-up (not timed)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(cur)
-    graph.replay()
-    ev1.record(cur)
-    torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
-    ms_per_step = ms_total / args.steps
+    # The timed region: exactly K whole calls, captured once into a HIP graph and replayed,
+    # so the host's per-call launch cost does not throttle the GPU.
+    ms_per_step = graph_time(full, args.steps)
     us = ms_per_step * 1e3
     gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
+    # The dominant kernel alone (the split-KV partial kernel; K launches in one graph), and the
+    # combine alone, each on the stream they are launched on.
+    split_ms = graph_time(split_only, args.steps)
+    combine_ms = graph_time(combine_only, args.steps) if not (plan.direct or plan.fused) else 0.0
+    split_gbs = algo_bytes / (split_ms * 1e-3) / 1e9
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -139,6 +269,7 @@ def main():
                "sample": f"{calls} full calls of {name} through the fp64 C oracle "
                          f"({el:.1f} s, {threads} OpenMP threads)"}
 
+    traffic = measured_traffic(name)
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -159,12 +290,17 @@ def main():
                    "head_dim": case.D, "capacity": cap, "page_size": case.page_size,
                    "sum_len": int(case.seq_lens.sum()), "algorithmic_bytes": algo_bytes,
                    "plan": plan.as_dict(), "rotated_sets": R, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "timed": "whole call (split kernel + combine), graph-replayed, event-timed"},
+        "roofline": {"bound": "hbm", "kernel": "gqa_split_kernel", "achieved": round(split_gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel_us": round(split_ms * 1e3, 3),
+                     "combine_us": round(combine_ms * 1e3, 3),
+                     "timed": "K launches of the split kernel alone in one HIP graph, HIP events"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    if args.copy_calibration:
+        copy_calibration()
 
 
 if __name__ == "__main__":

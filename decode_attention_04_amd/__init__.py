@@ -27,6 +27,7 @@ STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_
 
 # every symbol include/gqa_decode.h declares
 EXPORTED = ("gqa_decode_plan", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_paged_decode",
+            "gqa_decode_partials", "gqa_paged_decode_partials", "gqa_decode_combine",
             "gqa_status_string")
 
 
@@ -40,7 +41,8 @@ class Plan(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int), ("split_tokens", ctypes.c_int),
                 ("tile_tokens", ctypes.c_int), ("waves", ctypes.c_int), ("grid", ctypes.c_int),
                 ("direct", ctypes.c_int), ("fused", ctypes.c_int), ("fold_group", ctypes.c_int),
-                ("fold_groups", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+                ("fold_groups", ctypes.c_int), ("pv_mode", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -67,6 +69,12 @@ def load(path: str = LIB_PATH):
     lib.gqa_paged_decode.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, vp,
                                      sz, ci, vp]
     lib.gqa_paged_decode.restype = ci
+    lib.gqa_decode_partials.argtypes = lib.gqa_decode.argtypes
+    lib.gqa_decode_partials.restype = ci
+    lib.gqa_paged_decode_partials.argtypes = lib.gqa_paged_decode.argtypes
+    lib.gqa_paged_decode_partials.restype = ci
+    lib.gqa_decode_combine.argtypes = [vp, sz, ci, ci, ci, ci, ci, ci, ci, vp, vp]
+    lib.gqa_decode_combine.restype = ci
     lib.gqa_status_string.argtypes = [ci]
     lib.gqa_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -137,11 +145,12 @@ def _workspace(workspace, need, device):
 
 
 def gqa_decode(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None, num_splits=0,
-               stream=None):
+               stream=None, _entry="gqa_decode"):
     """Contiguous cache: q [B,Hq,D], k/v [B,Hkv,S_max,D] bf16, seq_lens int32 [B].
 
     Returns out (fp32 [B,Hq,D]).  `workspace` (a uint8 device tensor) is
-    allocated when not given; pass one to keep the call allocation-free."""
+    allocated (zero-filled) when not given; pass one to keep the call
+    allocation-free."""
     torch = _torch()
     B, Hq, D = q.shape
     _, Hkv, S_max, _ = k_cache.shape
@@ -150,19 +159,19 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None, n
     need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, S_max, 0, num_splits)
     workspace, ws_bytes = _workspace(workspace, need, q.device)
     bf = _bf16_types()
-    rc = load().gqa_decode(
+    rc = getattr(load(), _entry)(
         _dev_ptr(q, "q", bf), _dev_ptr(k_cache, "k_cache", bf), _dev_ptr(v_cache, "v_cache", bf),
         _dev_ptr(seq_lens, "seq_lens", (torch.int32,)), B, Hq, Hkv, D, S_max, float(scale),
         _dev_ptr(out, "out", (torch.float32,)),
         None if workspace is None else workspace.data_ptr(), ws_bytes, int(num_splits),
         _stream_ptr(stream, q.device))
     if rc != GQA_OK:
-        raise GqaError(rc, "gqa_decode")
+        raise GqaError(rc, _entry)
     return out
 
 
 def gqa_paged_decode(q, k_pool, v_pool, seq_lens, page_table, scale, out=None, workspace=None,
-                     num_splits=0, stream=None):
+                     num_splits=0, stream=None, _entry="gqa_paged_decode"):
     """Paged cache: k/v pools [P,Hkv,page_size,D] bf16, page_table int32 [B,max_pages]."""
     torch = _torch()
     B, Hq, D = q.shape
@@ -173,7 +182,7 @@ def gqa_paged_decode(q, k_pool, v_pool, seq_lens, page_table, scale, out=None, w
     need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, max_pages * page_size, page_size, num_splits)
     workspace, ws_bytes = _workspace(workspace, need, q.device)
     bf = _bf16_types()
-    rc = load().gqa_paged_decode(
+    rc = getattr(load(), _entry)(
         _dev_ptr(q, "q", bf), _dev_ptr(k_pool, "k_pool", bf), _dev_ptr(v_pool, "v_pool", bf),
         _dev_ptr(seq_lens, "seq_lens", (torch.int32,)),
         _dev_ptr(page_table, "page_table", (torch.int32,)), B, Hq, Hkv, D, page_size, P,
@@ -181,5 +190,36 @@ def gqa_paged_decode(q, k_pool, v_pool, seq_lens, page_table, scale, out=None, w
         None if workspace is None else workspace.data_ptr(), ws_bytes, int(num_splits),
         _stream_ptr(stream, q.device))
     if rc != GQA_OK:
-        raise GqaError(rc, "gqa_paged_decode")
+        raise GqaError(rc, _entry)
+    return out
+
+
+def gqa_decode_partials(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None,
+                        num_splits=0, stream=None):
+    """The split kernel of gqa_decode alone (partials into `workspace`, which must be given)."""
+    if workspace is None:
+        raise ValueError("gqa_decode_partials needs the workspace the combine will read")
+    return gqa_decode(q, k_cache, v_cache, seq_lens, scale, out, workspace, num_splits, stream,
+                      _entry="gqa_decode_partials")
+
+
+def gqa_paged_decode_partials(q, k_pool, v_pool, seq_lens, page_table, scale, out=None,
+                              workspace=None, num_splits=0, stream=None):
+    """The split kernel of gqa_paged_decode alone (partials into `workspace`)."""
+    if workspace is None:
+        raise ValueError("gqa_paged_decode_partials needs the workspace the combine will read")
+    return gqa_paged_decode(q, k_pool, v_pool, seq_lens, page_table, scale, out, workspace,
+                            num_splits, stream, _entry="gqa_paged_decode_partials")
+
+
+def gqa_decode_combine(workspace, out, B, Hq, Hkv, head_dim, max_seq_len, page_size=0,
+                       num_splits=0, stream=None):
+    """Fold the partials a *_partials call left in `workspace` into `out`."""
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().gqa_decode_combine(ws_ptr, ws_bytes, B, Hq, Hkv, head_dim, max_seq_len, page_size,
+                                   num_splits, _dev_ptr(out, "out", (_torch().float32,)),
+                                   _stream_ptr(stream, out.device))
+    if rc != GQA_OK:
+        raise GqaError(rc, "gqa_decode_combine")
     return out

@@ -55,6 +55,7 @@
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -162,21 +163,54 @@ __device__ __forceinline__ void load_tile(Tile<D, NB> &t, __amdgpu_buffer_rsrc_t
     }
 }
 
+// How PV is computed:
+//   kPvF32  v_mfma_f32_16x16x4_f32 on V widened to fp32 straight from the
+//           load registers (exact products, 2048 MFMA cycles per 16 keys at
+//           head_dim 256);
+//   kPvBf16 v_mfma_f32_16x16x16_bf16 with P split into bf16 hi + lo parts
+//           (P = hi + lo to about 2^-17 relative) and V transposed through a
+//           per-wave LDS buffer (8x fewer MFMA cycles than kPvF32).
+constexpr int kPvF32 = 0;
+constexpr int kPvBf16 = 1;
+
 // Running online-softmax state of one wave (lane (r, grp) holds query head r).
+//   kPvF32:  acc[c*DPL + e][i] = O[r][16*DPL*c + DPL*(4*grp+i) + e]
+//   kPvBf16: acc[nb][i]        = O[r][16*nb + 4*grp + i]
 template <int D>
 struct WaveState {
-    f32x4_t acc[Shape<D>::NACC];  // acc[c*DPL + e][i] = O[r][16*DPL*c + DPL*(4*grp+i) + e]
+    f32x4_t acc[Shape<D>::NACC];
     float m;                      // running max (log2 units), identical in the 4 lanes of head r
     float l;                      // this lane's share of the running sum
 };
 
+// Row stride (in bf16) of a wave's V staging buffer: 4 bf16 of padding put
+// the rows read by the four lane groups on different LDS banks.
+template <int D>
+constexpr int kStageStride = D + 4;
+
 // QK^T, online softmax and PV for one staged tile whose first key has index
-// `t0` in the sequence; keys at or beyond `t_end` are masked.
-template <int D, int NB>
+// `t0` in the sequence; keys at or beyond `t_end` are masked.  `stage` is
+// this wave's LDS staging buffer (kPvBf16 only).
+template <int D, int NB, int PV>
 __device__ __forceinline__ void compute_tile(const Tile<D, NB> &t, const bf16x8_t (&qb)[Shape<D>::KB],
-                                             WaveState<D> &st, int t0, int t_end, int grp,
-                                             float qk_scale_log2) {
+                                             WaveState<D> &st, int t0, int t_end, int r, int grp,
+                                             float qk_scale_log2, unsigned short *stage) {
     using S = Shape<D>;
+    constexpr int RS = kStageStride<D>;
+    if constexpr (PV == kPvBf16) {
+        // V rows (as loaded: key 16*blk + 4*grp + j, dims 16*DPL*c + DPL*r ..) into LDS.
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int c = 0; c < S::VC; ++c) {
+                    unsigned short *dst = stage + (16 * blk + 4 * grp + j) * RS + 16 * S::DPL * c + S::DPL * r;
+#pragma unroll
+                    for (int w = 0; w < S::VW; w += 2)
+                        *reinterpret_cast<u32x2_t *>(dst + 2 * w) = u32x2_t{t.v[blk][j][c][w], t.v[blk][j][c][w + 1]};
+                }
+    }
     f32x4_t sc[NB];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
@@ -217,30 +251,63 @@ __device__ __forceinline__ void compute_tile(const Tile<D, NB> &t, const bf16x8_
     st.m = m_new;
 #pragma unroll
     for (int a = 0; a < S::NACC; ++a) st.acc[a] *= alpha;
+    if constexpr (PV == kPvF32) {
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
+        for (int blk = 0; blk < NB; ++blk) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float p = sc[blk][j];
+            for (int j = 0; j < 4; ++j) {
+                const float p = sc[blk][j];
 #pragma unroll
-            for (int c = 0; c < S::VC; ++c) {
+                for (int c = 0; c < S::VC; ++c) {
 #pragma unroll
-                for (int e = 0; e < S::DPL; ++e) {
-                    const float vf = bf16_elem(t.v[blk][j][c], e);
-                    st.acc[c * S::DPL + e] =
-                        __builtin_amdgcn_mfma_f32_16x16x4f32(vf, p, st.acc[c * S::DPL + e], 0, 0, 0);
+                    for (int e = 0; e < S::DPL; ++e) {
+                        const float vf = bf16_elem(t.v[blk][j][c], e);
+                        st.acc[c * S::DPL + e] =
+                            __builtin_amdgcn_mfma_f32_16x16x4f32(vf, p, st.acc[c * S::DPL + e], 0, 0, 0);
+                    }
                 }
+            }
+        }
+    } else {
+        // O^T[d][g] += V^T[d][t] P^T[t][g] over the 16 keys of each block: the B
+        // operand is the lane's own four probabilities (keys 4*grp + i), the A
+        // operand four V values of dim 16*nb + r read back from LDS.
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            bf16x4_t hi, lo;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                hi[i] = (__bf16)sc[blk][i];
+                lo[i] = (__bf16)(sc[blk][i] - (float)hi[i]);
+            }
+            const unsigned short *src = stage + (16 * blk + 4 * grp) * RS + r;
+#pragma unroll
+            for (int nb = 0; nb < D / 16; ++nb) {
+                bf16x4_t av;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) av[i] = __builtin_bit_cast(__bf16, src[i * RS + 16 * nb]);
+                st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, hi, st.acc[nb], 0, 0, 0);
+                st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, lo, st.acc[nb], 0, 0, 0);
             }
         }
     }
 }
 
-template <int D>
+// Per-wave LDS region: the V staging buffer during the tile loop, then the
+// wave's accumulator rows [16][D + 4] fp32 for the fold (+4 floats so that
+// consecutive rows start on other banks).  Each wave only ever touches its
+// own region until the workgroup barrier, so the two uses never overlap.
+template <int D, int NB>
 struct FoldLds {
+    static constexpr int kFoldBytes = kMaxHeadsPerKv * (D + 4) * 4;
+    static constexpr int kStageBytes = 16 * NB * kStageStride<D> * 2;
+    static constexpr int kRegion = kFoldBytes > kStageBytes ? kFoldBytes : kStageBytes;
     float m[kWaves][kMaxHeadsPerKv];
     float l[kWaves][kMaxHeadsPerKv];
-    float acc[kWaves][kMaxHeadsPerKv][D + 4];  // +4 floats: consecutive rows start on other banks
     int last;
+    alignas(16) unsigned char region[kWaves][kRegion];
+    __device__ float *acc(int w) { return reinterpret_cast<float *>(region[w]); }
+    __device__ unsigned short *stage(int w) { return reinterpret_cast<unsigned short *>(region[w]); }
 };
 
 // Fold n partial blocks ([G][D] acc, [G][2] ml, block i at acc + i*G*D and
@@ -283,8 +350,8 @@ __device__ __forceinline__ void fold_blocks(const float *acc, const float *ml, i
 // `expected` workgroups to reach `counter`, after making this workgroup's
 // stores visible and, for the last one, acquiring everyone else's.  The last
 // arrival resets the counter to zero for the next call.
-template <int D>
-__device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int expected, FoldLds<D> &lds) {
+template <class Lds>
+__device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int expected, Lds &lds) {
     __threadfence();
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -298,11 +365,11 @@ __device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int 
     return last;
 }
 
-template <int D, int NB, bool PAGED>
+template <int D, int NB, bool PAGED, int PV>
 __global__ __launch_bounds__(64 * kWaves) void gqa_split_kernel(const SplitArgs a) {
     using S = Shape<D>;
     constexpr int TT = 16 * NB;  // keys per wave tile
-    __shared__ FoldLds<D> lds;
+    __shared__ FoldLds<D, NB> lds;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -364,14 +431,15 @@ __global__ __launch_bounds__(64 * kWaves) void gqa_split_kernel(const SplitArgs 
     };
     auto tile_start = [&](int it) { return t_begin + (wave + kWaves * it) * TT; };
 
+    unsigned short *stage = lds.stage(wave);
     Tile<D, NB> buf0, buf1;
     if (my_tiles > 0) issue(buf0, 0);
     for (int it = 0; it < my_tiles; it += 2) {
         if (it + 1 < my_tiles) issue(buf1, it + 1);
-        compute_tile<D, NB>(buf0, qb, st, tile_start(it), t_end, grp, a.qk_scale_log2);
+        compute_tile<D, NB, PV>(buf0, qb, st, tile_start(it), t_end, r, grp, a.qk_scale_log2, stage);
         if (it + 1 < my_tiles) {
             if (it + 2 < my_tiles) issue(buf0, it + 2);
-            compute_tile<D, NB>(buf1, qb, st, tile_start(it + 1), t_end, grp, a.qk_scale_log2);
+            compute_tile<D, NB, PV>(buf1, qb, st, tile_start(it + 1), t_end, r, grp, a.qk_scale_log2, stage);
         }
     }
 
@@ -380,22 +448,29 @@ __global__ __launch_bounds__(64 * kWaves) void gqa_split_kernel(const SplitArgs 
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
 
-    // Publish the wave's state; rows g >= G are never read.
+    // Publish the wave's state into its own region; rows g >= G are never read.
     if (r < a.G) {
         if (grp == 0) {
             lds.m[wave][r] = st.m;
             lds.l[wave][r] = lsum;
         }
+        float *row = lds.acc(wave) + r * (D + 4);
+        if constexpr (PV == kPvF32) {
 #pragma unroll
-        for (int c = 0; c < S::VC; ++c)
+            for (int c = 0; c < S::VC; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int e = 0; e < S::DPL; e += 4) {
-                    const f32x4_t x = {st.acc[c * S::DPL + e][i], st.acc[c * S::DPL + e + 1][i],
-                                       st.acc[c * S::DPL + e + 2][i], st.acc[c * S::DPL + e + 3][i]};
-                    *reinterpret_cast<f32x4_t *>(&lds.acc[wave][r][16 * S::DPL * c + S::DPL * (4 * grp + i) + e]) = x;
-                }
+                    for (int e = 0; e < S::DPL; e += 4) {
+                        const f32x4_t x = {st.acc[c * S::DPL + e][i], st.acc[c * S::DPL + e + 1][i],
+                                           st.acc[c * S::DPL + e + 2][i], st.acc[c * S::DPL + e + 3][i]};
+                        *reinterpret_cast<f32x4_t *>(row + 16 * S::DPL * c + S::DPL * (4 * grp + i) + e) = x;
+                    }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < D / 16; ++nb)
+                *reinterpret_cast<f32x4_t *>(row + 16 * nb + 4 * grp) = st.acc[nb];
+        }
     }
     __syncthreads();
 
@@ -419,7 +494,7 @@ __global__ __launch_bounds__(64 * kWaves) void gqa_split_kernel(const SplitArgs 
             for (int w = 0; w < kWaves; ++w) {
                 const float sw = __builtin_amdgcn_exp2f(lds.m[w][g] - M);
                 L += sw * lds.l[w][g];
-                acc += sw * *reinterpret_cast<const f32x4_t *>(&lds.acc[w][g][d]);
+                acc += sw * *reinterpret_cast<const f32x4_t *>(lds.acc(w) + g * (D + 4) + d);
             }
         }
         if (direct) {
@@ -443,7 +518,7 @@ __global__ __launch_bounds__(64 * kWaves) void gqa_split_kernel(const SplitArgs 
     const int g0 = grp_id * a.fold_group;
     const int gn = min(a.fold_group, nsplit - g0);
     unsigned int *ctr = a.counters + (size_t)bk * (ngroups + 1);
-    if (!arrive_last<D>(ctr + grp_id, (unsigned)gn, lds)) return;
+    if (!arrive_last(ctr + grp_id, (unsigned)gn, lds)) return;
     const float *src_acc = a.part_acc + ((size_t)bk * nsplit + g0) * G * D;
     const float *src_ml = a.part_ml + ((size_t)bk * nsplit + g0) * G * 2;
     if (ngroups == 1) {
@@ -452,23 +527,33 @@ __global__ __launch_bounds__(64 * kWaves) void gqa_split_kernel(const SplitArgs 
     }
     fold_blocks<D>(src_acc, src_ml, gn, G, a.grp_acc + ((size_t)bk * ngroups + grp_id) * G * D,
                    a.grp_ml + ((size_t)bk * ngroups + grp_id) * G * 2, nullptr);
-    if (!arrive_last<D>(ctr + ngroups, (unsigned)ngroups, lds)) return;
+    if (!arrive_last(ctr + ngroups, (unsigned)ngroups, lds)) return;
     fold_blocks<D>(a.grp_acc + (size_t)bk * ngroups * G * D, a.grp_ml + (size_t)bk * ngroups * G * 2,
                    ngroups, G, nullptr, nullptr, out_rows);
 }
 
 // Combine: one workgroup of 256 threads per (b, h, chunk of 4*NCOL dims).
 // Thread (sg, c) owns dims 4c .. 4c+3 of the chunk and the splits s with
-// s % NSG == sg (NSG = 256 / NCOL).  It issues the loads of all its splits
-// before using any (one memory round trip), folds them in ascending s with a
-// running max, and the NSG groups are then folded through LDS in ascending
-// order: a fixed summation order, so the result is bit-reproducible.
+// s % NSG == sg (NSG = 256 / NCOL).  It issues the loads of up to U of its
+// splits before using any, folds them in ascending s with a running max, and
+// the NSG groups are then folded pairwise through LDS (a fixed tree): the
+// summation order is fixed, so the result is bit-reproducible.
 constexpr int kCombineThreads = 256;
+
+__device__ __forceinline__ void lse_merge(float &m, float &l, f32x4_t &o, float m2, float l2, f32x4_t o2) {
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;
+    const float wa = __builtin_amdgcn_exp2f(m - mn);
+    const float wb = __builtin_amdgcn_exp2f(m2 - mn);
+    l = l * wa + l2 * wb;
+    o = o * wa + o2 * wb;
+    m = mn;
+}
 
 template <int NCOL>
 __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const CombineArgs a) {
     constexpr int NSG = kCombineThreads / NCOL;
-    constexpr int U = 4;  // splits per thread per round of loads
+    constexpr int U = 8;  // splits per thread per round of loads
     const int D = a.D;
     const int chunks = D / (4 * NCOL);
     const size_t bh = blockIdx.x / chunks;
@@ -504,40 +589,30 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const Comb
             }
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float m_new = fmaxf(m_run, mv[u]);
-            if (m_new != -INFINITY) {
-                const float wa = __builtin_amdgcn_exp2f(m_run - m_new);
-                const float wb = __builtin_amdgcn_exp2f(mv[u] - m_new);
-                l_run = l_run * wa + lv[u] * wb;
-                o_run = o_run * wa + av[u] * wb;
-                m_run = m_new;
-            }
-        }
+        for (int u = 0; u < U; ++u) lse_merge(m_run, l_run, o_run, mv[u], lv[u], av[u]);
     }
 
+    // Pairwise fold of the NSG split groups: at each step group i absorbs
+    // group i + w, for w = NSG/2, NSG/4, ..., 1.
     __shared__ f32x4_t part[NSG][NCOL];
-    __shared__ float mpart[NSG], lpart[NSG];
+    __shared__ float mpart[NSG][NCOL], lpart[NSG][NCOL];
     part[sg][c] = o_run;
-    if (c == 0) {
-        mpart[sg] = m_run;
-        lpart[sg] = l_run;
-    }
+    mpart[sg][c] = m_run;
+    lpart[sg][c] = l_run;
     __syncthreads();
-    if (sg == 0) {
-        float M = -INFINITY;
-        for (int i = 0; i < NSG; ++i) M = fmaxf(M, mpart[i]);
-        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-        float L = 0.f;
-        if (M != -INFINITY) {
-            for (int i = 0; i < NSG; ++i) {
-                const float w = __builtin_amdgcn_exp2f(mpart[i] - M);
-                L += w * lpart[i];
-                o += w * part[i][c];
-            }
+#pragma unroll
+    for (int w = NSG / 2; w > 0; w /= 2) {
+        if (sg < w) {
+            lse_merge(m_run, l_run, o_run, mpart[sg + w][c], lpart[sg + w][c], part[sg + w][c]);
+            part[sg][c] = o_run;
+            mpart[sg][c] = m_run;
+            lpart[sg][c] = l_run;
         }
+        __syncthreads();
+    }
+    if (sg == 0) {
         *reinterpret_cast<f32x4_t *>(a.out + bh * D + d0 + 4 * c) =
-            L > 0.f ? o / L : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            l_run > 0.f ? o_run / l_run : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 }
 
@@ -614,6 +689,13 @@ int env_fused() {
     return atoi(s) != 0 ? 1 : 0;
 }
 
+// PV contraction: GQA_DECODE_PV=f32 selects the fp32-MFMA variant for A/B.
+int env_pv_mode() {
+    const char *s = getenv("GQA_DECODE_PV");
+    if (s != nullptr && strcmp(s, "f32") == 0) return kPvF32;
+    return kPvBf16;
+}
+
 int env_splits() {
     const char *s = getenv("GQA_DECODE_SPLITS");
     if (s == nullptr || *s == '\0') return 0;
@@ -644,8 +726,12 @@ hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, hipStream
     if constexpr (NB * D > 256) {  // at most 16 KB of K+V (64 * NB * D bytes) per wave tile
         return hipErrorInvalidValue;
     } else {
-        hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED>), dim3((unsigned)plan.grid),
-                           dim3(64 * kWaves), 0, stream, a);
+        if (plan.pv_mode == kPvF32)
+            hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32>), dim3((unsigned)plan.grid),
+                               dim3(64 * kWaves), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16>), dim3((unsigned)plan.grid),
+                               dim3(64 * kWaves), 0, stream, a);
         return hipGetLastError();
     }
 }
@@ -660,8 +746,11 @@ hipError_t launch_split(const gqa_plan_t &plan, const SplitArgs &a, hipStream_t 
     }
 }
 
+constexpr int kPhaseSplit = 1;
+constexpr int kPhaseCombine = 2;
+
 gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, void *workspace,
-                 hipStream_t stream) {
+                 hipStream_t stream, int phases) {
     if (!plan.direct) {
         WorkspaceLayout w = workspace_layout(a.B, a.Hq, a.Hkv, D, plan.num_splits, plan.fused,
                                              plan.fold_groups);
@@ -676,14 +765,16 @@ gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, void *
         a.fold_groups = plan.fold_groups;
     }
     hipError_t e = hipSuccess;
-    switch (D) {
-        case 64: e = paged ? launch_split<64, true>(plan, a, stream) : launch_split<64, false>(plan, a, stream); break;
-        case 128: e = paged ? launch_split<128, true>(plan, a, stream) : launch_split<128, false>(plan, a, stream); break;
-        case 256: e = paged ? launch_split<256, true>(plan, a, stream) : launch_split<256, false>(plan, a, stream); break;
-        default: return GQA_ERR_UNSUPPORTED;
+    if (phases & kPhaseSplit) {
+        switch (D) {
+            case 64: e = paged ? launch_split<64, true>(plan, a, stream) : launch_split<64, false>(plan, a, stream); break;
+            case 128: e = paged ? launch_split<128, true>(plan, a, stream) : launch_split<128, false>(plan, a, stream); break;
+            case 256: e = paged ? launch_split<256, true>(plan, a, stream) : launch_split<256, false>(plan, a, stream); break;
+            default: return GQA_ERR_UNSUPPORTED;
+        }
+        if (e != hipSuccess) return GQA_ERR_HIP;
     }
-    if (e != hipSuccess) return GQA_ERR_HIP;
-    if (plan.direct || plan.fused) return GQA_OK;
+    if (plan.direct || plan.fused || !(phases & kPhaseCombine)) return GQA_OK;
     e = launch_combine(plan, a.part_acc, a.part_ml, a.out, a.B, a.Hq, a.Hkv, D, stream);
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
@@ -758,6 +849,7 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
     plan->grid = (int)grid;
     plan->direct = S == 1 ? 1 : 0;
     plan->fused = plan->direct ? 0 : env_fused();
+    plan->pv_mode = env_pv_mode();
     // Fold groups: one level up to 8 splits, else about sqrt(S) splits per
     // group and about sqrt(S) groups, so no workgroup folds many blocks.
     int fg = S;
@@ -782,10 +874,14 @@ size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_seq_len
     return plan.workspace_bytes;
 }
 
-gqa_status_t gqa_decode(const void *q, const void *k_cache, const void *v_cache,
-                        const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
-                        float scale, float *out, void *workspace, size_t workspace_bytes,
-                        int num_splits, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+gqa_status_t decode_contig(const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
+                           float scale, float *out, void *workspace, size_t workspace_bytes,
+                           int num_splits, hipStream_t stream, int phases) {
     gqa_status_t s = check_common(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, scale);
     if (s != GQA_OK) return s;
     if (S_max < 0 || num_splits < 0) return GQA_ERR_SHAPE;
@@ -809,14 +905,14 @@ gqa_status_t gqa_decode(const void *q, const void *k_cache, const void *v_cache,
     a.num_splits = plan.num_splits;
     a.split_tokens = plan.split_tokens;
     a.qk_scale_log2 = scale * 1.4426950408889634f;
-    return run(plan, a, D, false, workspace, stream);
+    return run(plan, a, D, false, workspace, stream, phases);
 }
 
-gqa_status_t gqa_paged_decode(const void *q, const void *k_pool, const void *v_pool,
-                              const int32_t *seq_lens, const int32_t *page_table, int B, int Hq,
-                              int Hkv, int D, int page_size, int num_pages, int max_pages,
-                              float scale, float *out, void *workspace, size_t workspace_bytes,
-                              int num_splits, hipStream_t stream) {
+gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
+                          const int32_t *seq_lens, const int32_t *page_table, int B, int Hq,
+                          int Hkv, int D, int page_size, int num_pages, int max_pages,
+                          float scale, float *out, void *workspace, size_t workspace_bytes,
+                          int num_splits, hipStream_t stream, int phases) {
     gqa_status_t s = check_common(q, k_pool, v_pool, seq_lens, out, B, Hq, Hkv, D, scale);
     if (s != GQA_OK) return s;
     if (B == 0) return (page_size > 0 && page_size % 16 == 0) ? GQA_OK : GQA_ERR_UNSUPPORTED;
@@ -847,7 +943,70 @@ gqa_status_t gqa_paged_decode(const void *q, const void *k_pool, const void *v_p
     a.num_splits = plan.num_splits;
     a.split_tokens = plan.split_tokens;
     a.qk_scale_log2 = scale * 1.4426950408889634f;
-    return run(plan, a, D, true, workspace, stream);
+    return run(plan, a, D, true, workspace, stream, phases);
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status_t gqa_decode(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
+                        float scale, float *out, void *workspace, size_t workspace_bytes,
+                        int num_splits, hipStream_t stream) {
+    return decode_contig(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale, out, workspace,
+                         workspace_bytes, num_splits, stream, kPhaseSplit | kPhaseCombine);
+}
+
+gqa_status_t gqa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
+                                 const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
+                                 float scale, float *out, void *workspace, size_t workspace_bytes,
+                                 int num_splits, hipStream_t stream) {
+    return decode_contig(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale, out, workspace,
+                         workspace_bytes, num_splits, stream, kPhaseSplit);
+}
+
+gqa_status_t gqa_paged_decode(const void *q, const void *k_pool, const void *v_pool,
+                              const int32_t *seq_lens, const int32_t *page_table, int B, int Hq,
+                              int Hkv, int D, int page_size, int num_pages, int max_pages,
+                              float scale, float *out, void *workspace, size_t workspace_bytes,
+                              int num_splits, hipStream_t stream) {
+    return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, Hq, Hkv, D, page_size, num_pages,
+                        max_pages, scale, out, workspace, workspace_bytes, num_splits, stream,
+                        kPhaseSplit | kPhaseCombine);
+}
+
+gqa_status_t gqa_paged_decode_partials(const void *q, const void *k_pool, const void *v_pool,
+                                       const int32_t *seq_lens, const int32_t *page_table, int B,
+                                       int Hq, int Hkv, int D, int page_size, int num_pages,
+                                       int max_pages, float scale, float *out, void *workspace,
+                                       size_t workspace_bytes, int num_splits, hipStream_t stream) {
+    return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, Hq, Hkv, D, page_size, num_pages,
+                        max_pages, scale, out, workspace, workspace_bytes, num_splits, stream,
+                        kPhaseSplit);
+}
+
+gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                                int D, int max_seq_len, int page_size, int num_splits, float *out,
+                                hipStream_t stream) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_seq_len < 0 || page_size < 0 ||
+        num_splits < 0)
+        return GQA_ERR_SHAPE;
+    if (!supported_dim(D) || Hq / Hkv > kMaxHeadsPerKv) return GQA_ERR_UNSUPPORTED;
+    if (page_size > 0 && page_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
+    if (B == 0) return GQA_OK;
+    if (out == nullptr) return GQA_ERR_NULL;
+    if (misaligned(out, 16) || (workspace != nullptr && misaligned(workspace, 16))) return GQA_ERR_ALIGN;
+    gqa_plan_t plan;
+    gqa_status_t s = plan_for_call(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, &plan);
+    if (s != GQA_OK) return s;
+    if (plan.direct || plan.fused) return GQA_OK;  // the split kernel already wrote `out`
+    if (workspace == nullptr) return GQA_ERR_NULL;
+    if (workspace_bytes < plan.workspace_bytes) return GQA_ERR_WORKSPACE;
+    SplitArgs a{};
+    a.out = out;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+    return run(plan, a, D, page_size > 0, const_cast<void *>(workspace), stream, kPhaseCombine);
 }
 
 const char *gqa_status_string(gqa_status_t status) {

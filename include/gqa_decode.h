@@ -71,6 +71,7 @@ typedef struct gqa_plan {
     int fused;              /* 1: the split kernel also folds the partials (one launch) */
     int fold_group;         /* splits folded together at the first fold level */
     int fold_groups;        /* first-level groups (1 = a single fold level) */
+    int pv_mode;            /* PV contraction: 1 = bf16 MFMA with P split hi+lo, 0 = fp32 MFMA */
     size_t workspace_bytes; /* scratch the call needs (0 when direct) */
 } gqa_plan_t;
 
@@ -130,6 +131,34 @@ gqa_status_t gqa_paged_decode(const void *q, const void *k_pool, const void *v_p
                               int Hkv, int head_dim, int page_size, int num_pages, int max_pages,
                               float scale, float *out, void *workspace, size_t workspace_bytes,
                               int num_splits, hipStream_t stream);
+
+/*
+ * The two steps of a call, for callers that schedule them separately (the
+ * split-KV partial kernel, then the combine kernel).  gqa_decode_partials /
+ * gqa_paged_decode_partials take exactly the arguments of gqa_decode /
+ * gqa_paged_decode and launch only the split kernel: it leaves the
+ * unnormalised (m, l, acc) partials in `workspace` (when the plan is direct
+ * it writes `out` instead).  gqa_decode_combine then folds those partials
+ * into `out` (it launches nothing for a direct plan); its shape arguments,
+ * num_splits and the environment must be those of the partials call, so that
+ * both compute the same plan (max_seq_len = S_max and page_size = 0 for a
+ * contiguous cache).  Running the two on one stream gives bit-for-bit the
+ * result of the one-call entry point.
+ */
+gqa_status_t gqa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
+                                 const int32_t *seq_lens, int B, int Hq, int Hkv, int head_dim,
+                                 int S_max, float scale, float *out, void *workspace,
+                                 size_t workspace_bytes, int num_splits, hipStream_t stream);
+
+gqa_status_t gqa_paged_decode_partials(const void *q, const void *k_pool, const void *v_pool,
+                                       const int32_t *seq_lens, const int32_t *page_table, int B,
+                                       int Hq, int Hkv, int head_dim, int page_size, int num_pages,
+                                       int max_pages, float scale, float *out, void *workspace,
+                                       size_t workspace_bytes, int num_splits, hipStream_t stream);
+
+gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, int B, int Hq,
+                                int Hkv, int head_dim, int max_seq_len, int page_size,
+                                int num_splits, float *out, hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char *gqa_status_string(gqa_status_t status);

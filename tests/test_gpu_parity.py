@@ -209,3 +209,50 @@ def test_shared_workspace_across_plans(monkeypatch):
         compare(ob.cpu().numpy(), rb, "plan B")
         compare(oc.cpu().numpy(), ra, "plan A, 37 splits")
     assert not torch.any(ws[:65536]), "the counter area must be back at zero after each call"
+
+
+@pytest.mark.parametrize("pv", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_pv_modes(monkeypatch, pv, D):
+    """Both PV contractions (fp32 MFMA; bf16 MFMA with P split hi+lo) match the oracle,
+    with a NaN-poisoned tail and ragged lengths."""
+    say(f"[parity] pv={pv} D={D}")
+    monkeypatch.setenv("GQA_DECODE_PV", pv)
+    assert gd.gqa_decode_plan(2, 16, 2, D, 300).pv_mode == (0 if pv == "f32" else 1)
+    case = W.contig_case(3, 16, 2, D, 300, seq_lens=[300, 17, 129], seed=40 + D, tail="nan")
+    dc = DeviceCase(case)
+    ref = oracle_out(case)
+    for splits in (0, 1, 4):
+        compare(dc.run_host(splits), ref, f"pv={pv} D={D} splits={splits}")
+    pk = W.peaky_case(1, 8, 1, D, 4000, frac=0.01, mul=8, seed=41)
+    compare(DeviceCase(pk).run_host(), oracle_out(pk), f"peaky pv={pv} D={D}")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_partials_then_combine_equals_one_call(paged):
+    """gqa_*_partials + gqa_decode_combine on one stream give the one-call result bit for bit."""
+    say(f"[parity] partials + combine, paged={paged}")
+    if paged:
+        case = W.paged_case(4, 32, 8, 128, 32, 200, seq_lens=[1000, 1, 555, 1024], max_len=1024,
+                            seed=50)
+    else:
+        case = W.contig_case(3, 24, 4, 256, 1500, seq_lens=[1500, 700, 3], seed=51, scale=1 / 16)
+    dc = DeviceCase(case)
+    one = dc.run_host()
+    cap, ps = case.capacity, case.page_size
+    for splits in (0, 5):
+        need = gd.gqa_decode_workspace_bytes(case.B, case.Hq, case.Hkv, case.D, cap, ps, splits)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+        out = torch.empty((case.B, case.Hq, case.D), dtype=torch.float32, device="cuda")
+        if paged:
+            gd.gqa_paged_decode_partials(dc.q, dc.k, dc.v, dc.seq_lens, dc.page_table, case.scale,
+                                         out=out, workspace=ws, num_splits=splits)
+        else:
+            gd.gqa_decode_partials(dc.q, dc.k, dc.v, dc.seq_lens, case.scale, out=out, workspace=ws,
+                                   num_splits=splits)
+        gd.gqa_decode_combine(ws, out, case.B, case.Hq, case.Hkv, case.D, cap, ps, splits)
+        torch.cuda.synchronize()
+        two = out.cpu().numpy()
+        ref = dc.run_host(splits)
+        assert np.array_equal(two.view(np.uint32), ref.view(np.uint32))
+    compare(one, oracle_out(case), "partials+combine")

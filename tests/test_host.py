@@ -75,6 +75,7 @@ def test_plan_invariants(shape, cu):
     assert p.grid == B * Hkv * p.num_splits
     assert p.direct == (p.num_splits == 1)
     assert p.fused == 0   # the in-kernel fold is opt-in (GQA_DECODE_FUSED=1)
+    assert p.pv_mode == 1  # bf16 MFMA PV unless GQA_DECODE_PV=f32
     assert p.fold_group * p.fold_groups >= p.num_splits
     assert (p.fold_groups - 1) * p.fold_group < p.num_splits
     if p.num_splits <= 8:
@@ -203,3 +204,16 @@ def test_fused_plan_workspace(monkeypatch):
         p = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, 0, 256)
         assert p.fused == 1
         assert p.workspace_bytes == expected_workspace(B, Hq, Hkv, D, p)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(B=1, Hq=8, Hkv=3), 2), (dict(D=96), 3), (dict(out=None), 1), (dict(out=A + 4), 4),
+    (dict(ws=None), 1), (dict(ws=A + 8), 4), (dict(ws_bytes=8), 5), (dict(ps=20), 3),
+    (dict(B=0, out=None, ws=None), 0),          # nothing to do
+    (dict(splits=1, ws=None, ws_bytes=0), 0),   # a direct plan has nothing to combine
+])
+def test_combine_rejects(lib, args, code):
+    kw = dict(ws=A, ws_bytes=1 << 30, B=1, Hq=8, Hkv=2, D=128, cap=64, ps=0, splits=2, out=A)
+    kw.update(args)
+    assert lib.gqa_decode_combine(kw["ws"], kw["ws_bytes"], kw["B"], kw["Hq"], kw["Hkv"], kw["D"],
+                                  kw["cap"], kw["ps"], kw["splits"], kw["out"], None) == code
