@@ -198,8 +198,8 @@ def main():
                                    workspace=ws, num_splits=args.splits, stream=stream)
 
     def combine_only(i, stream):
-        gd.gqa_decode_combine(ws, outs[i % R], case.B, case.Hq, case.Hkv, case.D, cap,
-                              case.page_size, args.splits, stream=stream)
+        gd.gqa_decode_combine(ws, sets[i % R].seq_lens, outs[i % R], case.B, case.Hq, case.Hkv,
+                              case.D, cap, case.page_size, args.splits, stream=stream)
 
     cur = torch.cuda.current_stream()
 

@@ -38,10 +38,13 @@ class GqaError(RuntimeError):
 
 
 class Plan(ctypes.Structure):
-    _fields_ = [("num_splits", ctypes.c_int), ("split_tokens", ctypes.c_int),
-                ("tile_tokens", ctypes.c_int), ("waves", ctypes.c_int), ("grid", ctypes.c_int),
-                ("direct", ctypes.c_int), ("fused", ctypes.c_int), ("fold_group", ctypes.c_int),
+    _fields_ = [("partition", ctypes.c_int), ("num_splits", ctypes.c_int),
+                ("split_tokens", ctypes.c_int), ("tile_tokens", ctypes.c_int),
+                ("waves", ctypes.c_int), ("grid", ctypes.c_int), ("direct", ctypes.c_int),
+                ("max_pieces", ctypes.c_int), ("slots", ctypes.c_int64),
+                ("fused", ctypes.c_int), ("fold_group", ctypes.c_int),
                 ("fold_groups", ctypes.c_int), ("pv_mode", ctypes.c_int),
+                ("double_buffer", ctypes.c_int),
                 ("workspace_bytes", ctypes.c_size_t)]
 
     def as_dict(self) -> dict:
@@ -73,7 +76,7 @@ def load(path: str = LIB_PATH):
     lib.gqa_decode_partials.restype = ci
     lib.gqa_paged_decode_partials.argtypes = lib.gqa_paged_decode.argtypes
     lib.gqa_paged_decode_partials.restype = ci
-    lib.gqa_decode_combine.argtypes = [vp, sz, ci, ci, ci, ci, ci, ci, ci, vp, vp]
+    lib.gqa_decode_combine.argtypes = [vp, sz, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp]
     lib.gqa_decode_combine.restype = ci
     lib.gqa_status_string.argtypes = [ci]
     lib.gqa_status_string.restype = ctypes.c_char_p
@@ -212,13 +215,15 @@ def gqa_paged_decode_partials(q, k_pool, v_pool, seq_lens, page_table, scale, ou
                             num_splits, stream, _entry="gqa_paged_decode_partials")
 
 
-def gqa_decode_combine(workspace, out, B, Hq, Hkv, head_dim, max_seq_len, page_size=0,
+def gqa_decode_combine(workspace, seq_lens, out, B, Hq, Hkv, head_dim, max_seq_len, page_size=0,
                        num_splits=0, stream=None):
     """Fold the partials a *_partials call left in `workspace` into `out`."""
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = load().gqa_decode_combine(ws_ptr, ws_bytes, B, Hq, Hkv, head_dim, max_seq_len, page_size,
-                                   num_splits, _dev_ptr(out, "out", (_torch().float32,)),
+    rc = load().gqa_decode_combine(ws_ptr, ws_bytes,
+                                   _dev_ptr(seq_lens, "seq_lens", (_torch().int32,)), B, Hq, Hkv,
+                                   head_dim, max_seq_len, page_size, num_splits,
+                                   _dev_ptr(out, "out", (_torch().float32,)),
                                    _stream_ptr(stream, out.device))
     if rc != GQA_OK:
         raise GqaError(rc, "gqa_decode_combine")

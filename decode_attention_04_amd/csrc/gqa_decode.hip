@@ -48,6 +48,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "gqa_decode.h"
@@ -61,6 +62,8 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;           // waves per workgroup
+constexpr int kPartitionFixed = 0;  // see "work partition" below
+constexpr int kPartitionEven = 1;
 constexpr int kMaxHeadsPerKv = 16;  // G is padded to the MFMA's 16 columns
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords (gfx9 family)
 
@@ -94,7 +97,11 @@ struct CombineArgs {
     const float *part_acc;
     const float *part_ml;
     float *out;
+    const int32_t *seq_lens;  // even partition only
     int D, G, Hq, num_splits;
+    int partition;            // kPartitionFixed / kPartitionEven
+    int B, Hkv, cap, tile;    // even partition: how the split kernel cut the tiles
+    int shares;               // even partition: workgroups of the split kernel
 };
 
 __device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
@@ -129,20 +136,24 @@ struct Tile {
 // Issue the loads of one tile.  `rk` / `rv` cover the rows of this tile's
 // (sequence, kv head) or page, ending at the last valid row; `row0` is the
 // tile's first row inside that range.
+constexpr int kLoadK = 1;
+constexpr int kLoadV = 2;
+
 template <int D, int NB>
 __device__ __forceinline__ void load_tile(Tile<D, NB> &t, __amdgpu_buffer_rsrc_t rk,
-                                          __amdgpu_buffer_rsrc_t rv, int row0, int r, int grp) {
+                                          __amdgpu_buffer_rsrc_t rv, int row0, int r, int grp,
+                                          int parts) {
     using S = Shape<D>;
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
         const int krow = row0 + 16 * blk + r;
 #pragma unroll
-        for (int kb = 0; kb < S::KB; ++kb) {
+        for (int kb = 0; kb < S::KB && (parts & kLoadK); ++kb) {
             const int off = (krow * D + 32 * kb + 8 * grp) * 2;
             t.k[blk][kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4 && (parts & kLoadV); ++j) {
             const int vrow = row0 + 16 * blk + 4 * grp + j;
 #pragma unroll
             for (int c = 0; c < S::VC; ++c) {
@@ -188,30 +199,34 @@ struct WaveState {
 template <int D>
 constexpr int kStageStride = D + 4;
 
-// QK^T, online softmax and PV for one staged tile whose first key has index
-// `t0` in the sequence; keys at or beyond `t_end` are masked.  `stage` is
-// this wave's LDS staging buffer (kPvBf16 only).
-template <int D, int NB, int PV>
-__device__ __forceinline__ void compute_tile(const Tile<D, NB> &t, const bf16x8_t (&qb)[Shape<D>::KB],
-                                             WaveState<D> &st, int t0, int t_end, int r, int grp,
-                                             float qk_scale_log2, unsigned short *stage) {
+// kPvBf16: V rows of a tile (as loaded: key 16*blk + 4*grp + j, dims
+// 16*DPL*c + DPL*r ..) into the wave's LDS staging buffer.
+template <int D, int NB>
+__device__ __forceinline__ void stage_v(const Tile<D, NB> &t, int r, int grp, unsigned short *stage) {
     using S = Shape<D>;
     constexpr int RS = kStageStride<D>;
-    if constexpr (PV == kPvBf16) {
-        // V rows (as loaded: key 16*blk + 4*grp + j, dims 16*DPL*c + DPL*r ..) into LDS.
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk)
+    for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int c = 0; c < S::VC; ++c) {
-                    unsigned short *dst = stage + (16 * blk + 4 * grp + j) * RS + 16 * S::DPL * c + S::DPL * r;
+            for (int c = 0; c < S::VC; ++c) {
+                unsigned short *dst = stage + (16 * blk + 4 * grp + j) * RS + 16 * S::DPL * c + S::DPL * r;
 #pragma unroll
-                    for (int w = 0; w < S::VW; w += 2)
-                        *reinterpret_cast<u32x2_t *>(dst + 2 * w) = u32x2_t{t.v[blk][j][c][w], t.v[blk][j][c][w + 1]};
-                }
-    }
-    f32x4_t sc[NB];
+                for (int w = 0; w < S::VW; w += 2)
+                    *reinterpret_cast<u32x2_t *>(dst + 2 * w) = u32x2_t{t.v[blk][j][c][w], t.v[blk][j][c][w + 1]};
+            }
+}
+
+// QK^T and the online-softmax update for one tile whose first key has index
+// `t0` in the sequence (keys at or beyond `t_end` masked).  On return
+// sc[blk][i] holds the probability of key 16*blk + 4*grp + i for head r
+// (relative to the new running max) and acc has been rescaled.
+template <int D, int NB>
+__device__ __forceinline__ void qk_softmax(const Tile<D, NB> &t, const bf16x8_t (&qb)[Shape<D>::KB],
+                                           WaveState<D> &st, int t0, int t_end, int grp,
+                                           float qk_scale_log2, f32x4_t (&sc)[NB]) {
+    using S = Shape<D>;
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
         f32x4_t c = {0.f, 0.f, 0.f, 0.f};
@@ -251,6 +266,14 @@ __device__ __forceinline__ void compute_tile(const Tile<D, NB> &t, const bf16x8_
     st.m = m_new;
 #pragma unroll
     for (int a = 0; a < S::NACC; ++a) st.acc[a] *= alpha;
+}
+
+// PV for one tile with probabilities sc (see qk_softmax).
+template <int D, int NB, int PV>
+__device__ __forceinline__ void pv_tile(const Tile<D, NB> &t, const f32x4_t (&sc)[NB], WaveState<D> &st,
+                                        int r, int grp, const unsigned short *stage) {
+    using S = Shape<D>;
+    constexpr int RS = kStageStride<D>;
     if constexpr (PV == kPvF32) {
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
@@ -291,6 +314,17 @@ __device__ __forceinline__ void compute_tile(const Tile<D, NB> &t, const bf16x8_
             }
         }
     }
+}
+
+// QK^T, online softmax and PV for one staged tile.
+template <int D, int NB, int PV>
+__device__ __forceinline__ void compute_tile(const Tile<D, NB> &t, const bf16x8_t (&qb)[Shape<D>::KB],
+                                             WaveState<D> &st, int t0, int t_end, int r, int grp,
+                                             float qk_scale_log2, unsigned short *stage) {
+    if constexpr (PV == kPvBf16) stage_v<D, NB>(t, r, grp, stage);
+    f32x4_t sc[NB];
+    qk_softmax<D, NB>(t, qb, st, t0, t_end, grp, qk_scale_log2, sc);
+    pv_tile<D, NB, PV>(t, sc, st, r, grp, stage);
 }
 
 // Per-wave LDS region: the V staging buffer during the tile loop, then the
@@ -365,27 +399,136 @@ __device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int 
     return last;
 }
 
-template <int D, int NB, bool PAGED, int PV>
-__global__ __launch_bounds__(64 * kWaves) void gqa_split_kernel(const SplitArgs a) {
+// Minimum waves per SIMD the compiler must leave room for: the single-buffer
+// variants rely on more resident waves for their latency hiding.
+template <int D, bool DBUF>
+constexpr int kMinWavesPerEu = DBUF ? 1 : (D >= 256 ? 2 : 4);
+
+// ------------------------------------------------------------ work partition
+//
+// The keys of one (sequence b, kv head) pair form a "segment" of
+// n_b = ceil(len_b / tile) tiles; segments are ordered b-major, kv-head-minor
+// (segment index i = b*Hkv + kvh).  Two partitions of the segments onto
+// workgroups exist:
+//   fixed  every segment is cut into S splits of split_tokens keys; workgroup
+//          (b, kvh, s) takes split s (the AstrAI split-KV scheme).  Partial slot
+//          of a split: (b*Hkv + kvh)*S + s.
+//   even   the concatenated tiles of all segments are cut into P equal shares,
+//          share w = tiles [floor(w*N/P), floor((w+1)*N/P)) of the N tiles,
+//          computed on the device from seq_lens, so a ragged batch gives every
+//          workgroup the same work (the length-aware scheduling that the pages'
+//          split rule leaves open).  A share may cover the end of one segment
+//          and the start of the next: each such piece is folded on its own and
+//          written to partial slot w + i (unique: along the tile axis every new
+//          piece starts a new share, a new segment or both, so w + i grows).
+
+__device__ __forceinline__ int clamp_len(const int32_t *seq_lens, int b, int cap) {
+    return min(max(seq_lens[b], 0), cap);
+}
+
+// Sum over the wave of an int (every lane gets the result).
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_scan(int x, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ long long uniform64(long long x) {
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)(x & 0xffffffffll));
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)x >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+// Tile counts of the sequences: total tiles of all segments, and (for a
+// target tile position `x` < total) the sequence b whose segments hold it and
+// the number of tiles before that sequence's first segment.  Every lane of
+// the wave returns the same values.
+struct SegmentLocation {
+    long long total;   // N: tiles of all segments
+    int b;             // sequence holding tile x
+    int len;           // its (clamped) length
+    long long before;  // tiles of all segments of sequences < b
+};
+
+__device__ __forceinline__ SegmentLocation locate_tile(const int32_t *seq_lens, int B, int Hkv, int cap,
+                                                       int TT, long long x, int lane) {
+    SegmentLocation loc{0, -1, 0, 0};
+    long long run = 0;  // tiles of sequences before this chunk
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        const int bb = c0 + lane;
+        const int ln = bb < B ? clamp_len(seq_lens, bb, cap) : 0;
+        const int n = (ln + TT - 1) / TT;
+        const int incl = wave_scan(n, lane);
+        const long long lo = (run + incl - n) * Hkv, hi = (run + incl) * Hkv;
+        const unsigned long long hit = __ballot(bb < B && lo <= x && x < hi);
+        if (loc.b < 0 && hit != 0ull) {
+            const int l = __builtin_ctzll(hit);
+            loc.b = c0 + l;
+            loc.len = __shfl(ln, l, 64);
+            loc.before = (run + __shfl(incl - n, l, 64)) * Hkv;
+        }
+        run += __shfl(incl, 63, 64);
+    }
+    loc.total = run * Hkv;
+    // identical in every lane: keep them in scalar registers
+    loc.b = __builtin_amdgcn_readfirstlane(loc.b);
+    loc.len = __builtin_amdgcn_readfirstlane(loc.len);
+    loc.total = uniform64(loc.total);
+    loc.before = uniform64(loc.before);
+    return loc;
+}
+
+// Tiles of all segments before sequence b's first one, and of all segments.
+__device__ __forceinline__ void prefix_tiles(const int32_t *seq_lens, int B, int Hkv, int cap, int TT, int b,
+                                             int lane, long long &before, long long &total) {
+    long long run = 0, pre = 0;
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        const int bb = c0 + lane;
+        const int n = bb < B ? (clamp_len(seq_lens, bb, cap) + TT - 1) / TT : 0;
+        const int cnt = wave_sum(bb < b ? n : 0);
+        pre += cnt;
+        run += wave_sum(n);
+    }
+    before = uniform64(pre * Hkv);
+    total = uniform64(run * Hkv);
+}
+
+// The share of workgroup w: [share_begin(w), share_begin(w + 1)).
+__device__ __forceinline__ long long share_begin(long long w, long long N, long long P) { return w * N / P; }
+
+// Largest workgroup whose share starts at or before tile x (the one holding x).
+__device__ __forceinline__ long long share_of(long long x, long long N, long long P) {
+    return ((x + 1) * P + N - 1) / N - 1;
+}
+
+// --------------------------------------------------------- one key range
+//
+// The workgroup's four waves process keys [t_begin, t_end) of segment
+// (b, kvh), whose length is len: wave w takes tiles w, w+4, ..., each wave
+// keeps its own (m, l, acc), and the waves are folded in ascending order
+// through LDS into partial slot `slot` (or straight into `out` when direct).
+// Must be called by all threads of the workgroup; ends with a barrier, after
+// which LDS may be reused.
+template <int D, int NB, bool PAGED, int PV, bool DBUF>
+__device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB> &lds, int b, int kvh,
+                                              int len, int t_begin, int t_end, size_t slot, bool direct) {
     using S = Shape<D>;
     constexpr int TT = 16 * NB;  // keys per wave tile
-    __shared__ FoldLds<D, NB> lds;
-
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int r = lane & 15;
     const int grp = lane >> 4;
-
-    const int split = blockIdx.x % a.num_splits;
-    const int bk = blockIdx.x / a.num_splits;
-    const int kvh = bk % a.Hkv;
-    const int b = bk / a.Hkv;
-    // Out-of-range lengths / page ids are clamped so that no access can leave
-    // the caller's buffers (the results for such inputs are unspecified).
     const int cap = PAGED ? a.max_pages * a.page_size : a.S_max;
-    const int len = min(max(a.seq_lens[b], 0), cap);
-    const int t_begin = split * a.split_tokens;
-    const int t_end = min(len, t_begin + a.split_tokens);
     const int ntiles = t_end > t_begin ? (t_end - t_begin + TT - 1) / TT : 0;
     const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
@@ -410,36 +553,71 @@ __global__ __launch_bounds__(64 * kWaves) void gqa_split_kernel(const SplitArgs 
     // Resources of the rows a tile reads.  Contiguous: the whole (b, kvh)
     // slab up to len.  Paged: the tile's page up to len (one table read).
     const size_t slab = (size_t)D;
-    auto issue = [&](Tile<D, NB> &tile, int it) {
+    // Paged: lane i holds the page of this wave's tile (64*chunk + i), read
+    // once per 64 tiles instead of one dependent scalar load per tile.
+    int page_vec = 0;
+    auto load_pages = [&](int chunk) {
+        if constexpr (PAGED) {
+            const int t0 = t_begin + (wave + kWaves * (64 * chunk + lane)) * TT;
+            page_vec = 0;
+            if (t0 < min(t_end, cap)) page_vec = a.page_table[(size_t)b * a.max_pages + t0 / a.page_size];
+        }
+    };
+    load_pages(0);
+    auto issue = [&](Tile<D, NB> &tile, int it, int parts) {
         const int t0 = t_begin + (wave + kWaves * it) * TT;
         if constexpr (PAGED) {
+            if (it > 0 && (it & 63) == 0) load_pages(it >> 6);
             const int pidx = t0 / a.page_size;
             const int row0 = t0 - pidx * a.page_size;
-            const int page = min(max(__builtin_amdgcn_readfirstlane(a.page_table[(size_t)b * a.max_pages + pidx]), 0),
-                                 a.num_pages - 1);
+            const int page = min(max(__builtin_amdgcn_readlane(page_vec, it & 63), 0), a.num_pages - 1);
             const int rows = min(a.page_size, len - pidx * a.page_size);
             const size_t base = ((size_t)page * a.Hkv + kvh) * (size_t)a.page_size * slab;
             __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, rows * D * 2, kRsrcWord3);
             __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, rows * D * 2, kRsrcWord3);
-            load_tile<D, NB>(tile, rk, rv, row0, r, grp);
+            load_tile<D, NB>(tile, rk, rv, row0, r, grp, parts);
         } else {
             const size_t base = ((size_t)b * a.Hkv + kvh) * (size_t)a.S_max * slab;
             __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, len * D * 2, kRsrcWord3);
             __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, len * D * 2, kRsrcWord3);
-            load_tile<D, NB>(tile, rk, rv, t0, r, grp);
+            load_tile<D, NB>(tile, rk, rv, t0, r, grp, parts);
         }
     };
     auto tile_start = [&](int it) { return t_begin + (wave + kWaves * it) * TT; };
 
     unsigned short *stage = lds.stage(wave);
-    Tile<D, NB> buf0, buf1;
-    if (my_tiles > 0) issue(buf0, 0);
-    for (int it = 0; it < my_tiles; it += 2) {
-        if (it + 1 < my_tiles) issue(buf1, it + 1);
-        compute_tile<D, NB, PV>(buf0, qb, st, tile_start(it), t_end, r, grp, a.qk_scale_log2, stage);
-        if (it + 1 < my_tiles) {
-            if (it + 2 < my_tiles) issue(buf0, it + 2);
-            compute_tile<D, NB, PV>(buf1, qb, st, tile_start(it + 1), t_end, r, grp, a.qk_scale_log2, stage);
+    if constexpr (DBUF) {
+        // Two tile buffers: the next tile's loads are in flight during this tile's math.
+        Tile<D, NB> buf0, buf1;
+        if (my_tiles > 0) issue(buf0, 0, kLoadK | kLoadV);
+        for (int it = 0; it < my_tiles; it += 2) {
+            if (it + 1 < my_tiles) issue(buf1, it + 1, kLoadK | kLoadV);
+            compute_tile<D, NB, PV>(buf0, qb, st, tile_start(it), t_end, r, grp, a.qk_scale_log2, stage);
+            if (it + 1 < my_tiles) {
+                if (it + 2 < my_tiles) issue(buf0, it + 2, kLoadK | kLoadV);
+                compute_tile<D, NB, PV>(buf1, qb, st, tile_start(it + 1), t_end, r, grp, a.qk_scale_log2, stage);
+            }
+        }
+    } else {
+        // One tile of registers, refilled as soon as each part is dead: the next
+        // tile's V loads go out once this tile's V is in LDS, its K loads once
+        // QK^T has consumed K, so they fly during softmax and PV.  Half the
+        // registers of the double buffer, so more waves fit per SIMD.
+        Tile<D, NB> buf;
+        if (my_tiles > 0) issue(buf, 0, kLoadV | kLoadK);
+        for (int it = 0; it < my_tiles; ++it) {
+            const bool more = it + 1 < my_tiles;
+            if constexpr (PV == kPvBf16) {
+                stage_v<D, NB>(buf, r, grp, stage);
+                if (more) issue(buf, it + 1, kLoadV);
+                f32x4_t sc[NB];
+                qk_softmax<D, NB>(buf, qb, st, tile_start(it), t_end, grp, a.qk_scale_log2, sc);
+                if (more) issue(buf, it + 1, kLoadK);
+                pv_tile<D, NB, PV>(buf, sc, st, r, grp, stage);
+            } else {
+                compute_tile<D, NB, PV>(buf, qb, st, tile_start(it), t_end, r, grp, a.qk_scale_log2, stage);
+                if (more) issue(buf, it + 1, kLoadK | kLoadV);
+            }
         }
     }
 
@@ -474,13 +652,11 @@ __global__ __launch_bounds__(64 * kWaves) void gqa_split_kernel(const SplitArgs 
     }
     __syncthreads();
 
-    // Fold the waves in ascending order: this split's partial (or the output).
+    // Fold the waves in ascending order: this range's partial (or the output).
     const int G = a.G;
-    const int nsplit = a.num_splits;
-    const bool direct = nsplit == 1;
     float *out_rows = a.out + ((size_t)b * a.Hq + (size_t)kvh * G) * D;
-    float *my_acc = a.part_acc + ((size_t)bk * nsplit + split) * G * D;
-    float *my_ml = a.part_ml + ((size_t)bk * nsplit + split) * G * 2;
+    float *my_acc = a.part_acc + slot * G * D;
+    float *my_ml = a.part_ml + slot * G * 2;
     for (int col = threadIdx.x; col < G * (D / 4); col += 64 * kWaves) {
         const int g = col / (D / 4);
         const int d = 4 * (col - g * (D / 4));
@@ -508,28 +684,91 @@ __global__ __launch_bounds__(64 * kWaves) void gqa_split_kernel(const SplitArgs 
             }
         }
     }
-    if (direct || !a.fused) return;
+    __syncthreads();
+}
 
-    // Two-level fold across workgroups: the last split to finish in each group
-    // of fold_group splits folds that group; the last group to finish folds the
-    // groups into the output (one level when there is a single group).
-    const int ngroups = a.fold_groups;
-    const int grp_id = split / a.fold_group;
-    const int g0 = grp_id * a.fold_group;
-    const int gn = min(a.fold_group, nsplit - g0);
-    unsigned int *ctr = a.counters + (size_t)bk * (ngroups + 1);
-    if (!arrive_last(ctr + grp_id, (unsigned)gn, lds)) return;
-    const float *src_acc = a.part_acc + ((size_t)bk * nsplit + g0) * G * D;
-    const float *src_ml = a.part_ml + ((size_t)bk * nsplit + g0) * G * 2;
-    if (ngroups == 1) {
-        fold_blocks<D>(src_acc, src_ml, gn, G, nullptr, nullptr, out_rows);
+template <int D, int NB, bool PAGED, int PV, bool DBUF, int PART>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEu<D, DBUF>)))
+void gqa_split_kernel(const SplitArgs a) {
+    constexpr int TT = 16 * NB;
+    __shared__ FoldLds<D, NB> lds;
+    const int cap = PAGED ? a.max_pages * a.page_size : a.S_max;
+    const int G = a.G;
+
+    if constexpr (PART == kPartitionEven) {
+        // This workgroup's equal share of all tiles, walked piece by piece.
+        const int lane = threadIdx.x & 63;
+        const long long P = gridDim.x;
+        SegmentLocation loc = locate_tile(a.seq_lens, a.B, a.Hkv, cap, TT, -1, lane);  // the total only
+        const long long N = loc.total;
+        long long cur = share_begin(blockIdx.x, N, P);
+        const long long end = share_begin(blockIdx.x + 1, N, P);
+        if (cur >= end) return;
+        loc = locate_tile(a.seq_lens, a.B, a.Hkv, cap, TT, cur, lane);
+        int b = loc.b;
+        int len = loc.len;
+        int nb_tiles = (len + TT - 1) / TT;
+        const int rel = (int)(cur - loc.before);  // < Hkv * nb_tiles
+        int kvh = __builtin_amdgcn_readfirstlane(rel / nb_tiles);
+        int off = __builtin_amdgcn_readfirstlane(rel - kvh * nb_tiles);
+        while (cur < end) {
+            const int take = (int)min((long long)(nb_tiles - off), end - cur);
+            const size_t slot = (size_t)blockIdx.x + (size_t)b * a.Hkv + kvh;
+            process_range<D, NB, PAGED, PV, DBUF>(a, lds, b, kvh, len, off * TT, min(len, (off + take) * TT),
+                                                  slot, false);
+            cur += take;
+            off += take;
+            if (off == nb_tiles && cur < end) {
+                off = 0;
+                if (++kvh == a.Hkv) {
+                    kvh = 0;
+                    do {  // sequences of length 0 hold no tiles
+                        ++b;
+                        len = b < a.B ? __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens, b, cap)) : 1;
+                    } while (len == 0);
+                    nb_tiles = (len + TT - 1) / TT;
+                }
+            }
+        }
         return;
+    } else {
+        const int split = blockIdx.x % a.num_splits;
+        const int bk = blockIdx.x / a.num_splits;
+        const int kvh = bk % a.Hkv;
+        const int b = bk / a.Hkv;
+        // Out-of-range lengths / page ids are clamped so that no access can leave
+        // the caller's buffers (the results for such inputs are unspecified).
+        const int len = clamp_len(a.seq_lens, b, cap);
+        const int t_begin = split * a.split_tokens;
+        const int t_end = min(len, t_begin + a.split_tokens);
+        const int nsplit = a.num_splits;
+        const bool direct = nsplit == 1;
+        process_range<D, NB, PAGED, PV, DBUF>(a, lds, b, kvh, len, t_begin, t_end,
+                                              (size_t)bk * nsplit + split, direct);
+        if (direct || !a.fused) return;
+
+        // Two-level fold across workgroups: the last split to finish in each group
+        // of fold_group splits folds that group; the last group to finish folds the
+        // groups into the output (one level when there is a single group).
+        float *out_rows = a.out + ((size_t)b * a.Hq + (size_t)kvh * G) * D;
+        const int ngroups = a.fold_groups;
+        const int grp_id = split / a.fold_group;
+        const int g0 = grp_id * a.fold_group;
+        const int gn = min(a.fold_group, nsplit - g0);
+        unsigned int *ctr = a.counters + (size_t)bk * (ngroups + 1);
+        if (!arrive_last(ctr + grp_id, (unsigned)gn, lds)) return;
+        const float *src_acc = a.part_acc + ((size_t)bk * nsplit + g0) * G * D;
+        const float *src_ml = a.part_ml + ((size_t)bk * nsplit + g0) * G * 2;
+        if (ngroups == 1) {
+            fold_blocks<D>(src_acc, src_ml, gn, G, nullptr, nullptr, out_rows);
+            return;
+        }
+        fold_blocks<D>(src_acc, src_ml, gn, G, a.grp_acc + ((size_t)bk * ngroups + grp_id) * G * D,
+                       a.grp_ml + ((size_t)bk * ngroups + grp_id) * G * 2, nullptr);
+        if (!arrive_last(ctr + ngroups, (unsigned)ngroups, lds)) return;
+        fold_blocks<D>(a.grp_acc + (size_t)bk * ngroups * G * D, a.grp_ml + (size_t)bk * ngroups * G * 2,
+                       ngroups, G, nullptr, nullptr, out_rows);
     }
-    fold_blocks<D>(src_acc, src_ml, gn, G, a.grp_acc + ((size_t)bk * ngroups + grp_id) * G * D,
-                   a.grp_ml + ((size_t)bk * ngroups + grp_id) * G * 2, nullptr);
-    if (!arrive_last(ctr + ngroups, (unsigned)ngroups, lds)) return;
-    fold_blocks<D>(a.grp_acc + (size_t)bk * ngroups * G * D, a.grp_ml + (size_t)bk * ngroups * G * 2,
-                   ngroups, G, nullptr, nullptr, out_rows);
 }
 
 // Combine: one workgroup of 256 threads per (b, h, chunk of 4*NCOL dims).
@@ -553,22 +792,47 @@ __device__ __forceinline__ void lse_merge(float &m, float &l, f32x4_t &o, float 
 template <int NCOL>
 __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const CombineArgs a) {
     constexpr int NSG = kCombineThreads / NCOL;
-    constexpr int U = 8;  // splits per thread per round of loads
+    constexpr int U = 4;  // splits per thread per round of loads
     const int D = a.D;
     const int chunks = D / (4 * NCOL);
     const size_t bh = blockIdx.x / chunks;
     const int d0 = (blockIdx.x % chunks) * 4 * NCOL;
     const int c = threadIdx.x % NCOL;
     const int sg = threadIdx.x / NCOL;
-    const int S = a.num_splits;
     const int G = a.G;
     const size_t b = bh / a.Hq;
     const int h = (int)(bh % a.Hq);
-    const size_t bk = b * (a.Hq / G) + h / G;   // b * Hkv + kvh
+    const size_t bk = b * (a.Hq / G) + h / G;   // segment b * Hkv + kvh
     const int g = h % G;
-    // split s of head g: acc at ((bk*S + s)*G + g)*D, ml at ((bk*S + s)*G + g)*2
-    const float *ml = a.part_ml + (bk * S * G + g) * 2;
-    const float *acc = a.part_acc + (bk * S * G + g) * D + d0 + 4 * c;
+    // The segment's partials are the consecutive slots [lo, lo + S); slot k of
+    // head g: acc at (k*G + g)*D, ml at (k*G + g)*2.
+    size_t lo;
+    int S;
+    long long N = 0, P = 1, w0 = 0;  // even partition: slot lo + s belongs to share w0 + s
+    bool maybe_empty = false;         // shares can be empty only when there are fewer tiles than shares
+    if (a.partition == kPartitionFixed) {
+        S = a.num_splits;
+        lo = bk * S;
+    } else {
+        long long before, total;
+        const int lane = threadIdx.x & 63;
+        prefix_tiles(a.seq_lens, a.B, a.Hkv, a.cap, a.tile, (int)b, lane, before, total);
+        const int n = (clamp_len(a.seq_lens, (int)b, a.cap) + a.tile - 1) / a.tile;
+        N = total;
+        P = a.shares;
+        maybe_empty = N < P;
+        if (n == 0) {
+            S = 0;
+            lo = 0;
+        } else {
+            const long long z = before + (long long)(h / G) * n;
+            w0 = share_of(z, N, P);
+            S = (int)(share_of(z + n - 1, N, P) - w0 + 1);
+            lo = (size_t)(w0 + (long long)bk);
+        }
+    }
+    const float *ml = a.part_ml + (lo * G + g) * 2;
+    const float *acc = a.part_acc + (lo * G + g) * D + d0 + 4 * c;
     const size_t ml_stride = (size_t)G * 2, acc_stride = (size_t)G * D;
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -582,7 +846,9 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const Comb
             mv[u] = -INFINITY;
             lv[u] = 0.f;
             av[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (s < S) {
+            // even partition: a share that holds no tile wrote nothing
+            const bool used = !maybe_empty || share_begin(w0 + s, N, P) < share_begin(w0 + s + 1, N, P);
+            if (s < S && used) {
                 mv[u] = ml[s * ml_stride];
                 lv[u] = ml[s * ml_stride + 1];
                 av[u] = *reinterpret_cast<const f32x4_t *>(acc + s * acc_stride);
@@ -621,7 +887,22 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const Comb
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
 
-int tile_tokens_for(int D) { return D == 64 ? 64 : (D == 128 ? 32 : 16); }
+int env_int(const char *name, int fallback) {
+    const char *s = getenv(name);
+    if (s == nullptr || *s == '\0') return fallback;
+    const int v = atoi(s);
+    return v > 0 ? v : fallback;
+}
+
+// Keys per wave tile: 16 KB of K+V per wave (64 keys at D=64, 32 at D=128,
+// 16 at D=256).  GQA_DECODE_TILE (16, 32 or 64) overrides it for A/B runs
+// when the result stays within 16 KB.
+int tile_tokens_for(int D, bool double_buffer) {
+    const int dflt = double_buffer ? (D == 64 ? 64 : (D == 128 ? 32 : 16)) : (D == 64 ? 32 : 16);
+    const int t = env_int("GQA_DECODE_TILE", dflt);
+    if ((t == 16 || t == 32 || t == 64) && t * D <= 4096) return t;
+    return dflt;
+}
 
 bool supported_dim(int D) { return D == 64 || D == 128 || D == 256; }
 
@@ -657,17 +938,19 @@ constexpr size_t kCounterBytes = 65536;
 constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(unsigned int));
 
 // Byte offsets of the workspace regions (all 256-byte aligned).
-WorkspaceLayout workspace_layout(int B, int Hq, int Hkv, int D, int S, int fused, int groups) {
-    (void)Hkv;
+// `slots` partial blocks of G heads: B*Hkv*S for fixed splits, P + B*Hkv for
+// even shares.
+WorkspaceLayout workspace_layout(int B, int Hq, int Hkv, int D, int64_t slots, int fused, int groups) {
     WorkspaceLayout w{};
     const size_t rows = (size_t)B * Hq;
+    const size_t G = (size_t)(Hq / Hkv);
     size_t off = 0;
     w.counters = 0;
     if (fused) off += kCounterBytes;
     w.part_acc = off;
-    off += align_up(rows * S * D * sizeof(float), 256);
+    off += align_up((size_t)slots * G * D * sizeof(float), 256);
     w.part_ml = off;
-    off += align_up(rows * S * 2 * sizeof(float), 256);
+    off += align_up((size_t)slots * G * 2 * sizeof(float), 256);
     w.grp_acc = off;
     w.grp_ml = off;
     if (fused && groups > 1) {
@@ -689,6 +972,13 @@ int env_fused() {
     return atoi(s) != 0 ? 1 : 0;
 }
 
+// Tile buffering: one register tile per wave refilled early (the default;
+// it leaves room for twice the waves), or GQA_DECODE_DBUF=1 for two.
+int env_dbuf() {
+    const char *s = getenv("GQA_DECODE_DBUF");
+    return (s != nullptr && strcmp(s, "1") == 0) ? 1 : 0;
+}
+
 // PV contraction: GQA_DECODE_PV=f32 selects the fp32-MFMA variant for A/B.
 int env_pv_mode() {
     const char *s = getenv("GQA_DECODE_PV");
@@ -706,14 +996,17 @@ int env_splits() {
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const float *part_ml,
-                          float *out, int B, int Hq, int Hkv, int D, hipStream_t stream) {
-    CombineArgs ca{part_acc, part_ml, out, D, Hq / Hkv, Hq, plan.num_splits};
+                          float *out, const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int cap,
+                          hipStream_t stream) {
+    CombineArgs ca{part_acc, part_ml, out, seq_lens, D, Hq / Hkv, Hq, plan.num_splits,
+                   plan.partition, B, Hkv, cap, plan.tile_tokens, plan.grid};
     // Narrow dim chunks (more workgroups, fewer splits per thread) when there
-    // are few heads and many splits.
+    // are few heads and many partials per head.
     const int64_t heads = (int64_t)B * Hq;
-    if (heads * (D / 64) >= 256 || plan.num_splits <= 64) {
+    const int pieces = plan.max_pieces;
+    if (heads * (D / 64) >= 256 || pieces <= 64) {
         hipLaunchKernelGGL(gqa_combine_kernel<16>, dim3((unsigned)(heads * (D / 64))), dim3(kCombineThreads), 0, stream, ca);
-    } else if (heads * (D / 32) >= 256 || plan.num_splits <= 256) {
+    } else if (heads * (D / 32) >= 256 || pieces <= 256) {
         hipLaunchKernelGGL(gqa_combine_kernel<8>, dim3((unsigned)(heads * (D / 32))), dim3(kCombineThreads), 0, stream, ca);
     } else {
         hipLaunchKernelGGL(gqa_combine_kernel<4>, dim3((unsigned)(heads * (D / 16))), dim3(kCombineThreads), 0, stream, ca);
@@ -726,12 +1019,18 @@ hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, hipStream
     if constexpr (NB * D > 256) {  // at most 16 KB of K+V (64 * NB * D bytes) per wave tile
         return hipErrorInvalidValue;
     } else {
-        if (plan.pv_mode == kPvF32)
-            hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32>), dim3((unsigned)plan.grid),
-                               dim3(64 * kWaves), 0, stream, a);
-        else
-            hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16>), dim3((unsigned)plan.grid),
-                               dim3(64 * kWaves), 0, stream, a);
+        const dim3 grid((unsigned)plan.grid), block(64 * kWaves);
+        const bool even = plan.partition == kPartitionEven;
+        if (plan.pv_mode == kPvF32) {
+            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionEven>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionFixed>), grid, block, 0, stream, a);
+        } else if (plan.double_buffer) {
+            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionEven>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionFixed>), grid, block, 0, stream, a);
+        } else {
+            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed>), grid, block, 0, stream, a);
+        }
         return hipGetLastError();
     }
 }
@@ -752,7 +1051,7 @@ constexpr int kPhaseCombine = 2;
 gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, void *workspace,
                  hipStream_t stream, int phases) {
     if (!plan.direct) {
-        WorkspaceLayout w = workspace_layout(a.B, a.Hq, a.Hkv, D, plan.num_splits, plan.fused,
+        WorkspaceLayout w = workspace_layout(a.B, a.Hq, a.Hkv, D, plan.slots, plan.fused,
                                              plan.fold_groups);
         char *base = static_cast<char *>(workspace);
         a.part_acc = reinterpret_cast<float *>(base + w.part_acc);
@@ -775,7 +1074,8 @@ gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, void *
         if (e != hipSuccess) return GQA_ERR_HIP;
     }
     if (plan.direct || plan.fused || !(phases & kPhaseCombine)) return GQA_OK;
-    e = launch_combine(plan, a.part_acc, a.part_ml, a.out, a.B, a.Hq, a.Hkv, D, stream);
+    const int cap = paged ? a.max_pages * a.page_size : a.S_max;
+    e = launch_combine(plan, a.part_acc, a.part_ml, a.out, a.seq_lens, a.B, a.Hq, a.Hkv, D, cap, stream);
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
@@ -816,17 +1116,49 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
     if (!supported_dim(D) || Hq / Hkv > kMaxHeadsPerKv) return GQA_ERR_UNSUPPORTED;
     if (page_size > 0 && page_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
 
-    int tt = tile_tokens_for(D);
+    const int dbuf = env_dbuf();
+    int tt = tile_tokens_for(D, dbuf != 0);
     if (page_size > 0) {
         while (page_size % tt != 0) tt /= 2;  // a tile never straddles a page (tt >= 16)
     }
     const int tiles_total = max_seq_len > 0 ? (max_seq_len + tt - 1) / tt : 1;
-    // Splits: enough workgroups to give every CU two of them, and no split
-    // longer than kMaxSplitTokens keys (so one long sequence in a ragged
-    // batch cannot serialise behind a single workgroup), but at least one
-    // tile per wave.
-    constexpr int kMaxSplitTokens = 1024;
     const int base = B > 0 ? B * Hkv : 1;
+    const char *part_env = getenv("GQA_DECODE_PARTITION");
+    const bool want_fixed = part_env != nullptr && strcmp(part_env, "fixed") == 0;
+    plan->tile_tokens = tt;
+    plan->waves = kWaves;
+    plan->pv_mode = env_pv_mode();
+    plan->double_buffer = dbuf;
+    plan->fold_group = 0;
+    plan->fold_groups = 0;
+    plan->fused = 0;
+
+    // Even shares (the default for batches): about two workgroups per CU, each at least
+    // one tile per wave at full length; a segment short enough for one
+    // workgroup (<= 4 tiles per wave) is written directly instead.
+    // A single sequence cannot be ragged: fixed splits give it the same work
+    // split without the device-side length scan.
+    if (num_splits == 0 && !want_fixed && !env_fused() && tiles_total > 4 * kWaves && B > 1) {
+        const int64_t tiles_max = (int64_t)base * tiles_total;
+        int64_t P = env_int("GQA_DECODE_SHARES", 2 * cu_count);
+        if (P > (tiles_max + kWaves - 1) / kWaves) P = (tiles_max + kWaves - 1) / kWaves;
+        if (P < 1) P = 1;
+        if (P > INT32_MAX / 2) return GQA_ERR_SHAPE;
+        plan->partition = kPartitionEven;
+        plan->num_splits = 0;
+        plan->split_tokens = (int)((tiles_max + P - 1) / P) * tt;  // keys per share at full length
+        plan->grid = B > 0 ? (int)P : 0;
+        plan->direct = 0;
+        plan->slots = (int64_t)P + base;
+        plan->max_pieces = (int)std::min<int64_t>(P, (int64_t)tiles_total * P / tiles_max + 1);
+        plan->workspace_bytes = workspace_layout(B, Hq, Hkv, D, plan->slots, 0, 0).total;
+        return GQA_OK;
+    }
+
+    // Fixed splits: enough workgroups to give every CU two of them, and no
+    // split longer than kMaxSplitTokens keys, but at least one tile per wave;
+    // a short segment (<= 4 tiles per wave) gets a single split.
+    const int kMaxSplitTokens = env_int("GQA_DECODE_SPLIT_KEYS", 2048);
     int S = num_splits;
     if (S == 0) {
         const int fill = (2 * cu_count + base - 1) / base;
@@ -834,22 +1166,23 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
         S = fill > len_cap ? fill : len_cap;
         const int most = (tiles_total + kWaves - 1) / kWaves;
         if (S > most) S = most;
+        if (tiles_total <= 4 * kWaves && !env_fused()) S = 1;
     }
     if (S > tiles_total) S = tiles_total;
     if (S < 1) S = 1;
     int split_tiles = (tiles_total + S - 1) / S;
     S = (tiles_total + split_tiles - 1) / split_tiles;  // drop splits that would be empty
 
+    plan->partition = kPartitionFixed;
     plan->num_splits = S;
     plan->split_tokens = split_tiles * tt;
-    plan->tile_tokens = tt;
-    plan->waves = kWaves;
     const int64_t grid = (int64_t)(B > 0 ? B : 0) * Hkv * S;
     if (grid > INT32_MAX) return GQA_ERR_SHAPE;
     plan->grid = (int)grid;
     plan->direct = S == 1 ? 1 : 0;
+    plan->slots = (int64_t)base * S;
+    plan->max_pieces = S;
     plan->fused = plan->direct ? 0 : env_fused();
-    plan->pv_mode = env_pv_mode();
     // Fold groups: one level up to 8 splits, else about sqrt(S) splits per
     // group and about sqrt(S) groups, so no workgroup folds many blocks.
     int fg = S;
@@ -863,7 +1196,7 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
         plan->fused = 0;  // too many (sequence, kv head) pairs for the counter area
     plan->workspace_bytes = 0;
     if (!plan->direct)
-        plan->workspace_bytes = workspace_layout(B, Hq, Hkv, D, S, plan->fused, plan->fold_groups).total;
+        plan->workspace_bytes = workspace_layout(B, Hq, Hkv, D, plan->slots, plan->fused, plan->fold_groups).total;
     return GQA_OK;
 }
 
@@ -986,17 +1319,19 @@ gqa_status_t gqa_paged_decode_partials(const void *q, const void *k_pool, const 
                         kPhaseSplit);
 }
 
-gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
-                                int D, int max_seq_len, int page_size, int num_splits, float *out,
-                                hipStream_t stream) {
+gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, const int32_t *seq_lens,
+                                int B, int Hq, int Hkv, int D, int max_seq_len, int page_size,
+                                int num_splits, float *out, hipStream_t stream) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_seq_len < 0 || page_size < 0 ||
         num_splits < 0)
         return GQA_ERR_SHAPE;
     if (!supported_dim(D) || Hq / Hkv > kMaxHeadsPerKv) return GQA_ERR_UNSUPPORTED;
     if (page_size > 0 && page_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
     if (B == 0) return GQA_OK;
-    if (out == nullptr) return GQA_ERR_NULL;
-    if (misaligned(out, 16) || (workspace != nullptr && misaligned(workspace, 16))) return GQA_ERR_ALIGN;
+    if (out == nullptr || seq_lens == nullptr) return GQA_ERR_NULL;
+    if (misaligned(out, 16) || misaligned(seq_lens, 4) ||
+        (workspace != nullptr && misaligned(workspace, 16)))
+        return GQA_ERR_ALIGN;
     gqa_plan_t plan;
     gqa_status_t s = plan_for_call(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, &plan);
     if (s != GQA_OK) return s;
@@ -1005,7 +1340,14 @@ gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, i
     if (workspace_bytes < plan.workspace_bytes) return GQA_ERR_WORKSPACE;
     SplitArgs a{};
     a.out = out;
+    a.seq_lens = seq_lens;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+    if (page_size > 0) {
+        a.page_size = page_size;
+        a.max_pages = max_seq_len / page_size;
+    } else {
+        a.S_max = max_seq_len;
+    }
     return run(plan, a, D, page_size > 0, const_cast<void *>(workspace), stream, kPhaseCombine);
 }
 

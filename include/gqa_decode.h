@@ -62,16 +62,20 @@ typedef enum gqa_status {
 
 /* How a call is laid out on the device (host-side, deterministic). */
 typedef struct gqa_plan {
-    int num_splits;         /* S: KV partitions per (sequence, kv head) */
-    int split_tokens;       /* tokens per split, a multiple of tile_tokens */
-    int tile_tokens;        /* tokens one wave stages per pipeline step */
+    int partition;          /* 0: fixed splits per (sequence, kv head); 1: even shares */
+    int num_splits;         /* fixed: S, KV partitions per (sequence, kv head); even: 0 */
+    int split_tokens;       /* fixed: keys per split; even: keys per share at full length */
+    int tile_tokens;        /* keys one wave stages per pipeline step */
     int waves;              /* waves (of 64 lanes) per workgroup */
-    int grid;               /* workgroups of the split kernel: B * Hkv * S */
+    int grid;               /* workgroups of the split kernel: B * Hkv * S, or the shares */
     int direct;             /* 1: S == 1, the split kernel writes `out` itself */
+    int max_pieces;         /* most partials one (sequence, kv head) can have */
+    int64_t slots;          /* partial blocks in the workspace: B*Hkv*S, or shares + B*Hkv */
     int fused;              /* 1: the split kernel also folds the partials (one launch) */
     int fold_group;         /* splits folded together at the first fold level */
     int fold_groups;        /* first-level groups (1 = a single fold level) */
     int pv_mode;            /* PV contraction: 1 = bf16 MFMA with P split hi+lo, 0 = fp32 MFMA */
+    int double_buffer;      /* 1: two tile buffers per wave; 0: one (more waves per SIMD) */
     size_t workspace_bytes; /* scratch the call needs (0 when direct) */
 } gqa_plan_t;
 
@@ -79,9 +83,12 @@ typedef struct gqa_plan {
  * The split plan for a call (the split-count rule of the AstrAI csrc commit
  * log: fill the device, bounded by the tile count).  max_seq_len is the cache
  * capacity (contiguous S_max, or max_pages * page_size when paged);
- * page_size = 0 means a contiguous cache.  num_splits = 0 picks the count from
- * cu_count; num_splits > 0 forces it (clamped to the tile count).  Pure host
- * code: needs no GPU.
+ * page_size = 0 means a contiguous cache.  num_splits = 0 picks the layout
+ * from cu_count: by default even shares (the concatenated tiles of all
+ * sequences cut into equal parts on the device, from seq_lens), or a single
+ * direct split for short caches; num_splits > 0 forces that many fixed splits
+ * per (sequence, kv head) (clamped to the tile count).  Pure host code: needs
+ * no GPU.
  */
 gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int head_dim, int max_seq_len, int page_size,
                              int num_splits, int cu_count, gqa_plan_t *plan);
@@ -139,10 +146,10 @@ gqa_status_t gqa_paged_decode(const void *q, const void *k_pool, const void *v_p
  * gqa_paged_decode and launch only the split kernel: it leaves the
  * unnormalised (m, l, acc) partials in `workspace` (when the plan is direct
  * it writes `out` instead).  gqa_decode_combine then folds those partials
- * into `out` (it launches nothing for a direct plan); its shape arguments,
- * num_splits and the environment must be those of the partials call, so that
- * both compute the same plan (max_seq_len = S_max and page_size = 0 for a
- * contiguous cache).  Running the two on one stream gives bit-for-bit the
+ * into `out` (it launches nothing for a direct plan); its seq_lens, shape
+ * arguments, num_splits and the environment must be those of the partials
+ * call, so that both compute the same plan (max_seq_len = S_max and
+ * page_size = 0 for a contiguous cache).  Running the two on one stream gives bit-for-bit the
  * result of the one-call entry point.
  */
 gqa_status_t gqa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
@@ -156,9 +163,10 @@ gqa_status_t gqa_paged_decode_partials(const void *q, const void *k_pool, const 
                                        int max_pages, float scale, float *out, void *workspace,
                                        size_t workspace_bytes, int num_splits, hipStream_t stream);
 
-gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, int B, int Hq,
-                                int Hkv, int head_dim, int max_seq_len, int page_size,
-                                int num_splits, float *out, hipStream_t stream);
+gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes,
+                                const int32_t *seq_lens, int B, int Hq, int Hkv, int head_dim,
+                                int max_seq_len, int page_size, int num_splits, float *out,
+                                hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char *gqa_status_string(gqa_status_t status);

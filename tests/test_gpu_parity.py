@@ -250,9 +250,64 @@ def test_partials_then_combine_equals_one_call(paged):
         else:
             gd.gqa_decode_partials(dc.q, dc.k, dc.v, dc.seq_lens, case.scale, out=out, workspace=ws,
                                    num_splits=splits)
-        gd.gqa_decode_combine(ws, out, case.B, case.Hq, case.Hkv, case.D, cap, ps, splits)
+        gd.gqa_decode_combine(ws, dc.seq_lens, out, case.B, case.Hq, case.Hkv, case.D, cap, ps,
+                              splits)
         torch.cuda.synchronize()
         two = out.cpu().numpy()
         ref = dc.run_host(splits)
         assert np.array_equal(two.view(np.uint32), ref.view(np.uint32))
     compare(one, oracle_out(case), "partials+combine")
+
+
+# ------------------------------------------------------------------ even-share partition
+EVEN_LENS = {
+    "mixed": [1, 0, 700, 3, 5000, 17, 0, 2048, 1, 33],
+    "short_many": [(7 * i) % 40 for i in range(100)],          # B > 64: the scan loops over chunks
+    "one_long": [0, 0, 20000, 0],
+    "all_zero": [0, 0, 0],
+}
+
+
+@pytest.mark.parametrize("lens", list(EVEN_LENS))
+@pytest.mark.parametrize("shares", ["1", "3", "7", "64", "1000"])
+def test_even_shares_contiguous(monkeypatch, lens, shares):
+    """Equal shares of the concatenated tiles, any share count, ragged and empty sequences."""
+    say(f"[parity] even shares={shares} lens={lens}")
+    monkeypatch.setenv("GQA_DECODE_SHARES", shares)
+    L = EVEN_LENS[lens]
+    S_max = max(max(L), 1)
+    case = W.contig_case(len(L), 16, 4, 128, S_max, seq_lens=L, seed=60, tail="nan")
+    p = gd.gqa_decode_plan(case.B, 16, 4, 128, S_max)
+    if p.partition != 1:
+        pytest.skip("short cache: direct plan")
+    dc = DeviceCase(case)
+    out = [dc.run_host() for _ in range(2)]
+    compare(out[0], oracle_out(case), f"even shares={shares} {lens}")
+    assert np.array_equal(out[0].view(np.uint32), out[1].view(np.uint32))
+    for b, n in enumerate(L):
+        if n == 0:
+            assert np.all(out[0][b] == 0)
+
+
+@pytest.mark.parametrize("shares", ["5", "0"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_even_shares_paged(monkeypatch, shares, D):
+    say(f"[parity] even shares paged D={D} shares={shares}")
+    if shares != "0":
+        monkeypatch.setenv("GQA_DECODE_SHARES", shares)
+    L = [1, 0, 900, 31, 2000, 16, 0, 1500]
+    case = W.paged_case(len(L), 8, 2, D, 32, 250, seq_lens=L, max_len=2048, seed=61 + D)
+    assert gd.gqa_decode_plan(case.B, 8, 2, D, 2048, 32).partition == 1
+    compare(DeviceCase(case).run_host(), oracle_out(case), f"even paged D={D}")
+
+
+def test_fixed_and_even_agree_with_oracle(monkeypatch):
+    say("[parity] fixed vs even")
+    case = W.paged_case(8, 32, 8, 128, 32, 2100, max_len=8192, seed=62)
+    dc = DeviceCase(case)
+    ref = oracle_out(case)
+    even = dc.run_host()
+    monkeypatch.setenv("GQA_DECODE_PARTITION", "fixed")
+    fixed = dc.run_host()
+    compare(even, ref, "even")
+    compare(fixed, ref, "fixed")

@@ -25,17 +25,18 @@ def lib():
 
 
 def expected_workspace(B, Hq, Hkv, D, p):
-    """Split partials [B*Hq*S] x (D + 2) floats, group partials [B*Hq*groups] x (D + 2) floats
-    when there are two fold levels, and a fixed 64 KiB counter area in front when fused;
-    every region rounded up to 256 bytes."""
+    """Partial blocks (slots) of G x (D + 2) floats, group partials [B*Hq*groups] x (D + 2)
+    floats when the fused fold has two levels, and a fixed 64 KiB counter area in front when
+    fused; every region rounded up to 256 bytes."""
     if p.direct:
         return 0
     align = lambda x: (x + 255) // 256 * 256
-    rows = B * Hq
-    total = align(rows * p.num_splits * D * 4) + align(rows * p.num_splits * 2 * 4)
+    G = Hq // Hkv
+    total = align(p.slots * G * D * 4) + align(p.slots * G * 2 * 4)
     if p.fused:
         total += 65536  # fixed counter area at the front
         if p.fold_groups > 1:
+            rows = B * Hq
             total += align(rows * p.fold_groups * D * 4) + align(rows * p.fold_groups * 2 * 4)
     return total
 
@@ -66,42 +67,63 @@ def test_status_strings(lib):
 def test_plan_invariants(shape, cu):
     B, Hq, Hkv, D, cap, ps = shape
     p = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, 0, cu)
-    assert p.split_tokens % p.tile_tokens == 0
     assert p.tile_tokens % 16 == 0
     if ps:
         assert ps % p.tile_tokens == 0        # one page-table lookup per tile
-    assert p.num_splits * p.split_tokens >= cap
-    assert (p.num_splits - 1) * p.split_tokens < cap  # no split starts past the capacity
-    assert p.grid == B * Hkv * p.num_splits
-    assert p.direct == (p.num_splits == 1)
+    tiles = -(-cap // p.tile_tokens)
+    if p.partition == 1:                      # even shares
+        assert p.num_splits == 0 and p.direct == 0
+        assert 1 <= p.grid <= 2 * cu
+        assert p.grid * 4 <= B * Hkv * tiles + 3   # at least one tile per wave at full length
+        assert p.slots == p.grid + B * Hkv
+        assert p.split_tokens % p.tile_tokens == 0
+        assert p.split_tokens * p.grid >= B * Hkv * cap
+    else:                                      # fixed splits
+        assert p.split_tokens % p.tile_tokens == 0
+        assert p.num_splits * p.split_tokens >= cap
+        assert (p.num_splits - 1) * p.split_tokens < cap  # no split starts past the capacity
+        assert p.grid == B * Hkv * p.num_splits
+        assert p.direct == (p.num_splits == 1)
+        assert p.slots == B * Hkv * p.num_splits
     assert p.fused == 0   # the in-kernel fold is opt-in (GQA_DECODE_FUSED=1)
     assert p.pv_mode == 1  # bf16 MFMA PV unless GQA_DECODE_PV=f32
-    assert p.fold_group * p.fold_groups >= p.num_splits
-    assert (p.fold_groups - 1) * p.fold_group < p.num_splits
-    if p.num_splits <= 8:
-        assert p.fold_groups == 1
-    else:
-        assert p.fold_group * p.fold_group >= p.num_splits
+    assert p.double_buffer == 0
     assert p.workspace_bytes == expected_workspace(B, Hq, Hkv, D, p)
     again = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, 0, cu)
     assert again.as_dict() == p.as_dict()
 
 
+@pytest.mark.parametrize("shape", WORKLOAD_SHAPES)
+def test_fixed_plan_invariants(monkeypatch, shape):
+    monkeypatch.setenv("GQA_DECODE_PARTITION", "fixed")
+    B, Hq, Hkv, D, cap, ps = shape
+    p = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, 0, 256)
+    assert p.partition == 0
+    assert p.num_splits * p.split_tokens >= cap
+    assert p.grid == B * Hkv * p.num_splits
+    assert p.workspace_bytes == expected_workspace(B, Hq, Hkv, D, p)
+    if p.num_splits > 1:
+        assert p.split_tokens <= 2048
+
+
 def test_plan_fills_the_device():
-    # one kv head, 131072 keys: enough splits for two workgroups per CU
+    # one kv head, 131072 keys: two workgroups per CU share the keys (one sequence: fixed splits)
     p = gd.gqa_decode_plan(1, 8, 1, 128, 131072, 0, 0, 256)
-    assert p.grid >= 512
+    assert p.partition == 0 and p.grid == 512
+    # a batch gets even shares
+    p = gd.gqa_decode_plan(32, 32, 8, 128, 8192, 32, 0, 256)
+    assert p.partition == 1 and p.grid == 512
     # the GQA-6 layer (4 kv heads, 4096 keys) cannot give every wave more than one tile
     p = gd.gqa_decode_plan(1, 24, 4, 256, 4096, 0, 0, 256)
     assert p.grid == 256 and p.split_tokens == 4 * p.tile_tokens
-    # ragged paged batch: no split longer than 1024 keys
-    p = gd.gqa_decode_plan(32, 32, 8, 128, 8192, 32, 0, 256)
-    assert p.split_tokens <= 1024
+    # a short cache is one direct split per (sequence, kv head)
+    p = gd.gqa_decode_plan(1, 8, 2, 64, 512, 0, 0, 256)
+    assert p.partition == 0 and p.direct == 1 and p.workspace_bytes == 0
 
 
 def test_forced_splits_are_clamped_to_tiles():
     p = gd.gqa_decode_plan(1, 8, 2, 64, 512, 0, 1000, 256)
-    assert p.num_splits == 512 // p.tile_tokens
+    assert p.partition == 0 and p.num_splits == 512 // p.tile_tokens
     p = gd.gqa_decode_plan(1, 8, 2, 64, 512, 0, 1, 256)
     assert p.num_splits == 1 and p.direct == 1 and p.workspace_bytes == 0
     p = gd.gqa_decode_plan(2, 8, 2, 128, 1000, 0, 7, 256)
@@ -199,21 +221,24 @@ def test_fused_falls_back_when_counters_do_not_fit(monkeypatch):
 
 def test_fused_plan_workspace(monkeypatch):
     monkeypatch.setenv("GQA_DECODE_FUSED", "1")
-    for shape in WORKLOAD_SHAPES:
+    for shape in WORKLOAD_SHAPES[1:]:
         B, Hq, Hkv, D, cap, ps = shape
         p = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, 0, 256)
-        assert p.fused == 1
+        assert p.fused == 1 and p.partition == 0
         assert p.workspace_bytes == expected_workspace(B, Hq, Hkv, D, p)
 
 
 @pytest.mark.parametrize("args,code", [
     (dict(B=1, Hq=8, Hkv=3), 2), (dict(D=96), 3), (dict(out=None), 1), (dict(out=A + 4), 4),
     (dict(ws=None), 1), (dict(ws=A + 8), 4), (dict(ws_bytes=8), 5), (dict(ps=20), 3),
+    (dict(lens=None), 1), (dict(lens=A + 2), 4),
     (dict(B=0, out=None, ws=None), 0),          # nothing to do
     (dict(splits=1, ws=None, ws_bytes=0), 0),   # a direct plan has nothing to combine
 ])
 def test_combine_rejects(lib, args, code):
-    kw = dict(ws=A, ws_bytes=1 << 30, B=1, Hq=8, Hkv=2, D=128, cap=64, ps=0, splits=2, out=A)
+    kw = dict(ws=A, ws_bytes=1 << 30, lens=A, B=1, Hq=8, Hkv=2, D=128, cap=64, ps=0, splits=2,
+              out=A)
     kw.update(args)
-    assert lib.gqa_decode_combine(kw["ws"], kw["ws_bytes"], kw["B"], kw["Hq"], kw["Hkv"], kw["D"],
-                                  kw["cap"], kw["ps"], kw["splits"], kw["out"], None) == code
+    assert lib.gqa_decode_combine(kw["ws"], kw["ws_bytes"], kw["lens"], kw["B"], kw["Hq"],
+                                  kw["Hkv"], kw["D"], kw["cap"], kw["ps"], kw["splits"], kw["out"],
+                                  None) == code
