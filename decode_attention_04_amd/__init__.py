@@ -44,7 +44,7 @@ class Plan(ctypes.Structure):
                 ("max_pieces", ctypes.c_int), ("slots", ctypes.c_int64),
                 ("fused", ctypes.c_int), ("fold_group", ctypes.c_int),
                 ("fold_groups", ctypes.c_int), ("pv_mode", ctypes.c_int),
-                ("double_buffer", ctypes.c_int),
+                ("double_buffer", ctypes.c_int), ("streaming", ctypes.c_int),
                 ("workspace_bytes", ctypes.c_size_t)]
 
     def as_dict(self) -> dict:

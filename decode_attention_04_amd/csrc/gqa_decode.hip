@@ -139,7 +139,12 @@ struct Tile {
 constexpr int kLoadK = 1;
 constexpr int kLoadV = 2;
 
-template <int D, int NB>
+// Cache policy of the K/V loads: 0 = default, kNonTemporal = the "nt" bit
+// (streamed data that is not re-read; on gfx950 it lets large caches stream
+// at a markedly higher rate).
+constexpr int kNonTemporal = 2;
+
+template <int D, int NB, int CPOL>
 __device__ __forceinline__ void load_tile(Tile<D, NB> &t, __amdgpu_buffer_rsrc_t rk,
                                           __amdgpu_buffer_rsrc_t rv, int row0, int r, int grp,
                                           int parts) {
@@ -150,7 +155,7 @@ __device__ __forceinline__ void load_tile(Tile<D, NB> &t, __amdgpu_buffer_rsrc_t
 #pragma unroll
         for (int kb = 0; kb < S::KB && (parts & kLoadK); ++kb) {
             const int off = (krow * D + 32 * kb + 8 * grp) * 2;
-            t.k[blk][kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+            t.k[blk][kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, CPOL));
         }
 #pragma unroll
         for (int j = 0; j < 4 && (parts & kLoadV); ++j) {
@@ -159,13 +164,13 @@ __device__ __forceinline__ void load_tile(Tile<D, NB> &t, __amdgpu_buffer_rsrc_t
             for (int c = 0; c < S::VC; ++c) {
                 const int off = (vrow * D + 16 * S::DPL * c + S::DPL * r) * 2;
                 if constexpr (S::VW == 4) {
-                    u32x4_t x = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+                    u32x4_t x = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, CPOL));
                     t.v[blk][j][c][0] = x[0];
                     t.v[blk][j][c][1] = x[1];
                     t.v[blk][j][c][2] = x[2];
                     t.v[blk][j][c][3] = x[3];
                 } else {
-                    u32x2_t x = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0));
+                    u32x2_t x = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, CPOL));
                     t.v[blk][j][c][0] = x[0];
                     t.v[blk][j][c][1] = x[1];
                 }
@@ -519,7 +524,7 @@ __device__ __forceinline__ long long share_of(long long x, long long N, long lon
 // through LDS into partial slot `slot` (or straight into `out` when direct).
 // Must be called by all threads of the workgroup; ends with a barrier, after
 // which LDS may be reused.
-template <int D, int NB, bool PAGED, int PV, bool DBUF>
+template <int D, int NB, bool PAGED, int PV, bool DBUF, int CPOL>
 __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB> &lds, int b, int kvh,
                                               int len, int t_begin, int t_end, size_t slot, bool direct) {
     using S = Shape<D>;
@@ -575,12 +580,12 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
             const size_t base = ((size_t)page * a.Hkv + kvh) * (size_t)a.page_size * slab;
             __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, rows * D * 2, kRsrcWord3);
             __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, rows * D * 2, kRsrcWord3);
-            load_tile<D, NB>(tile, rk, rv, row0, r, grp, parts);
+            load_tile<D, NB, CPOL>(tile, rk, rv, row0, r, grp, parts);
         } else {
             const size_t base = ((size_t)b * a.Hkv + kvh) * (size_t)a.S_max * slab;
             __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, len * D * 2, kRsrcWord3);
             __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, len * D * 2, kRsrcWord3);
-            load_tile<D, NB>(tile, rk, rv, t0, r, grp, parts);
+            load_tile<D, NB, CPOL>(tile, rk, rv, t0, r, grp, parts);
         }
     };
     auto tile_start = [&](int it) { return t_begin + (wave + kWaves * it) * TT; };
@@ -687,7 +692,7 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
     __syncthreads();
 }
 
-template <int D, int NB, bool PAGED, int PV, bool DBUF, int PART>
+template <int D, int NB, bool PAGED, int PV, bool DBUF, int PART, int CPOL>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEu<D, DBUF>)))
 void gqa_split_kernel(const SplitArgs a) {
     constexpr int TT = 16 * NB;
@@ -699,12 +704,31 @@ void gqa_split_kernel(const SplitArgs a) {
         // This workgroup's equal share of all tiles, walked piece by piece.
         const int lane = threadIdx.x & 63;
         const long long P = gridDim.x;
-        SegmentLocation loc = locate_tile(a.seq_lens, a.B, a.Hkv, cap, TT, -1, lane);  // the total only
-        const long long N = loc.total;
-        long long cur = share_begin(blockIdx.x, N, P);
-        const long long end = share_begin(blockIdx.x + 1, N, P);
-        if (cur >= end) return;
-        loc = locate_tile(a.seq_lens, a.B, a.Hkv, cap, TT, cur, lane);
+        SegmentLocation loc;
+        long long cur, end;
+        if (a.B <= 64) {
+            // one load of the lengths: the total, then this share's start
+            const int ln = lane < a.B ? clamp_len(a.seq_lens, lane, cap) : 0;
+            const int n = (ln + TT - 1) / TT;
+            const int incl = wave_scan(n, lane);
+            const long long N = uniform64((long long)__shfl(incl, 63, 64) * a.Hkv);
+            cur = share_begin(blockIdx.x, N, P);
+            end = share_begin(blockIdx.x + 1, N, P);
+            if (cur >= end) return;
+            const unsigned long long hit =
+                __ballot(lane < a.B && (long long)(incl - n) * a.Hkv <= cur && cur < (long long)incl * a.Hkv);
+            const int l = __builtin_ctzll(hit);
+            loc.total = N;
+            loc.b = __builtin_amdgcn_readfirstlane(l);
+            loc.len = __builtin_amdgcn_readfirstlane(__shfl(ln, l, 64));
+            loc.before = uniform64((long long)__shfl(incl - n, l, 64) * a.Hkv);
+        } else {
+            loc = locate_tile(a.seq_lens, a.B, a.Hkv, cap, TT, -1, lane);  // the total only
+            cur = share_begin(blockIdx.x, loc.total, P);
+            end = share_begin(blockIdx.x + 1, loc.total, P);
+            if (cur >= end) return;
+            loc = locate_tile(a.seq_lens, a.B, a.Hkv, cap, TT, cur, lane);
+        }
         int b = loc.b;
         int len = loc.len;
         int nb_tiles = (len + TT - 1) / TT;
@@ -714,7 +738,7 @@ void gqa_split_kernel(const SplitArgs a) {
         while (cur < end) {
             const int take = (int)min((long long)(nb_tiles - off), end - cur);
             const size_t slot = (size_t)blockIdx.x + (size_t)b * a.Hkv + kvh;
-            process_range<D, NB, PAGED, PV, DBUF>(a, lds, b, kvh, len, off * TT, min(len, (off + take) * TT),
+            process_range<D, NB, PAGED, PV, DBUF, CPOL>(a, lds, b, kvh, len, off * TT, min(len, (off + take) * TT),
                                                   slot, false);
             cur += take;
             off += take;
@@ -743,7 +767,7 @@ void gqa_split_kernel(const SplitArgs a) {
         const int t_end = min(len, t_begin + a.split_tokens);
         const int nsplit = a.num_splits;
         const bool direct = nsplit == 1;
-        process_range<D, NB, PAGED, PV, DBUF>(a, lds, b, kvh, len, t_begin, t_end,
+        process_range<D, NB, PAGED, PV, DBUF, CPOL>(a, lds, b, kvh, len, t_begin, t_end,
                                               (size_t)bk * nsplit + split, direct);
         if (direct || !a.fused) return;
 
@@ -1021,15 +1045,19 @@ hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, hipStream
     } else {
         const dim3 grid((unsigned)plan.grid), block(64 * kWaves);
         const bool even = plan.partition == kPartitionEven;
+        const bool nt = plan.streaming != 0;
         if (plan.pv_mode == kPvF32) {
-            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionEven>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionFixed>), grid, block, 0, stream, a);
+            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionEven, 0>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionFixed, 0>), grid, block, 0, stream, a);
         } else if (plan.double_buffer) {
-            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionEven>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionFixed>), grid, block, 0, stream, a);
+            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionEven, 0>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionFixed, 0>), grid, block, 0, stream, a);
+        } else if (nt) {
+            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, kNonTemporal>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, kNonTemporal>), grid, block, 0, stream, a);
         } else {
-            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed>), grid, block, 0, stream, a);
+            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, 0>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, 0>), grid, block, 0, stream, a);
         }
         return hipGetLastError();
     }
@@ -1129,6 +1157,13 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
     plan->waves = kWaves;
     plan->pv_mode = env_pv_mode();
     plan->double_buffer = dbuf;
+    // Non-temporal K/V loads: every KV byte is read once per call, and in a
+    // decode step the caches of all layers together far exceed the 256 MB
+    // Infinity Cache, so they stream from HBM (measured faster at every
+    // workload size when the inputs are not cache-resident).
+    // GQA_DECODE_NT=0 selects the default policy for A/B runs.
+    const char *nt_env = getenv("GQA_DECODE_NT");
+    plan->streaming = (nt_env != nullptr && strcmp(nt_env, "0") == 0) ? 0 : 1;
     plan->fold_group = 0;
     plan->fold_groups = 0;
     plan->fused = 0;
@@ -1155,13 +1190,15 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
         return GQA_OK;
     }
 
-    // Fixed splits: enough workgroups to give every CU two of them, and no
-    // split longer than kMaxSplitTokens keys, but at least one tile per wave;
-    // a short segment (<= 4 tiles per wave) gets a single split.
+    // Fixed splits: enough workgroups to give every CU one of them (measured
+    // best for one long sequence: fewer partials to fold, no loss in the
+    // stream), and no split longer than kMaxSplitTokens keys, but at least
+    // one tile per wave; a short segment (<= 4 tiles per wave) gets a single
+    // split.
     const int kMaxSplitTokens = env_int("GQA_DECODE_SPLIT_KEYS", 2048);
     int S = num_splits;
     if (S == 0) {
-        const int fill = (2 * cu_count + base - 1) / base;
+        const int fill = (cu_count + base - 1) / base;
         const int len_cap = (max_seq_len + kMaxSplitTokens - 1) / kMaxSplitTokens;
         S = fill > len_cap ? fill : len_cap;
         const int most = (tiles_total + kWaves - 1) / kWaves;

@@ -76,6 +76,7 @@ typedef struct gqa_plan {
     int fold_groups;        /* first-level groups (1 = a single fold level) */
     int pv_mode;            /* PV contraction: 1 = bf16 MFMA with P split hi+lo, 0 = fp32 MFMA */
     int double_buffer;      /* 1: two tile buffers per wave; 0: one (more waves per SIMD) */
+    int streaming;          /* 1: K/V loads carry the non-temporal hint (large caches) */
     size_t workspace_bytes; /* scratch the call needs (0 when direct) */
 } gqa_plan_t;
 

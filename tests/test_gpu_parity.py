@@ -311,3 +311,17 @@ def test_fixed_and_even_agree_with_oracle(monkeypatch):
     fixed = dc.run_host()
     compare(even, ref, "even")
     compare(fixed, ref, "fixed")
+
+
+@pytest.mark.parametrize("nt", ["0", "1"])
+def test_cache_policy_variants(monkeypatch, nt):
+    """Both K/V load cache policies give the same bits (only the hint differs)."""
+    say(f"[parity] GQA_DECODE_NT={nt}")
+    case = W.contig_case(2, 16, 2, 128, 3000, seq_lens=[3000, 1234], seed=70, tail="nan")
+    dc = DeviceCase(case)
+    base = dc.run_host()
+    monkeypatch.setenv("GQA_DECODE_NT", nt)
+    assert gd.gqa_decode_plan(2, 16, 2, 128, 3000).streaming == int(nt)  # default: 1
+    out = dc.run_host()
+    assert np.array_equal(out.view(np.uint32), base.view(np.uint32))
+    compare(out, oracle_out(case), f"nt={nt}")

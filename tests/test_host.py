@@ -88,6 +88,7 @@ def test_plan_invariants(shape, cu):
     assert p.fused == 0   # the in-kernel fold is opt-in (GQA_DECODE_FUSED=1)
     assert p.pv_mode == 1  # bf16 MFMA PV unless GQA_DECODE_PV=f32
     assert p.double_buffer == 0
+    assert p.streaming == 1
     assert p.workspace_bytes == expected_workspace(B, Hq, Hkv, D, p)
     again = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, 0, cu)
     assert again.as_dict() == p.as_dict()
@@ -107,9 +108,9 @@ def test_fixed_plan_invariants(monkeypatch, shape):
 
 
 def test_plan_fills_the_device():
-    # one kv head, 131072 keys: two workgroups per CU share the keys (one sequence: fixed splits)
+    # one kv head, 131072 keys: one workgroup per CU (one sequence: fixed splits)
     p = gd.gqa_decode_plan(1, 8, 1, 128, 131072, 0, 0, 256)
-    assert p.partition == 0 and p.grid == 512
+    assert p.partition == 0 and p.grid == 256
     # a batch gets even shares
     p = gd.gqa_decode_plan(32, 32, 8, 128, 8192, 32, 0, 256)
     assert p.partition == 1 and p.grid == 512
