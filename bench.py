@@ -181,7 +181,7 @@ def main():
                               args.splits, torch.cuda.get_device_properties(0).multi_processor_count)
     need = gd.gqa_decode_workspace_bytes(case.B, case.Hq, case.Hkv, case.D, cap, case.page_size,
                                          args.splits)
-    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
     outs = [torch.empty((case.B, case.Hq, case.D), dtype=torch.float32, device="cuda")
             for _ in range(R)]
     def full(i, stream):
@@ -245,7 +245,7 @@ def main():
     # The dominant kernel alone (the split-KV partial kernel; K launches in one graph), and the
     # combine alone, each on the stream they are launched on.
     split_ms = graph_time(split_only, args.steps)
-    combine_ms = graph_time(combine_only, args.steps) if not (plan.direct or plan.fused) else 0.0
+    combine_ms = graph_time(combine_only, args.steps) if not plan.direct else 0.0
     split_gbs = algo_bytes / (split_ms * 1e-3) / 1e9
 
     cpu = None

@@ -42,8 +42,7 @@ class Plan(ctypes.Structure):
                 ("split_tokens", ctypes.c_int), ("tile_tokens", ctypes.c_int),
                 ("waves", ctypes.c_int), ("grid", ctypes.c_int), ("direct", ctypes.c_int),
                 ("max_pieces", ctypes.c_int), ("slots", ctypes.c_int64),
-                ("fused", ctypes.c_int), ("fold_group", ctypes.c_int),
-                ("fold_groups", ctypes.c_int), ("pv_mode", ctypes.c_int),
+                ("pv_mode", ctypes.c_int),
                 ("double_buffer", ctypes.c_int), ("streaming", ctypes.c_int),
                 ("workspace_bytes", ctypes.c_size_t)]
 
@@ -142,8 +141,7 @@ def _workspace(workspace, need, device):
     if need == 0:
         return None, 0
     if workspace is None:
-        # zero-filled: the library's arrival counters start at zero
-        workspace = torch.zeros(need, dtype=torch.uint8, device=device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
     return workspace, workspace.numel() * workspace.element_size()
 
 

@@ -67,10 +67,8 @@ constexpr int kPartitionEven = 1;
 constexpr int kMaxHeadsPerKv = 16;  // G is padded to the MFMA's 16 columns
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords (gfx9 family)
 
-// Partials of one (sequence, kv head) are blocks of [G][D] (acc) and [G][2]
-// (m in log2 units, l): the split partials at part_acc/part_ml, indexed
-// [b*Hkv + kvh][split], and the group partials of the two-level fold at
-// grp_acc/grp_ml, indexed [b*Hkv + kvh][group].
+// Partials are blocks of [G][D] (acc) and [G][2] (m in log2 units, l), one
+// per slot (see "work partition" below for the slot numbering).
 struct SplitArgs {
     const uint16_t *q;
     const uint16_t *k;
@@ -79,17 +77,12 @@ struct SplitArgs {
     const int32_t *page_table;  // paged only
     float *part_acc;
     float *part_ml;
-    float *grp_acc;
-    float *grp_ml;
-    unsigned int *counters;     // [B*Hkv][fold_groups + 1], zero between calls
     float *out;                 // [B][Hq][D]
     int B, Hq, Hkv, G;
     int S_max;                  // contiguous capacity
     int page_size, max_pages;   // paged
     int num_pages;              // paged
     int num_splits, split_tokens;
-    int fused;                  // 1: the last workgroups fold the partials in this kernel
-    int fold_group, fold_groups;
     float qk_scale_log2;        // scale * log2(e)
 };
 
@@ -107,8 +100,39 @@ struct CombineArgs {
 __device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ float xor_max(float x, int mask) {
-    return fmaxf(x, __shfl_xor(x, mask, 64));
+// Cross-row exchanges (gfx950 VALU lane swaps, no LDS round trip).
+// rows16: for a lane in rows (2k, 2k+1) of 16 lanes, x in row 2k and in row
+// 2k+1 at the same position; halves32: x in the lower and the upper half of
+// the wave at the same position.  Both lanes of a pair get the same two values.
+struct LanePair {
+    float lo, hi;
+};
+__device__ __forceinline__ LanePair rows16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return {__uint_as_float(p[0]), __uint_as_float(p[1])};
+}
+__device__ __forceinline__ LanePair halves32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return {__uint_as_float(p[0]), __uint_as_float(p[1])};
+}
+// Max and sum over the four lanes r, r+16, r+32, r+48 (the result in all four).
+__device__ __forceinline__ float max_rows(float x) {
+    LanePair p = rows16(x);
+    p = halves32(fmaxf(p.lo, p.hi));
+    return fmaxf(p.lo, p.hi);
+}
+__device__ __forceinline__ float sum_rows(float x) {
+    LanePair p = rows16(x);
+    p = halves32(p.lo + p.hi);
+    return p.lo + p.hi;
+}
+// x of lane (i - n) mod 16 in this lane's row of 16.
+__device__ __forceinline__ float row_ror(float x, int n) {
+    switch (n) {
+        case 4: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+        case 8: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+        default: return x;
+    }
 }
 
 // Element e (0..2*N-1) of a vector of N dwords holding 2*N bf16 values.
@@ -252,8 +276,7 @@ __device__ __forceinline__ void qk_softmax(const Tile<D, NB> &t, const bf16x8_t 
             mx = fmaxf(mx, x);
         }
     }
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32);
+    mx = max_rows(mx);
     // The tile holds at least one unmasked key, so m_new is finite.
     const float m_new = fmaxf(st.m, mx);
     const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 on the first tile
@@ -343,65 +366,20 @@ struct FoldLds {
     static constexpr int kRegion = kFoldBytes > kStageBytes ? kFoldBytes : kStageBytes;
     float m[kWaves][kMaxHeadsPerKv];
     float l[kWaves][kMaxHeadsPerKv];
-    int last;
     alignas(16) unsigned char region[kWaves][kRegion];
     __device__ float *acc(int w) { return reinterpret_cast<float *>(region[w]); }
     __device__ unsigned short *stage(int w) { return reinterpret_cast<unsigned short *>(region[w]); }
 };
 
-// Fold n partial blocks ([G][D] acc, [G][2] ml, block i at acc + i*G*D and
-// ml + i*G*2) with the log-sum-exp rescale, blocks in ascending order.  The
-// result goes to out rows out[g*D ..] normalised (final) or, if out is null,
-// to the partial block dst_acc / dst_ml.  All threads of the workgroup take
-// part; each owns 4 consecutive dims of one head.
-template <int D>
-__device__ __forceinline__ void fold_blocks(const float *acc, const float *ml, int n, int G,
-                                            float *dst_acc, float *dst_ml, float *out) {
-    for (int col = threadIdx.x; col < G * (D / 4); col += 64 * kWaves) {
-        const int g = col / (D / 4);
-        const int d = 4 * (col - g * (D / 4));
-        float M = -INFINITY;
-        for (int i = 0; i < n; ++i) M = fmaxf(M, ml[(i * G + g) * 2]);
-        f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-        float L = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll 8
-            for (int i = 0; i < n; ++i) {
-                const float w = __builtin_amdgcn_exp2f(ml[(i * G + g) * 2] - M);
-                L += w * ml[(i * G + g) * 2 + 1];
-                sum += w * *reinterpret_cast<const f32x4_t *>(acc + ((size_t)i * G + g) * D + d);
-            }
-        }
-        if (out != nullptr) {
-            *reinterpret_cast<f32x4_t *>(out + (size_t)g * D + d) =
-                L > 0.f ? sum / L : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        } else {
-            *reinterpret_cast<f32x4_t *>(dst_acc + (size_t)g * D + d) = sum;
-            if (d == 0) {
-                dst_ml[g * 2] = M;
-                dst_ml[g * 2 + 1] = L;
-            }
-        }
-    }
-}
-
-// Cross-workgroup arrival: returns true (in every thread) for the last of
-// `expected` workgroups to reach `counter`, after making this workgroup's
-// stores visible and, for the last one, acquiring everyone else's.  The last
-// arrival resets the counter to zero for the next call.
-template <class Lds>
-__device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int expected, Lds &lds) {
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned int t = atomicAdd(counter, 1u);
-        lds.last = t + 1 == expected;
-        if (t + 1 == expected) *counter = 0u;
-    }
-    __syncthreads();
-    const bool last = lds.last;
-    if (last) __threadfence();
-    return last;
+// Folds partial (m2, l2, o2) into the running (m, l, o) with the log-sum-exp rescale.
+__device__ __forceinline__ void lse_merge(float &m, float &l, f32x4_t &o, float m2, float l2, f32x4_t o2) {
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;
+    const float wa = __builtin_amdgcn_exp2f(m - mn);
+    const float wb = __builtin_amdgcn_exp2f(m2 - mn);
+    l = l * wa + l2 * wb;
+    o = o * wa + o2 * wb;
+    m = mn;
 }
 
 // Minimum waves per SIMD the compiler must leave room for: the single-buffer
@@ -627,9 +605,7 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
     }
 
     // This wave's sum for head r: the four lanes r, r+16, r+32, r+48.
-    float lsum = st.l;
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+    const float lsum = sum_rows(st.l);
 
     // Publish the wave's state into its own region; rows g >= G are never read.
     if (r < a.G) {
@@ -698,7 +674,6 @@ void gqa_split_kernel(const SplitArgs a) {
     constexpr int TT = 16 * NB;
     __shared__ FoldLds<D, NB> lds;
     const int cap = PAGED ? a.max_pages * a.page_size : a.S_max;
-    const int G = a.G;
 
     if constexpr (PART == kPartitionEven) {
         // This workgroup's equal share of all tiles, walked piece by piece.
@@ -769,54 +744,60 @@ void gqa_split_kernel(const SplitArgs a) {
         const bool direct = nsplit == 1;
         process_range<D, NB, PAGED, PV, DBUF, CPOL>(a, lds, b, kvh, len, t_begin, t_end,
                                               (size_t)bk * nsplit + split, direct);
-        if (direct || !a.fused) return;
-
-        // Two-level fold across workgroups: the last split to finish in each group
-        // of fold_group splits folds that group; the last group to finish folds the
-        // groups into the output (one level when there is a single group).
-        float *out_rows = a.out + ((size_t)b * a.Hq + (size_t)kvh * G) * D;
-        const int ngroups = a.fold_groups;
-        const int grp_id = split / a.fold_group;
-        const int g0 = grp_id * a.fold_group;
-        const int gn = min(a.fold_group, nsplit - g0);
-        unsigned int *ctr = a.counters + (size_t)bk * (ngroups + 1);
-        if (!arrive_last(ctr + grp_id, (unsigned)gn, lds)) return;
-        const float *src_acc = a.part_acc + ((size_t)bk * nsplit + g0) * G * D;
-        const float *src_ml = a.part_ml + ((size_t)bk * nsplit + g0) * G * 2;
-        if (ngroups == 1) {
-            fold_blocks<D>(src_acc, src_ml, gn, G, nullptr, nullptr, out_rows);
-            return;
-        }
-        fold_blocks<D>(src_acc, src_ml, gn, G, a.grp_acc + ((size_t)bk * ngroups + grp_id) * G * D,
-                       a.grp_ml + ((size_t)bk * ngroups + grp_id) * G * 2, nullptr);
-        if (!arrive_last(ctr + ngroups, (unsigned)ngroups, lds)) return;
-        fold_blocks<D>(a.grp_acc + (size_t)bk * ngroups * G * D, a.grp_ml + (size_t)bk * ngroups * G * 2,
-                       ngroups, G, nullptr, nullptr, out_rows);
     }
 }
 
 // Combine: one workgroup of 256 threads per (b, h, chunk of 4*NCOL dims).
-// Thread (sg, c) owns dims 4c .. 4c+3 of the chunk and the splits s with
-// s % NSG == sg (NSG = 256 / NCOL).  It issues the loads of up to U of its
-// splits before using any, folds them in ascending s with a running max, and
-// the NSG groups are then folded pairwise through LDS (a fixed tree): the
-// summation order is fixed, so the result is bit-reproducible.
+// Thread (sg, c), c = tid % NCOL, owns dims 4c .. 4c+3 of the chunk and the
+// pieces s with s % NSG == sg (NSG = 256 / NCOL).  It loads U of its pieces
+// at a time and folds each round into its running (m, l, o) against the
+// round's maximum (independent exponentials, not a chain of merges).  The
+// NSG folds of a column are then merged with the log-sum-exp rescale in a
+// fixed tree: inside each wave over the lanes that share c (row rotations,
+// then the row-pair and half-wave swaps), then the four waves in order
+// through LDS.  Every step has a fixed order, so the result is
+// bit-reproducible.
 constexpr int kCombineThreads = 256;
 
-__device__ __forceinline__ void lse_merge(float &m, float &l, f32x4_t &o, float m2, float l2, f32x4_t o2) {
-    const float mn = fmaxf(m, m2);
-    if (mn == -INFINITY) return;
-    const float wa = __builtin_amdgcn_exp2f(m - mn);
-    const float wb = __builtin_amdgcn_exp2f(m2 - mn);
-    l = l * wa + l2 * wb;
-    o = o * wa + o2 * wb;
-    m = mn;
+struct Fold {
+    float m, l;
+    f32x4_t o;
+};
+
+__device__ __forceinline__ void merge_into(Fold &x, const Fold &y) { lse_merge(x.m, x.l, x.o, y.m, y.l, y.o); }
+
+// Merges the fold of lane (i - n) mod 16 of the row into this lane's.
+__device__ __forceinline__ void merge_ror(Fold &x, int n) {
+    Fold y;
+    y.m = row_ror(x.m, n);
+    y.l = row_ror(x.l, n);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y.o[i] = row_ror(x.o[i], n);
+    merge_into(x, y);
+}
+
+// Merges the folds of the two rows of a row pair (16-lane rows 2k, 2k+1), or
+// of the two halves of the wave: both lanes of a pair compute the same value.
+template <bool HALVES>
+__device__ __forceinline__ void merge_swap(Fold &x) {
+    auto pair = [](float v) { return HALVES ? halves32(v) : rows16(v); };
+    const LanePair m = pair(x.m), l = pair(x.l);
+    Fold lo{m.lo, l.lo, {}}, hi{m.hi, l.hi, {}};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const LanePair o = pair(x.o[i]);
+        lo.o[i] = o.lo;
+        hi.o[i] = o.hi;
+    }
+    merge_into(lo, hi);
+    x = lo;
 }
 
 template <int NCOL>
 __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const CombineArgs a) {
+    static_assert(NCOL == 4 || NCOL == 8 || NCOL == 16, "lanes of one column must share rows of 16");
     constexpr int NSG = kCombineThreads / NCOL;
-    constexpr int U = 4;  // splits per thread per round of loads
+    constexpr int U = 4;  // pieces per thread per round of loads
     const int D = a.D;
     const int chunks = D / (4 * NCOL);
     const size_t bh = blockIdx.x / chunks;
@@ -859,8 +840,7 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const Comb
     const float *acc = a.part_acc + (lo * G + g) * D + d0 + 4 * c;
     const size_t ml_stride = (size_t)G * 2, acc_stride = (size_t)G * D;
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4_t o_run = {0.f, 0.f, 0.f, 0.f};
+    Fold run{-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}};
     for (int s0 = sg; s0 < S; s0 += U * NSG) {
         float mv[U], lv[U];
         f32x4_t av[U];
@@ -878,31 +858,55 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const Comb
                 av[u] = *reinterpret_cast<const f32x4_t *>(acc + s * acc_stride);
             }
         }
+        float mr = run.m;
 #pragma unroll
-        for (int u = 0; u < U; ++u) lse_merge(m_run, l_run, o_run, mv[u], lv[u], av[u]);
+        for (int u = 0; u < U; ++u) mr = fmaxf(mr, mv[u]);
+        if (mr != -INFINITY) {
+            const float wr = __builtin_amdgcn_exp2f(run.m - mr);
+            run.l *= wr;
+            run.o *= wr;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float w = __builtin_amdgcn_exp2f(mv[u] - mr);
+                run.l += w * lv[u];
+                run.o += w * av[u];
+            }
+            run.m = mr;
+        }
     }
 
-    // Pairwise fold of the NSG split groups: at each step group i absorbs
-    // group i + w, for w = NSG/2, NSG/4, ..., 1.
-    __shared__ f32x4_t part[NSG][NCOL];
-    __shared__ float mpart[NSG][NCOL], lpart[NSG][NCOL];
-    part[sg][c] = o_run;
-    mpart[sg][c] = m_run;
-    lpart[sg][c] = l_run;
-    __syncthreads();
-#pragma unroll
-    for (int w = NSG / 2; w > 0; w /= 2) {
-        if (sg < w) {
-            lse_merge(m_run, l_run, o_run, mpart[sg + w][c], lpart[sg + w][c], part[sg + w][c]);
-            part[sg][c] = o_run;
-            mpart[sg][c] = m_run;
-            lpart[sg][c] = l_run;
-        }
-        __syncthreads();
+    // Lanes of one column inside a wave: c, c + NCOL, ... (64 / NCOL of them).
+    if constexpr (NCOL == 4) merge_ror(run, 4);
+    if constexpr (NCOL <= 8) merge_ror(run, 8);
+    merge_swap<false>(run);
+    merge_swap<true>(run);
+
+    // The four waves, in order (lane c of each wave holds its column c).
+    __shared__ float wm[kWaves][NCOL], wl[kWaves][NCOL];
+    __shared__ f32x4_t wo[kWaves][NCOL];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane < NCOL) {
+        wm[wave][lane] = run.m;
+        wl[wave][lane] = run.l;
+        wo[wave][lane] = run.o;
     }
-    if (sg == 0) {
+    __syncthreads();
+    if (threadIdx.x < NCOL) {
+        float M = wm[0][c];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w][c]);
+        float L = 0.f;
+        f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float wt = __builtin_amdgcn_exp2f(wm[w][c] - M);
+                L += wt * wl[w][c];
+                O += wt * wo[w][c];
+            }
+        }
         *reinterpret_cast<f32x4_t *>(a.out + bh * D + d0 + 4 * c) =
-            l_run > 0.f ? o_run / l_run : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            L > 0.f ? O / L : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 }
 
@@ -951,49 +955,21 @@ gqa_status_t device_cu_count(int *out) {
 }
 
 struct WorkspaceLayout {
-    size_t part_acc, part_ml, grp_acc, grp_ml, counters, total;
+    size_t part_acc, part_ml, total;
 };
 
-// The arrival counters of the fused fold live in a fixed area at the start of
-// every workspace that no other region ever overlaps, so a zero-filled
-// workspace stays valid across calls with different shapes: each call leaves
-// the counters it used at zero.
-constexpr size_t kCounterBytes = 65536;
-constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(unsigned int));
-
-// Byte offsets of the workspace regions (all 256-byte aligned).
 // `slots` partial blocks of G heads: B*Hkv*S for fixed splits, P + B*Hkv for
 // even shares.
-WorkspaceLayout workspace_layout(int B, int Hq, int Hkv, int D, int64_t slots, int fused, int groups) {
+WorkspaceLayout workspace_layout(int Hq, int Hkv, int D, int64_t slots) {
     WorkspaceLayout w{};
-    const size_t rows = (size_t)B * Hq;
     const size_t G = (size_t)(Hq / Hkv);
     size_t off = 0;
-    w.counters = 0;
-    if (fused) off += kCounterBytes;
     w.part_acc = off;
     off += align_up((size_t)slots * G * D * sizeof(float), 256);
     w.part_ml = off;
     off += align_up((size_t)slots * G * 2 * sizeof(float), 256);
-    w.grp_acc = off;
-    w.grp_ml = off;
-    if (fused && groups > 1) {
-        off += align_up(rows * groups * D * sizeof(float), 256);
-        w.grp_ml = off;
-        off += align_up(rows * groups * 2 * sizeof(float), 256);
-    }
     w.total = off;
     return w;
-}
-
-// The in-kernel fold is off unless GQA_DECODE_FUSED=1: on gfx950 each
-// workgroup's device-scope release/acquire is an L2 writeback/invalidate of
-// its XCD, costing microseconds that serialise per XCD, which is far more
-// than the separate combine launch it saves.
-int env_fused() {
-    const char *s = getenv("GQA_DECODE_FUSED");
-    if (s == nullptr || *s == '\0') return 0;
-    return atoi(s) != 0 ? 1 : 0;
 }
 
 // Tile buffering: one register tile per wave refilled early (the default;
@@ -1024,17 +1000,20 @@ hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const f
                           hipStream_t stream) {
     CombineArgs ca{part_acc, part_ml, out, seq_lens, D, Hq / Hkv, Hq, plan.num_splits,
                    plan.partition, B, Hkv, cap, plan.tile_tokens, plan.grid};
-    // Narrow dim chunks (more workgroups, fewer splits per thread) when there
-    // are few heads and many partials per head.
+    // The widest dim chunk (NCOL = 16, 8 or 4 columns of 4 dims) that still
+    // gives at least 128 workgroups: narrower chunks put more threads on the
+    // pieces of a column (measured best for few heads with many pieces).
+    // GQA_DECODE_COMBINE_COLS = 4, 8 or 16 overrides it.
     const int64_t heads = (int64_t)B * Hq;
-    const int pieces = plan.max_pieces;
-    if (heads * (D / 64) >= 256 || pieces <= 64) {
-        hipLaunchKernelGGL(gqa_combine_kernel<16>, dim3((unsigned)(heads * (D / 64))), dim3(kCombineThreads), 0, stream, ca);
-    } else if (heads * (D / 32) >= 256 || pieces <= 256) {
-        hipLaunchKernelGGL(gqa_combine_kernel<8>, dim3((unsigned)(heads * (D / 32))), dim3(kCombineThreads), 0, stream, ca);
-    } else {
-        hipLaunchKernelGGL(gqa_combine_kernel<4>, dim3((unsigned)(heads * (D / 16))), dim3(kCombineThreads), 0, stream, ca);
+    int ncol = env_int("GQA_DECODE_COMBINE_COLS", 0);
+    if (ncol != 4 && ncol != 8 && ncol != 16) {
+        ncol = 16;
+        while (ncol > 4 && heads * (D / (4 * ncol)) < 128) ncol /= 2;
     }
+    const unsigned grid = (unsigned)(heads * (D / (4 * ncol)));
+    if (ncol == 16) hipLaunchKernelGGL(gqa_combine_kernel<16>, dim3(grid), dim3(kCombineThreads), 0, stream, ca);
+    else if (ncol == 8) hipLaunchKernelGGL(gqa_combine_kernel<8>, dim3(grid), dim3(kCombineThreads), 0, stream, ca);
+    else hipLaunchKernelGGL(gqa_combine_kernel<4>, dim3(grid), dim3(kCombineThreads), 0, stream, ca);
     return hipGetLastError();
 }
 
@@ -1044,6 +1023,7 @@ hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, hipStream
         return hipErrorInvalidValue;
     } else {
         const dim3 grid((unsigned)plan.grid), block(64 * kWaves);
+
         const bool even = plan.partition == kPartitionEven;
         const bool nt = plan.streaming != 0;
         if (plan.pv_mode == kPvF32) {
@@ -1079,17 +1059,10 @@ constexpr int kPhaseCombine = 2;
 gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, void *workspace,
                  hipStream_t stream, int phases) {
     if (!plan.direct) {
-        WorkspaceLayout w = workspace_layout(a.B, a.Hq, a.Hkv, D, plan.slots, plan.fused,
-                                             plan.fold_groups);
+        WorkspaceLayout w = workspace_layout(a.Hq, a.Hkv, D, plan.slots);
         char *base = static_cast<char *>(workspace);
         a.part_acc = reinterpret_cast<float *>(base + w.part_acc);
         a.part_ml = reinterpret_cast<float *>(base + w.part_ml);
-        a.grp_acc = reinterpret_cast<float *>(base + w.grp_acc);
-        a.grp_ml = reinterpret_cast<float *>(base + w.grp_ml);
-        a.counters = reinterpret_cast<unsigned int *>(base + w.counters);
-        a.fused = plan.fused;
-        a.fold_group = plan.fold_group;
-        a.fold_groups = plan.fold_groups;
     }
     hipError_t e = hipSuccess;
     if (phases & kPhaseSplit) {
@@ -1101,7 +1074,7 @@ gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, void *
         }
         if (e != hipSuccess) return GQA_ERR_HIP;
     }
-    if (plan.direct || plan.fused || !(phases & kPhaseCombine)) return GQA_OK;
+    if (plan.direct || !(phases & kPhaseCombine)) return GQA_OK;
     const int cap = paged ? a.max_pages * a.page_size : a.S_max;
     e = launch_combine(plan, a.part_acc, a.part_ml, a.out, a.seq_lens, a.B, a.Hq, a.Hkv, D, cap, stream);
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
@@ -1153,6 +1126,7 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
     const int base = B > 0 ? B * Hkv : 1;
     const char *part_env = getenv("GQA_DECODE_PARTITION");
     const bool want_fixed = part_env != nullptr && strcmp(part_env, "fixed") == 0;
+    const bool want_even = part_env != nullptr && strcmp(part_env, "even") == 0;
     plan->tile_tokens = tt;
     plan->waves = kWaves;
     plan->pv_mode = env_pv_mode();
@@ -1164,18 +1138,15 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
     // GQA_DECODE_NT=0 selects the default policy for A/B runs.
     const char *nt_env = getenv("GQA_DECODE_NT");
     plan->streaming = (nt_env != nullptr && strcmp(nt_env, "0") == 0) ? 0 : 1;
-    plan->fold_group = 0;
-    plan->fold_groups = 0;
-    plan->fused = 0;
 
     // Even shares (the default for batches): about two workgroups per CU, each at least
     // one tile per wave at full length; a segment short enough for one
     // workgroup (<= 4 tiles per wave) is written directly instead.
     // A single sequence cannot be ragged: fixed splits give it the same work
     // split without the device-side length scan.
-    if (num_splits == 0 && !want_fixed && !env_fused() && tiles_total > 4 * kWaves && B > 1) {
+    if (num_splits == 0 && !want_fixed && tiles_total > 4 * kWaves && (B > 1 || want_even)) {
         const int64_t tiles_max = (int64_t)base * tiles_total;
-        int64_t P = env_int("GQA_DECODE_SHARES", 2 * cu_count);
+        int64_t P = env_int("GQA_DECODE_SHARES", B > 1 ? 2 * cu_count : cu_count);
         if (P > (tiles_max + kWaves - 1) / kWaves) P = (tiles_max + kWaves - 1) / kWaves;
         if (P < 1) P = 1;
         if (P > INT32_MAX / 2) return GQA_ERR_SHAPE;
@@ -1186,7 +1157,7 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
         plan->direct = 0;
         plan->slots = (int64_t)P + base;
         plan->max_pieces = (int)std::min<int64_t>(P, (int64_t)tiles_total * P / tiles_max + 1);
-        plan->workspace_bytes = workspace_layout(B, Hq, Hkv, D, plan->slots, 0, 0).total;
+        plan->workspace_bytes = workspace_layout(Hq, Hkv, D, plan->slots).total;
         return GQA_OK;
     }
 
@@ -1203,7 +1174,7 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
         S = fill > len_cap ? fill : len_cap;
         const int most = (tiles_total + kWaves - 1) / kWaves;
         if (S > most) S = most;
-        if (tiles_total <= 4 * kWaves && !env_fused()) S = 1;
+        if (tiles_total <= 4 * kWaves) S = 1;
     }
     if (S > tiles_total) S = tiles_total;
     if (S < 1) S = 1;
@@ -1219,21 +1190,8 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
     plan->direct = S == 1 ? 1 : 0;
     plan->slots = (int64_t)base * S;
     plan->max_pieces = S;
-    plan->fused = plan->direct ? 0 : env_fused();
-    // Fold groups: one level up to 8 splits, else about sqrt(S) splits per
-    // group and about sqrt(S) groups, so no workgroup folds many blocks.
-    int fg = S;
-    if (S > 8) {
-        fg = 1;
-        while (fg * fg < S) ++fg;
-    }
-    plan->fold_group = fg;
-    plan->fold_groups = (S + fg - 1) / fg;
-    if (plan->fused && (int64_t)B * Hkv * (plan->fold_groups + 1) > kMaxCounters)
-        plan->fused = 0;  // too many (sequence, kv head) pairs for the counter area
     plan->workspace_bytes = 0;
-    if (!plan->direct)
-        plan->workspace_bytes = workspace_layout(B, Hq, Hkv, D, plan->slots, plan->fused, plan->fold_groups).total;
+    if (!plan->direct) plan->workspace_bytes = workspace_layout(Hq, Hkv, D, plan->slots).total;
     return GQA_OK;
 }
 
@@ -1372,7 +1330,7 @@ gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, c
     gqa_plan_t plan;
     gqa_status_t s = plan_for_call(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, &plan);
     if (s != GQA_OK) return s;
-    if (plan.direct || plan.fused) return GQA_OK;  // the split kernel already wrote `out`
+    if (plan.direct) return GQA_OK;  // the split kernel already wrote `out`
     if (workspace == nullptr) return GQA_ERR_NULL;
     if (workspace_bytes < plan.workspace_bytes) return GQA_ERR_WORKSPACE;
     SplitArgs a{};

@@ -71,9 +71,6 @@ typedef struct gqa_plan {
     int direct;             /* 1: S == 1, the split kernel writes `out` itself */
     int max_pieces;         /* most partials one (sequence, kv head) can have */
     int64_t slots;          /* partial blocks in the workspace: B*Hkv*S, or shares + B*Hkv */
-    int fused;              /* 1: the split kernel also folds the partials (one launch) */
-    int fold_group;         /* splits folded together at the first fold level */
-    int fold_groups;        /* first-level groups (1 = a single fold level) */
     int pv_mode;            /* PV contraction: 1 = bf16 MFMA with P split hi+lo, 0 = fp32 MFMA */
     int double_buffer;      /* 1: two tile buffers per wave; 0: one (more waves per SIMD) */
     int streaming;          /* 1: K/V loads carry the non-temporal hint (large caches) */
@@ -112,10 +109,10 @@ size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int max_
  *   out      fp32 [B][Hq][head_dim]  (written)
  *   workspace: at least gqa_decode_workspace_bytes(B, Hq, Hkv, head_dim,
  *              S_max, 0, num_splits) bytes; may be NULL when that is 0.
- *              It must be zero-filled before its first use; every call
- *              leaves it in a state fit for the next call (its arrival
- *              counters back at zero), so calls that share one workspace
- *              must not overlap in time.
+ *              It needs no initialisation: it carries one call's partials
+ *              from the split kernel to the combine kernel, so calls that
+ *              share a workspace must not run concurrently (one stream
+ *              orders them).
  *   num_splits: 0 = heuristic, > 0 = forced.
  */
 gqa_status_t gqa_decode(const void *q, const void *k_cache, const void *v_cache,

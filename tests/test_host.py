@@ -25,20 +25,12 @@ def lib():
 
 
 def expected_workspace(B, Hq, Hkv, D, p):
-    """Partial blocks (slots) of G x (D + 2) floats, group partials [B*Hq*groups] x (D + 2)
-    floats when the fused fold has two levels, and a fixed 64 KiB counter area in front when
-    fused; every region rounded up to 256 bytes."""
+    """Partial blocks (slots) of G x (D + 2) floats, each region rounded up to 256 bytes."""
     if p.direct:
         return 0
     align = lambda x: (x + 255) // 256 * 256
     G = Hq // Hkv
-    total = align(p.slots * G * D * 4) + align(p.slots * G * 2 * 4)
-    if p.fused:
-        total += 65536  # fixed counter area at the front
-        if p.fold_groups > 1:
-            rows = B * Hq
-            total += align(rows * p.fold_groups * D * 4) + align(rows * p.fold_groups * 2 * 4)
-    return total
+    return align(p.slots * G * D * 4) + align(p.slots * G * 2 * 4)
 
 
 def declared_functions():
@@ -85,7 +77,6 @@ def test_plan_invariants(shape, cu):
         assert p.grid == B * Hkv * p.num_splits
         assert p.direct == (p.num_splits == 1)
         assert p.slots == B * Hkv * p.num_splits
-    assert p.fused == 0   # the in-kernel fold is opt-in (GQA_DECODE_FUSED=1)
     assert p.pv_mode == 1  # bf16 MFMA PV unless GQA_DECODE_PV=f32
     assert p.double_buffer == 0
     assert p.streaming == 1
@@ -210,23 +201,6 @@ def test_workspace_bytes_matches_plan_when_forced(lib):
                 gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, s, 256).workspace_bytes
     with pytest.raises(gd.GqaError):
         gd.gqa_decode_workspace_bytes(1, 8, 3, 128, 100, 0, 2)
-
-
-def test_fused_falls_back_when_counters_do_not_fit(monkeypatch):
-    monkeypatch.setenv("GQA_DECODE_FUSED", "1")
-    p = gd.gqa_decode_plan(4096, 32, 8, 128, 8192, 0, 4, 256)
-    assert p.fold_groups == 1 and p.fused == 0          # 4096*8*2 counters > 16384
-    p = gd.gqa_decode_plan(64, 32, 8, 128, 8192, 0, 4, 256)
-    assert p.fused == 1
-
-
-def test_fused_plan_workspace(monkeypatch):
-    monkeypatch.setenv("GQA_DECODE_FUSED", "1")
-    for shape in WORKLOAD_SHAPES[1:]:
-        B, Hq, Hkv, D, cap, ps = shape
-        p = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, 0, 256)
-        assert p.fused == 1 and p.partition == 0
-        assert p.workspace_bytes == expected_workspace(B, Hq, Hkv, D, p)
 
 
 @pytest.mark.parametrize("args,code", [
