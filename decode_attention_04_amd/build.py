@@ -16,6 +16,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the kernels' leading scalar arguments are preloaded into SGPRs at launch
+    "-mllvm", "-amdgpu-kernarg-preload-count=7",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

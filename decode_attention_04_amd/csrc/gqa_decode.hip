@@ -92,7 +92,6 @@ struct CombineArgs {
     float *out;
     const int32_t *seq_lens;  // even partition only
     int D, G, Hq, num_splits;
-    int partition;            // kPartitionFixed / kPartitionEven
     int B, Hkv, cap, tile;    // even partition: how the split kernel cut the tiles
     int shares;               // even partition: workgroups of the split kernel
 };
@@ -409,6 +408,15 @@ __device__ __forceinline__ int clamp_len(const int32_t *seq_lens, int b, int cap
     return min(max(seq_lens[b], 0), cap);
 }
 
+// seq_lens[b] through the vector memory path (a buffer load), so that the
+// wave can issue it before the scalar kernel-argument fetches complete and
+// wait for the two independently.
+__device__ __forceinline__ int load_len_vmem(const int32_t *seq_lens, int b) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void *)seq_lens, (short)0, (b + 1) * 4, kRsrcWord3);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, b * 4, 0, 0);
+}
+
 // Sum over the wave of an int (every lane gets the result).
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
@@ -583,19 +591,30 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
         }
     } else {
         // One tile of registers, refilled as soon as each part is dead: the next
-        // tile's V loads go out once this tile's V is in LDS, its K loads once
-        // QK^T has consumed K, so they fly during softmax and PV.  Half the
-        // registers of the double buffer, so more waves fit per SIMD.
+        // tile's K loads go out once QK^T has consumed K, its V loads once this
+        // tile's V is in LDS, so they fly during the rest of the tile's math.
+        // Half the registers of the double buffer, so more waves fit per SIMD.
         Tile<D, NB> buf;
         if (my_tiles > 0) issue(buf, 0, kLoadV | kLoadK);
         for (int it = 0; it < my_tiles; ++it) {
             const bool more = it + 1 < my_tiles;
             if constexpr (PV == kPvBf16) {
-                stage_v<D, NB>(buf, r, grp, stage);
-                if (more) issue(buf, it + 1, kLoadV);
                 f32x4_t sc[NB];
-                qk_softmax<D, NB>(buf, qb, st, tile_start(it), t_end, grp, a.qk_scale_log2, sc);
-                if (more) issue(buf, it + 1, kLoadK);
+                if (it == 0) {
+                    // The first tile's K arrives before its V (issued first):
+                    // QK^T and the softmax run while V is still in flight.
+                    qk_softmax<D, NB>(buf, qb, st, tile_start(it), t_end, grp, a.qk_scale_log2, sc);
+                    if (more) issue(buf, it + 1, kLoadK);
+                    stage_v<D, NB>(buf, r, grp, stage);
+                    if (more) issue(buf, it + 1, kLoadV);
+                } else {
+                    // Later tiles: stage V first, so that QK^T covers the LDS
+                    // write latency before PV reads the staged V back.
+                    stage_v<D, NB>(buf, r, grp, stage);
+                    if (more) issue(buf, it + 1, kLoadV);
+                    qk_softmax<D, NB>(buf, qb, st, tile_start(it), t_end, grp, a.qk_scale_log2, sc);
+                    if (more) issue(buf, it + 1, kLoadK);
+                }
                 pv_tile<D, NB, PV>(buf, sc, st, r, grp, stage);
             } else {
                 compute_tile<D, NB, PV>(buf, qb, st, tile_start(it), t_end, r, grp, a.qk_scale_log2, stage);
@@ -641,18 +660,26 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
     for (int col = threadIdx.x; col < G * (D / 4); col += 64 * kWaves) {
         const int g = col / (D / 4);
         const int d = 4 * (col - g * (D / 4));
-        float M = -INFINITY;
+        // every LDS read of the column is issued before any is used
+        float mw[kWaves], lw[kWaves];
+        f32x4_t aw[kWaves];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds.m[w][g]);
+        for (int w = 0; w < kWaves; ++w) {
+            mw[w] = lds.m[w][g];
+            lw[w] = lds.l[w][g];
+            aw[w] = *reinterpret_cast<const f32x4_t *>(lds.acc(w) + g * (D + 4) + d);
+        }
+        float M = mw[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mw[w]);
         float L = 0.f;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        if (M != -INFINITY) {
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float sw = __builtin_amdgcn_exp2f(lds.m[w][g] - M);
-                L += sw * lds.l[w][g];
-                acc += sw * *reinterpret_cast<const f32x4_t *>(lds.acc(w) + g * (D + 4) + d);
-            }
+        for (int w = 0; w < kWaves; ++w) {
+            // a wave without keys has m = -inf, l = 0 and a zero accumulator
+            const float sw = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+            L += sw * lw[w];
+            acc += sw * aw[w];
         }
         if (direct) {
             *reinterpret_cast<f32x4_t *>(out_rows + (size_t)g * D + d) =
@@ -670,10 +697,16 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
 
 template <int D, int NB, bool PAGED, int PV, bool DBUF, int PART, int CPOL>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEu<D, DBUF>)))
-void gqa_split_kernel(const SplitArgs a) {
+void gqa_split_kernel(const int32_t *seq_lens, int num_splits, int Hkv, int B, int cap, const SplitArgs args) {
     constexpr int TT = 16 * NB;
     __shared__ FoldLds<D, NB> lds;
-    const int cap = PAGED ? a.max_pages * a.page_size : a.S_max;
+    // The leading scalar arguments arrive preloaded in SGPRs, so the length
+    // loads below issue without waiting for the kernel-argument fetch.
+    SplitArgs a = args;
+    a.seq_lens = seq_lens;
+    a.num_splits = num_splits;
+    a.Hkv = Hkv;
+    a.B = B;
 
     if constexpr (PART == kPartitionEven) {
         // This workgroup's equal share of all tiles, walked piece by piece.
@@ -731,13 +764,15 @@ void gqa_split_kernel(const SplitArgs a) {
         }
         return;
     } else {
-        const int split = blockIdx.x % a.num_splits;
-        const int bk = blockIdx.x / a.num_splits;
-        const int kvh = bk % a.Hkv;
-        const int b = bk / a.Hkv;
+        const int split = blockIdx.x % num_splits;
+        const int bk = blockIdx.x / num_splits;
+        const int kvh = bk % Hkv;
+        const int b = bk / Hkv;
+        const int len_v = load_len_vmem(seq_lens, b);
+        __builtin_amdgcn_sched_barrier(0);  // the length load goes out first
         // Out-of-range lengths / page ids are clamped so that no access can leave
         // the caller's buffers (the results for such inputs are unspecified).
-        const int len = clamp_len(a.seq_lens, b, cap);
+        const int len = min(max(__builtin_amdgcn_readfirstlane(len_v), 0), cap);
         const int t_begin = split * a.split_tokens;
         const int t_end = min(len, t_begin + a.split_tokens);
         const int nsplit = a.num_splits;
@@ -793,8 +828,18 @@ __device__ __forceinline__ void merge_swap(Fold &x) {
     x = lo;
 }
 
-template <int NCOL>
-__global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const CombineArgs a) {
+template <int NCOL, int PART>
+__global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const float *part_acc, const float *part_ml,
+                                                                        int num_splits, int G_arg, int Hq, int D_arg,
+                                                                        const CombineArgs args) {
+    // leading scalar arguments: preloaded in SGPRs (the partial loads wait on nothing else)
+    CombineArgs a = args;
+    a.part_acc = part_acc;
+    a.part_ml = part_ml;
+    a.num_splits = num_splits;
+    a.G = G_arg;
+    a.Hq = Hq;
+    a.D = D_arg;
     static_assert(NCOL == 4 || NCOL == 8 || NCOL == 16, "lanes of one column must share rows of 16");
     constexpr int NSG = kCombineThreads / NCOL;
     constexpr int U = 4;  // pieces per thread per round of loads
@@ -815,7 +860,7 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const Comb
     int S;
     long long N = 0, P = 1, w0 = 0;  // even partition: slot lo + s belongs to share w0 + s
     bool maybe_empty = false;         // shares can be empty only when there are fewer tiles than shares
-    if (a.partition == kPartitionFixed) {
+    if constexpr (PART == kPartitionFixed) {
         S = a.num_splits;
         lo = bk * S;
     } else {
@@ -999,7 +1044,7 @@ hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const f
                           float *out, const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int cap,
                           hipStream_t stream) {
     CombineArgs ca{part_acc, part_ml, out, seq_lens, D, Hq / Hkv, Hq, plan.num_splits,
-                   plan.partition, B, Hkv, cap, plan.tile_tokens, plan.grid};
+                   B, Hkv, cap, plan.tile_tokens, plan.grid};
     // The widest dim chunk (NCOL = 16, 8 or 4 columns of 4 dims) that still
     // gives at least 128 workgroups: narrower chunks put more threads on the
     // pieces of a column (measured best for few heads with many pieces).
@@ -1011,9 +1056,14 @@ hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const f
         while (ncol > 4 && heads * (D / (4 * ncol)) < 128) ncol /= 2;
     }
     const unsigned grid = (unsigned)(heads * (D / (4 * ncol)));
-    if (ncol == 16) hipLaunchKernelGGL(gqa_combine_kernel<16>, dim3(grid), dim3(kCombineThreads), 0, stream, ca);
-    else if (ncol == 8) hipLaunchKernelGGL(gqa_combine_kernel<8>, dim3(grid), dim3(kCombineThreads), 0, stream, ca);
-    else hipLaunchKernelGGL(gqa_combine_kernel<4>, dim3(grid), dim3(kCombineThreads), 0, stream, ca);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kCombineThreads), 0, stream, ca.part_acc, ca.part_ml,
+                           ca.num_splits, ca.G, ca.Hq, ca.D, ca);
+    };
+    const bool even = plan.partition == kPartitionEven;
+    if (ncol == 16) even ? go(gqa_combine_kernel<16, kPartitionEven>) : go(gqa_combine_kernel<16, kPartitionFixed>);
+    else if (ncol == 8) even ? go(gqa_combine_kernel<8, kPartitionEven>) : go(gqa_combine_kernel<8, kPartitionFixed>);
+    else even ? go(gqa_combine_kernel<4, kPartitionEven>) : go(gqa_combine_kernel<4, kPartitionFixed>);
     return hipGetLastError();
 }
 
@@ -1023,21 +1073,21 @@ hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, hipStream
         return hipErrorInvalidValue;
     } else {
         const dim3 grid((unsigned)plan.grid), block(64 * kWaves);
-
+        const int cap = PAGED ? a.max_pages * a.page_size : a.S_max;
         const bool even = plan.partition == kPartitionEven;
         const bool nt = plan.streaming != 0;
         if (plan.pv_mode == kPvF32) {
-            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionEven, 0>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionFixed, 0>), grid, block, 0, stream, a);
+            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionEven, 0>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
+            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionFixed, 0>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
         } else if (plan.double_buffer) {
-            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionEven, 0>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionFixed, 0>), grid, block, 0, stream, a);
+            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionEven, 0>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
+            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionFixed, 0>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
         } else if (nt) {
-            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, kNonTemporal>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, kNonTemporal>), grid, block, 0, stream, a);
+            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, kNonTemporal>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
+            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, kNonTemporal>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
         } else {
-            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, 0>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, 0>), grid, block, 0, stream, a);
+            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, 0>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
+            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, 0>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
         }
         return hipGetLastError();
     }
