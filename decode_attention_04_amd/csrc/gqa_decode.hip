@@ -57,6 +57,8 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -222,10 +224,13 @@ struct WaveState {
     float l;                      // this lane's share of the running sum
 };
 
-// Row stride (in bf16) of a wave's V staging buffer: 4 bf16 of padding put
-// the rows read by the four lane groups on different LDS banks.
+// Row stride (in bf16) of a wave's V staging buffer.  The padding puts the
+// four key rows that a transposing read gathers per lane group on distinct
+// LDS banks (rows 32 bytes apart modulo 256 for D >= 128, 144 for D = 64)
+// and keeps rows aligned for the stores (16 bytes for D >= 128, 8 for D = 64,
+// which also keeps the largest D = 64 tile within four workgroups per CU).
 template <int D>
-constexpr int kStageStride = D + 4;
+constexpr int kStageStride = D == 64 ? D + 8 : D + 16;
 
 // kPvBf16: V rows of a tile (as loaded: key 16*blk + 4*grp + j, dims
 // 16*DPL*c + DPL*r ..) into the wave's LDS staging buffer.
@@ -240,9 +245,12 @@ __device__ __forceinline__ void stage_v(const Tile<D, NB> &t, int r, int grp, un
 #pragma unroll
             for (int c = 0; c < S::VC; ++c) {
                 unsigned short *dst = stage + (16 * blk + 4 * grp + j) * RS + 16 * S::DPL * c + S::DPL * r;
-#pragma unroll
-                for (int w = 0; w < S::VW; w += 2)
-                    *reinterpret_cast<u32x2_t *>(dst + 2 * w) = u32x2_t{t.v[blk][j][c][w], t.v[blk][j][c][w + 1]};
+                if constexpr (S::VW == 4) {
+                    *reinterpret_cast<u32x4_t *>(dst) =
+                        u32x4_t{t.v[blk][j][c][0], t.v[blk][j][c][1], t.v[blk][j][c][2], t.v[blk][j][c][3]};
+                } else {
+                    *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{t.v[blk][j][c][0], t.v[blk][j][c][1]};
+                }
             }
 }
 
@@ -321,7 +329,11 @@ __device__ __forceinline__ void pv_tile(const Tile<D, NB> &t, const f32x4_t (&sc
     } else {
         // O^T[d][g] += V^T[d][t] P^T[t][g] over the 16 keys of each block: the B
         // operand is the lane's own four probabilities (keys 4*grp + i), the A
-        // operand four V values of dim 16*nb + r read back from LDS.
+        // operand the four V values V[4*grp + i][16*nb + r], gathered from the
+        // row-major staging buffer by one transposing LDS read: within each
+        // group of 16 lanes, lane r receives element r % 4 of the 8-byte row
+        // pieces that lanes 4*i + r / 4 point at, so lane r points at key
+        // 4*grp + r / 4, dims 16*nb + 4*(r % 4) .. + 3.
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
             bf16x4_t hi, lo;
@@ -330,12 +342,11 @@ __device__ __forceinline__ void pv_tile(const Tile<D, NB> &t, const f32x4_t (&sc
                 hi[i] = (__bf16)sc[blk][i];
                 lo[i] = (__bf16)(sc[blk][i] - (float)hi[i]);
             }
-            const unsigned short *src = stage + (16 * blk + 4 * grp) * RS + r;
+            const unsigned short *src = stage + (16 * blk + 4 * grp + (r >> 2)) * RS + 4 * (r & 3);
 #pragma unroll
             for (int nb = 0; nb < D / 16; ++nb) {
-                bf16x4_t av;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) av[i] = __builtin_bit_cast(__bf16, src[i * RS + 16 * nb]);
+                const bf16x4_t av = __builtin_bit_cast(
+                    bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(src + 16 * nb)));
                 st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, hi, st.acc[nb], 0, 0, 0);
                 st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, lo, st.acc[nb], 0, 0, 0);
             }
