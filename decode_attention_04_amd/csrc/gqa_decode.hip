@@ -168,6 +168,8 @@ constexpr int kLoadV = 2;
 // (streamed data that is not re-read; on gfx950 it lets large caches stream
 // at a markedly higher rate).
 constexpr int kNonTemporal = 2;
+// Cache policy of the partial stores: the "sc1" (device scope) bit.
+constexpr int kDeviceScope = 16;
 
 template <int D, int NB, int CPOL>
 __device__ __forceinline__ void load_tile(Tile<D, NB> &t, __amdgpu_buffer_rsrc_t rk,
@@ -696,10 +698,17 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
             *reinterpret_cast<f32x4_t *>(out_rows + (size_t)g * D + d) =
                 L > 0.f ? acc / L : f32x4_t{0.f, 0.f, 0.f, 0.f};
         } else {
-            *reinterpret_cast<f32x4_t *>(my_acc + (size_t)g * D + d) = acc;
+            // Device-scope (write-through) stores: the combine kernel reads the
+            // partials from other XCDs, and the kernel-end L2 writeback then has
+            // nothing of them left to flush (measured faster hand-off).
+            const __amdgpu_buffer_rsrc_t ra =
+                __builtin_amdgcn_make_buffer_rsrc((void *)my_acc, (short)0, G * D * 4, kRsrcWord3);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc), ra, (g * D + d) * 4, 0, kDeviceScope);
             if (d == 0) {
-                my_ml[g * 2] = M;
-                my_ml[g * 2 + 1] = L;
+                const __amdgpu_buffer_rsrc_t rm =
+                    __builtin_amdgcn_make_buffer_rsrc((void *)my_ml, (short)0, G * 2 * 4, kRsrcWord3);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(M), __float_as_uint(L)}, rm, g * 8, 0,
+                                                      kDeviceScope);
             }
         }
     }
