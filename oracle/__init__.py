@@ -5,9 +5,10 @@ baseline leg of the benchmark may import this module; the product path never
 does.  It shares no code with the HIP library.
 
 Every function takes the raw bf16 bit patterns (numpy uint16) that the GPU
-path receives, int32 lengths / page tables, and a float32 scale, and returns
-float64 outputs of shape [B, Hq, D].  See oracle.c for the definition and the
-passages of the pages it follows.
+path receives (or, for the *_fp8 functions, OCP FP8 E4M3 bytes as numpy uint8
+plus one fp32 scale per K / V tensor), int32 lengths / page tables, and a
+float32 scale, and returns float64 outputs of shape [B, Hq, D].  See oracle.c
+for the definition and the passages of the pages it follows.
 """
 from __future__ import annotations
 
@@ -53,8 +54,13 @@ def load(path: str | None = None):
                                         cf, f64p]
     lib.oracle_paged_decode_split.argtypes = [u16p, u16p, u16p, i32p, i32p, ci, ci, ci, ci, ci,
                                               ci, ci, cf, ci, f64p]
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    lib.oracle_decode_fp8.argtypes = [u16p, u8p, u8p, i32p, ci, ci, ci, ci, ci, cf, cf, cf, ci, f64p]
+    lib.oracle_paged_decode_fp8.argtypes = [u16p, u8p, u8p, i32p, i32p, ci, ci, ci, ci, ci, ci, ci,
+                                            cf, cf, cf, ci, f64p]
     for fn in (lib.oracle_decode, lib.oracle_decode_split, lib.oracle_paged_decode,
-               lib.oracle_paged_decode_split, lib.oracle_max_threads):
+               lib.oracle_paged_decode_split, lib.oracle_max_threads, lib.oracle_decode_fp8,
+               lib.oracle_paged_decode_fp8):
         fn.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ci]
     lib.oracle_set_threads.restype = None
@@ -121,6 +127,55 @@ def paged_decode(q, k_pool, v_pool, seq_lens, page_table, scale, *, chunk: int =
         rc = lib.oracle_paged_decode(*args, _ptr(out, ctypes.c_double))
     if rc != 0:
         raise ValueError(f"oracle_paged_decode failed with code {rc}")
+    return out
+
+
+def _u8(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint8:
+        raise TypeError("fp8 inputs must be passed as uint8 E4M3 bytes")
+    return a
+
+
+def decode_fp8(q, k, v, seq_lens, scale, k_scale, v_scale, *, chunk: int = 0,
+               lib=None) -> np.ndarray:
+    """Contiguous E4M3 cache: k/v [B,Hkv,S_max,D] uint8, one fp32 scale per tensor."""
+    lib = lib or load()
+    q, k, v, seq_lens = _u16(q), _u8(k), _u8(v), _i32(seq_lens)
+    B, Hq, D = q.shape
+    Bk, Hkv, S_max, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D or seq_lens.shape != (B,):
+        raise ValueError("shape mismatch")
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    rc = lib.oracle_decode_fp8(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint8),
+                               _ptr(v, ctypes.c_uint8), _ptr(seq_lens, ctypes.c_int32), B, Hq,
+                               Hkv, D, S_max, ctypes.c_float(scale), ctypes.c_float(k_scale),
+                               ctypes.c_float(v_scale), int(chunk), _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle_decode_fp8 failed with code {rc}")
+    return out
+
+
+def paged_decode_fp8(q, k_pool, v_pool, seq_lens, page_table, scale, k_scale, v_scale, *,
+                     chunk: int = 0, lib=None) -> np.ndarray:
+    """Paged E4M3 cache: k/v pools [P,Hkv,page_size,D] uint8, page_table [B,max_pages]."""
+    lib = lib or load()
+    q, k_pool, v_pool = _u16(q), _u8(k_pool), _u8(v_pool)
+    seq_lens, page_table = _i32(seq_lens), _i32(page_table)
+    B, Hq, D = q.shape
+    P, Hkv, ps, Dk = k_pool.shape
+    if v_pool.shape != k_pool.shape or Dk != D or seq_lens.shape != (B,) or \
+            page_table.ndim != 2 or page_table.shape[0] != B:
+        raise ValueError("shape mismatch")
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    rc = lib.oracle_paged_decode_fp8(_ptr(q, ctypes.c_uint16), _ptr(k_pool, ctypes.c_uint8),
+                                     _ptr(v_pool, ctypes.c_uint8), _ptr(seq_lens, ctypes.c_int32),
+                                     _ptr(page_table, ctypes.c_int32), B, Hq, Hkv, D, ps, P,
+                                     page_table.shape[1], ctypes.c_float(scale),
+                                     ctypes.c_float(k_scale), ctypes.c_float(v_scale), int(chunk),
+                                     _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle_paged_decode_fp8 failed with code {rc}")
     return out
 
 

@@ -29,6 +29,13 @@
  * in ascending chunk order.  They exist only so the tests can pin the split
  * algebra (invariance to the split count) against the plain definition.
  *
+ * Quantized cache (the int8/fp8 pools of sparkinfer PR #874, "Cost and
+ * fallbacks", dequantised before use; the pages fix no format, the reading
+ * taken here is the plainest one): K and V hold OCP FP8 E4M3 bytes, one
+ * fp32 scale per tensor, and the value of an element is its scale times the
+ * E4M3 value of the byte (sign bit, 4-bit exponent with bias 7, 3-bit
+ * mantissa; exponent 0 is subnormal, m/8 * 2^-6; byte 0x7F / 0xFF is NaN).
+ *
  * Cache layouts (the pages fix only the index order K[b, h/G, t]):
  *   contiguous: K, V are [B][Hkv][S_max][D]
  *   paged:      K, V pools are [num_pages][Hkv][page_size][D]; token t of
@@ -49,11 +56,13 @@
 #endif
 
 typedef struct {
-    const uint16_t *k, *v;
+    const void *k, *v;
     const int32_t *page_table; /* NULL for the contiguous layout */
     int Hkv, D;
     int S_max;                 /* contiguous capacity per (b, kv head) */
     int page_size, max_pages;  /* paged only */
+    int fp8;                   /* 0: bf16 bit patterns; 1: E4M3 bytes times k_scale / v_scale */
+    double k_scale, v_scale;
 } kv_layout;
 
 /* bf16 -> double: the bf16 pattern is the upper half of an IEEE float. */
@@ -62,6 +71,25 @@ static double widen_bf16(uint16_t bits) {
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/* OCP FP8 E4M3 byte -> double, from the format's definition. */
+static double decode_e4m3(uint8_t byte) {
+    const double sign = (byte & 0x80) ? -1.0 : 1.0;
+    const int e = (byte >> 3) & 0xF, m = byte & 7;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) return sign * ldexp((double)m / 8.0, -6);
+    return sign * ldexp(1.0 + (double)m / 8.0, e - 7);
+}
+
+/* Element i of the K / V storage, dequantised. */
+static double k_elem(const kv_layout *L, size_t i) {
+    if (L->fp8) return L->k_scale * decode_e4m3(((const uint8_t *)L->k)[i]);
+    return widen_bf16(((const uint16_t *)L->k)[i]);
+}
+static double v_elem(const kv_layout *L, size_t i) {
+    if (L->fp8) return L->v_scale * decode_e4m3(((const uint8_t *)L->v)[i]);
+    return widen_bf16(((const uint16_t *)L->v)[i]);
 }
 
 /* Element offset of row (b, kvh, t) in the K or V storage. */
@@ -75,9 +103,9 @@ static size_t row_offset(const kv_layout *L, int b, int kvh, int t) {
 
 /* score of token t for the query row q (D bf16 values) */
 static double score(const kv_layout *L, const uint16_t *q, int b, int kvh, int t, double scale) {
-    const uint16_t *krow = L->k + row_offset(L, b, kvh, t);
+    const size_t kbase = row_offset(L, b, kvh, t);
     double dot = 0.0;
-    for (int d = 0; d < L->D; ++d) dot += widen_bf16(q[d]) * widen_bf16(krow[d]);
+    for (int d = 0; d < L->D; ++d) dot += widen_bf16(q[d]) * k_elem(L, kbase + d);
     return scale * dot;
 }
 
@@ -98,9 +126,9 @@ static void range_stats(const kv_layout *L, const uint16_t *q, int b, int kvh, i
     }
     for (int t = t0; t < t1; ++t) {
         double w = exp(s[t - t0] - m);
-        const uint16_t *vrow = L->v + row_offset(L, b, kvh, t);
+        const size_t vbase = row_offset(L, b, kvh, t);
         l += w;
-        for (int d = 0; d < D; ++d) acc[d] += w * widen_bf16(vrow[d]);
+        for (int d = 0; d < D; ++d) acc[d] += w * v_elem(L, vbase + d);
     }
     *m_out = m;
     *l_out = l;
@@ -181,7 +209,7 @@ static int decode_all(const kv_layout *L, const uint16_t *q, const int32_t *seq_
 
 int oracle_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *seq_lens,
                   int B, int Hq, int Hkv, int D, int S_max, float scale, double *out) {
-    kv_layout L = {k, v, NULL, Hkv, D, S_max, 0, 0};
+    kv_layout L = {k, v, NULL, Hkv, D, S_max, 0, 0, 0, 1.0, 1.0};
     for (int b = 0; b < B; ++b)
         if (seq_lens[b] > S_max) return 2;
     return decode_all(&L, q, seq_lens, B, Hq, (double)scale, 0, out);
@@ -190,7 +218,7 @@ int oracle_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
 int oracle_decode_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
                         float scale, int chunk, double *out) {
-    kv_layout L = {k, v, NULL, Hkv, D, S_max, 0, 0};
+    kv_layout L = {k, v, NULL, Hkv, D, S_max, 0, 0, 0, 1.0, 1.0};
     if (chunk <= 0) return 1;
     for (int b = 0; b < B; ++b)
         if (seq_lens[b] > S_max) return 2;
@@ -201,7 +229,7 @@ int oracle_paged_decode(const uint16_t *q, const uint16_t *k_pool, const uint16_
                         const int32_t *seq_lens, const int32_t *page_table, int B, int Hq, int Hkv,
                         int D, int page_size, int num_pages, int max_pages, float scale,
                         double *out) {
-    kv_layout L = {k_pool, v_pool, page_table, Hkv, D, 0, page_size, max_pages};
+    kv_layout L = {k_pool, v_pool, page_table, Hkv, D, 0, page_size, max_pages, 0, 1.0, 1.0};
     if (page_size <= 0 || max_pages < 0) return 1;
     for (int b = 0; b < B; ++b) {
         if (seq_lens[b] > page_size * max_pages) return 2;
@@ -218,8 +246,36 @@ int oracle_paged_decode_split(const uint16_t *q, const uint16_t *k_pool, const u
                               const int32_t *seq_lens, const int32_t *page_table, int B, int Hq,
                               int Hkv, int D, int page_size, int num_pages, int max_pages,
                               float scale, int chunk, double *out) {
-    kv_layout L = {k_pool, v_pool, page_table, Hkv, D, 0, page_size, max_pages};
+    kv_layout L = {k_pool, v_pool, page_table, Hkv, D, 0, page_size, max_pages, 0, 1.0, 1.0};
     if (page_size <= 0 || max_pages < 0 || chunk <= 0) return 1;
+    for (int b = 0; b < B; ++b) {
+        if (seq_lens[b] > page_size * max_pages) return 2;
+        int used = (seq_lens[b] + page_size - 1) / page_size;
+        for (int i = 0; i < used; ++i) {
+            int p = page_table[(size_t)b * max_pages + i];
+            if (p < 0 || p >= num_pages) return 2;
+        }
+    }
+    return decode_all(&L, q, seq_lens, B, Hq, (double)scale, chunk, out);
+}
+
+/* The same over an E4M3 cache with per-tensor scales (chunk > 0: split mode). */
+int oracle_decode_fp8(const uint16_t *q, const uint8_t *k, const uint8_t *v, const int32_t *seq_lens,
+                      int B, int Hq, int Hkv, int D, int S_max, float scale, float k_scale,
+                      float v_scale, int chunk, double *out) {
+    kv_layout L = {k, v, NULL, Hkv, D, S_max, 0, 0, 1, (double)k_scale, (double)v_scale};
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] > S_max) return 2;
+    return decode_all(&L, q, seq_lens, B, Hq, (double)scale, chunk, out);
+}
+
+int oracle_paged_decode_fp8(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
+                            const int32_t *seq_lens, const int32_t *page_table, int B, int Hq,
+                            int Hkv, int D, int page_size, int num_pages, int max_pages,
+                            float scale, float k_scale, float v_scale, int chunk, double *out) {
+    kv_layout L = {k_pool, v_pool, page_table, Hkv, D, 0, page_size, max_pages, 1, (double)k_scale,
+                   (double)v_scale};
+    if (page_size <= 0 || max_pages < 0) return 1;
     for (int b = 0; b < B; ++b) {
         if (seq_lens[b] > page_size * max_pages) return 2;
         int used = (seq_lens[b] + page_size - 1) / page_size;

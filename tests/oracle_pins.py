@@ -273,9 +273,79 @@ def pin_page_permutation(lib):
         raise AssertionError("page permutation changed the output")
 
 
+# --------------------------------------------------------------------- the E4M3 cache
+def _fp8_values(lib, v_scale=1.0) -> np.ndarray:
+    """The oracle's value of every E4M3 byte (NaN bytes 0x7F / 0xFF read as NaN), through the
+    len = 1 identity out = V[0]: the V row holds the 256 byte values."""
+    D = 256
+    q = _bits(np.zeros((1, 1, D), np.float32))
+    k = np.zeros((1, 1, 1, D), np.uint8)
+    row = np.arange(256, dtype=np.uint8)
+    finite = (row != 0x7F) & (row != 0xFF)
+    v = np.where(finite, row, 0).astype(np.uint8).reshape(1, 1, 1, D)
+    out = oracle.decode_fp8(q, k, v, np.array([1], np.int32), 1.0, 1.0, v_scale, lib=lib)[0, 0]
+    return np.where(finite, out, np.nan)
+
+
+def pin_fp8_values(lib):
+    """The E4M3 values the oracle dequantises to, against values of the OCP FP8 format:
+    zero, the subnormal steps of 2^-9, every power of two 2^-6 .. 2^8, a few interior
+    points, the maximum 448, strict growth over 0x00..0x7E and sign symmetry."""
+    val = _fp8_values(lib)
+    facts = {0x00: 0.0, 0x01: 2.0 ** -9, 0x02: 2.0 ** -8, 0x03: 3 * 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+             0x39: 1.125, 0x3C: 1.5, 0x3F: 1.875, 0x44: 3.0, 0x6F: 120.0, 0x7E: 448.0,
+             0x80: 0.0, 0xB8: -1.0, 0xFE: -448.0}
+    for e in range(1, 16):
+        facts[e << 3] = 2.0 ** (e - 7)
+    for b, x in facts.items():
+        assert val[b] == x, f"E4M3 byte {b:#04x}: {val[b]} != {x}"
+    pos = val[:0x7F]
+    assert np.all(np.diff(pos) > 0), "E4M3 values must grow strictly over 0x00 .. 0x7E"
+    assert np.array_equal(val[0x80:0xFF], -pos), "E4M3 sign bit must negate"
+    assert np.isnan(val[0x7F]) and np.isnan(val[0xFF])
+    half = _fp8_values(lib, v_scale=0.5)
+    assert np.array_equal(half[:0x7F], pos * 0.5), "v_scale must multiply V"
+
+
+def _fp8_as_bf16(lib, case: W.Case) -> W.Case:
+    """The same call with K and V dequantised (power-of-two scales: exact in bf16)."""
+    table = _fp8_values(lib)
+    kd = (table[case.k] * case.k_scale).astype(np.float32)
+    vd = (table[case.v] * case.v_scale).astype(np.float32)
+    return W.Case(case.name, case.B, case.Hq, case.Hkv, case.D, case.scale, case.q,
+                  _bits(kd), _bits(vd), case.seq_lens, case.page_table, case.page_size)
+
+
+def pin_fp8_matches_bf16(lib):
+    """With power-of-two per-tensor scales every dequantised element is a bf16 value, so the
+    E4M3 path must give exactly the bf16 path's output on the dequantised cache."""
+    c = W.fp8_contig_case(2, 8, 2, 64, 40, seq_lens=[40, 17], seed=70, k_scale=0.5, v_scale=0.25)
+    got = oracle.decode_fp8(c.q, c.k, c.v, c.seq_lens, c.scale, c.k_scale, c.v_scale, lib=lib)
+    d = _fp8_as_bf16(lib, c)
+    ref = oracle.decode(d.q, d.k, d.v, d.seq_lens, d.scale, lib=lib)
+    assert np.array_equal(got, ref), "fp8 cache != bf16 cache holding the same values"
+    p = W.fp8_paged_case(3, 8, 2, 64, 16, 40, seq_lens=[33, 1, 64], seed=71, k_scale=2.0,
+                         v_scale=0.125)
+    got = oracle.paged_decode_fp8(p.q, p.k, p.v, p.seq_lens, p.page_table, p.scale, p.k_scale,
+                                  p.v_scale, lib=lib)
+    d = _fp8_as_bf16(lib, p)
+    ref = oracle.paged_decode(d.q, d.k, d.v, d.seq_lens, d.page_table, d.scale, lib=lib)
+    assert np.array_equal(got, ref), "paged fp8 cache != bf16 cache holding the same values"
+
+
+def pin_fp8_split_invariance(lib):
+    c = W.fp8_contig_case(2, 8, 1, 64, 70, seq_lens=[70, 9], seed=72)
+    ref = oracle.decode_fp8(c.q, c.k, c.v, c.seq_lens, c.scale, c.k_scale, c.v_scale, lib=lib)
+    for chunk in (1, 3, 16, 70):
+        got = oracle.decode_fp8(c.q, c.k, c.v, c.seq_lens, c.scale, c.k_scale, c.v_scale,
+                                chunk=chunk, lib=lib)
+        _close(got, ref, what=f"fp8 split chunk={chunk}")
+
+
 ALL_PINS = [
     pin_golden_closed_forms, pin_torch_sdpa, pin_brute_force, pin_len_one_is_v0,
     pin_uniform_weights_give_mean, pin_dominant_key, pin_scale_moves_into_q, pin_v_is_linear,
     pin_token_permutation, pin_head_mapping, pin_nan_tail_ignored, pin_split_invariance,
-    pin_paged_equals_gathered, pin_page_permutation,
+    pin_paged_equals_gathered, pin_page_permutation, pin_fp8_values, pin_fp8_matches_bf16,
+    pin_fp8_split_invariance,
 ]

@@ -56,3 +56,26 @@ def test_named_workload_shapes():
     c = W.make("tiny_gqa4_d64_ctx512")
     assert (c.B, c.Hq, c.Hkv, c.D, c.S_max, c.scale) == (1, 8, 2, 64, 512, 0.125)
     assert c.algorithmic_bytes() == 512 * 2 * 64 * 4 + 8 * 64 * 2 + 8 * 64 * 4
+
+
+def test_e4m3_encoder():
+    """Nearest E4M3 value, ties to an even mantissa, saturation at 448, NaN -> 0x7F."""
+    x = np.array([0.0, 1.0, 1.0625, 1.1875, 448.0, 1e6, -1.0, 2.0 ** -9, 2.0 ** -10,
+                  3 * 2.0 ** -10, np.nan, -0.0, 240.0, 232.0], np.float32)
+    got = W.f32_to_e4m3_bytes(x)
+    want = [0x00, 0x38, 0x38, 0x3A, 0x7E, 0x7E, 0xB8, 0x01, 0x00, 0x02, 0x7F, 0x80, 0x77, 0x76]
+    assert got.tolist() == want
+    # every finite byte value is encoded to itself
+    grid = W._E4M3
+    assert np.array_equal(W.f32_to_e4m3_bytes(grid.astype(np.float32)), np.arange(127, dtype=np.uint8))
+    assert np.array_equal(W.f32_to_e4m3_bytes(-grid[1:].astype(np.float32)),
+                          (np.arange(1, 127) | 0x80).astype(np.uint8))
+
+
+def test_fp8_cases():
+    c = W.fp8_contig_case(2, 8, 2, 64, 50, seq_lens=[50, 7], seed=3, tail="nan")
+    assert c.kv == "fp8" and c.k.dtype == np.uint8 and c.k.shape == (2, 2, 50, 64)
+    assert np.all(c.k[1, :, 7:, :] == 0x7F) and not np.any(c.k[0] == 0x7F)
+    assert c.algorithmic_bytes() == 57 * 2 * 64 * 2 + 2 * 8 * 64 * 6
+    p = W.fp8_paged_case(4, 8, 2, 64, 16, 64, max_len=100, seed=4)
+    assert p.paged and p.k.dtype == np.uint8 and p.page_table.shape == (4, 7)

@@ -17,6 +17,11 @@ Recipe (all five named workloads):
     unused table entries are -1;
   * the peaky long-context workload multiplies the whole key row of
     floor(1% of the context) distinct token positions by 8 (exact in bf16).
+
+FP8 caches (the quantized-KV variant): q as above; K and V ~ N(0, 1) drawn
+as float32, divided by their per-tensor scale (1/16 unless stated, a power of
+two) and rounded to the nearest OCP FP8 E4M3 value (ties to an even
+mantissa, saturating at +-448), stored as uint8 bytes.
 """
 from __future__ import annotations
 
@@ -52,6 +57,42 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+# ---------------------------------------------------------------- fp8 (E4M3) bytes
+def _e4m3_grid() -> np.ndarray:
+    """Values of the bytes 0x00 .. 0x7E (all finite non-negative E4M3 values, ascending)."""
+    b = np.arange(127)
+    e, m = (b >> 3) & 0xF, b & 7
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7)).astype(np.float64)
+
+
+_E4M3 = _e4m3_grid()
+
+
+def f32_to_e4m3_bytes(x: np.ndarray) -> np.ndarray:
+    """float32 -> OCP FP8 E4M3 bytes: nearest value, ties to an even mantissa, saturating
+    at +-448; NaN -> 0x7F."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x).astype(np.float64).reshape(-1)
+    hi = np.clip(np.searchsorted(_E4M3, a), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    dlo, dhi = np.abs(a - _E4M3[lo]), np.abs(_E4M3[hi] - a)
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a >= _E4M3[126], 126, pick).astype(np.uint8)
+    out = pick | np.where(np.signbit(x.reshape(-1)), 0x80, 0).astype(np.uint8)
+    out[np.isnan(x.reshape(-1))] = 0x7F
+    return out.reshape(x.shape)
+
+
+def _normal_fp8(rng: np.random.Generator, shape, kv_scale: float) -> np.ndarray:
+    out = np.empty(shape, np.uint8)
+    flat = out.reshape(-1)
+    n, step = flat.size, 1 << 22
+    for i in range(0, n, step):
+        m = min(step, n - i)
+        flat[i:i + m] = f32_to_e4m3_bytes(rng.standard_normal(m, dtype=np.float32) / np.float32(kv_scale))
+    return out
+
+
 def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
     return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32)).reshape(shape)
 
@@ -72,6 +113,9 @@ class Case:
     seq_lens: np.ndarray          # int32 [B]
     page_table: np.ndarray | None = None   # int32 [B, max_pages] (paged only)
     page_size: int = 0
+    kv: str = "bf16"              # "bf16": k, v are uint16 bf16 bits; "fp8": uint8 E4M3 bytes
+    k_scale: float = 1.0          # fp8: per-tensor scales (float32 values)
+    v_scale: float = 1.0
 
     @property
     def paged(self) -> bool:
@@ -98,9 +142,14 @@ class Case:
         """Largest sequence length the cache can hold."""
         return self.max_pages * self.page_size if self.paged else self.S_max
 
+    @property
+    def kv_bytes(self) -> int:
+        """Bytes per cache element (2 for bf16, 1 for fp8)."""
+        return 1 if self.kv == "fp8" else 2
+
     def algorithmic_bytes(self) -> int:
-        """sum(len) * Hkv * D * 2 (K and V) * 2 B + q (bf16) + out (fp32)."""
-        return (int(self.seq_lens.astype(np.int64).sum()) * self.Hkv * self.D * 4
+        """sum(len) * Hkv * D * 2 (K and V) * element bytes + q (bf16) + out (fp32)."""
+        return (int(self.seq_lens.astype(np.int64).sum()) * self.Hkv * self.D * 2 * self.kv_bytes
                 + self.B * self.Hq * self.D * 2 + self.B * self.Hq * self.D * 4)
 
 
@@ -128,6 +177,44 @@ def _contig(rng, B, Hq, Hkv, D, S_max, seq_lens, scale, tail, name) -> Case:
             v[b, :, lens[b]:, :] = fill
     return Case(name, B, Hq, Hkv, D, default_scale(D) if scale is None else float(np.float32(scale)),
                 q, k, v, lens)
+
+
+def fp8_contig_case(B, Hq, Hkv, D, S_max, seq_lens=None, *, seed=0, scale=None, k_scale=1 / 16,
+                    v_scale=1 / 16, tail=None, name="fp8_contig") -> Case:
+    """Contiguous E4M3 cache with per-tensor scales.  tail "nan" poisons rows >= len (0x7F)."""
+    rng = np.random.default_rng(seed)
+    q = _normal_bf16(rng, (B, Hq, D))
+    k = _normal_fp8(rng, (B, Hkv, S_max, D), k_scale)
+    v = _normal_fp8(rng, (B, Hkv, S_max, D), v_scale)
+    lens = np.full(B, S_max, np.int32) if seq_lens is None else np.asarray(seq_lens, np.int32)
+    if tail == "nan":
+        for b in range(B):
+            k[b, :, lens[b]:, :] = 0x7F
+            v[b, :, lens[b]:, :] = 0x7F
+    return Case(name, B, Hq, Hkv, D, default_scale(D) if scale is None else float(np.float32(scale)),
+                q, k, v, lens, kv="fp8", k_scale=float(np.float32(k_scale)),
+                v_scale=float(np.float32(v_scale)))
+
+
+def fp8_paged_case(B, Hq, Hkv, D, page_size, num_pages, seq_lens=None, *, max_len=None, seed=0,
+                   scale=None, k_scale=1 / 16, v_scale=1 / 16, max_pages=None,
+                   name="fp8_paged") -> Case:
+    """Paged E4M3 cache.  If seq_lens is None they are drawn uniformly from 1..max_len."""
+    rng = np.random.default_rng(seed)
+    q = _normal_bf16(rng, (B, Hq, D))
+    k = _normal_fp8(rng, (num_pages, Hkv, page_size, D), k_scale)
+    v = _normal_fp8(rng, (num_pages, Hkv, page_size, D), v_scale)
+    if seq_lens is None:
+        lens = rng.integers(1, max_len, size=B, endpoint=True).astype(np.int32)
+    else:
+        lens = np.asarray(seq_lens, np.int32)
+    cap = max_len if max_len is not None else int(lens.max(initial=0))
+    if max_pages is None:
+        max_pages = max(1, (cap + page_size - 1) // page_size)
+    table = assign_pages(rng, lens, page_size, num_pages, max_pages)
+    return Case(name, B, Hq, Hkv, D, default_scale(D) if scale is None else float(np.float32(scale)),
+                q, k, v, lens, table, page_size, kv="fp8", k_scale=float(np.float32(k_scale)),
+                v_scale=float(np.float32(v_scale)))
 
 
 def assign_pages(rng: np.random.Generator, lens, page_size: int, num_pages: int,
