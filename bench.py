@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's heuristic")
+    ap.add_argument("--kv", choices=("bf16", "fp8"), default="bf16",
+                    help="cache element type: bf16 (the headline), or the workload's OCP FP8 E4M3 "
+                         "form with per-tensor scales (gqa_decode_fp8)")
     ap.add_argument("--rotate-bytes", type=float, default=2.0 * 2**30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -163,7 +166,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     gd.load()
     name = args.workload or W.HEADLINE
-    case = W.make(name)
+    case = W.make(name, kv=args.kv)
     base = DeviceCase(case)
     algo_bytes = case.algorithmic_bytes()
     kv_bytes = case.k.nbytes + case.v.nbytes
@@ -189,7 +192,17 @@ def main():
 
     def split_only(i, stream):
         d = sets[i % R]
-        if case.paged:
+        if case.kv == "fp8":
+            if case.paged:
+                gd.gqa_paged_decode_fp8_partials(d.q, d.k, d.v, d.seq_lens, d.page_table,
+                                                 case.scale, case.k_scale, case.v_scale,
+                                                 out=outs[i % R], workspace=ws,
+                                                 num_splits=args.splits, stream=stream)
+            else:
+                gd.gqa_decode_fp8_partials(d.q, d.k, d.v, d.seq_lens, case.scale, case.k_scale,
+                                           case.v_scale, out=outs[i % R], workspace=ws,
+                                           num_splits=args.splits, stream=stream)
+        elif case.paged:
             gd.gqa_paged_decode_partials(d.q, d.k, d.v, d.seq_lens, d.page_table, case.scale,
                                          out=outs[i % R], workspace=ws, num_splits=args.splits,
                                          stream=stream)
@@ -255,7 +268,13 @@ def main():
         t0 = time.perf_counter()
         calls = 0
         while True:
-            if case.paged:
+            if case.kv == "fp8" and case.paged:
+                oracle.paged_decode_fp8(case.q, case.k, case.v, case.seq_lens, case.page_table,
+                                        case.scale, case.k_scale, case.v_scale)
+            elif case.kv == "fp8":
+                oracle.decode_fp8(case.q, case.k, case.v, case.seq_lens, case.scale, case.k_scale,
+                                  case.v_scale)
+            elif case.paged:
                 oracle.paged_decode(case.q, case.k, case.v, case.seq_lens, case.page_table,
                                     case.scale)
             else:
@@ -269,9 +288,9 @@ def main():
                "sample": f"{calls} full calls of {name} through the fp64 C oracle "
                          f"({el:.1f} s, {threads} OpenMP threads)"}
 
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(name) if args.kv == "bf16" else None
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.kv == "bf16" else METRIC + ", OCP FP8 E4M3 KV cache (1 B/element)",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -284,8 +303,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 q/K/V)",
+        "dtype": "bf16" if args.kv == "bf16" else "fp8-e4m3 KV, bf16 q and MFMA",
+        "data": "synthetic (seeded N(0,1) bf16 q/K/V)" if args.kv == "bf16" else
+                "synthetic (seeded N(0,1) bf16 q; K/V the same draws rounded to E4M3 at scale 1/16)",
         "config": {"workload": name, "batch": case.B, "q_heads": case.Hq, "kv_heads": case.Hkv,
                    "head_dim": case.D, "capacity": cap, "page_size": case.page_size,
                    "sum_len": int(case.seq_lens.sum()), "algorithmic_bytes": algo_bytes,

@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_
 # every symbol include/gqa_decode.h declares
 EXPORTED = ("gqa_decode_plan", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_paged_decode",
             "gqa_decode_partials", "gqa_paged_decode_partials", "gqa_decode_combine",
-            "gqa_status_string")
+            "gqa_decode_fp8", "gqa_paged_decode_fp8", "gqa_decode_fp8_partials",
+            "gqa_paged_decode_fp8_partials", "gqa_status_string")
 
 
 class GqaError(RuntimeError):
@@ -77,6 +78,15 @@ def load(path: str = LIB_PATH):
     lib.gqa_paged_decode_partials.restype = ci
     lib.gqa_decode_combine.argtypes = [vp, sz, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp]
     lib.gqa_decode_combine.restype = ci
+    lib.gqa_decode_fp8.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, cf, cf, vp, vp, sz, ci, vp]
+    lib.gqa_decode_fp8.restype = ci
+    lib.gqa_paged_decode_fp8.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, cf, cf,
+                                         vp, vp, sz, ci, vp]
+    lib.gqa_paged_decode_fp8.restype = ci
+    lib.gqa_decode_fp8_partials.argtypes = lib.gqa_decode_fp8.argtypes
+    lib.gqa_decode_fp8_partials.restype = ci
+    lib.gqa_paged_decode_fp8_partials.argtypes = lib.gqa_paged_decode_fp8.argtypes
+    lib.gqa_paged_decode_fp8_partials.restype = ci
     lib.gqa_status_string.argtypes = [ci]
     lib.gqa_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -150,8 +160,7 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None, n
     """Contiguous cache: q [B,Hq,D], k/v [B,Hkv,S_max,D] bf16, seq_lens int32 [B].
 
     Returns out (fp32 [B,Hq,D]).  `workspace` (a uint8 device tensor) is
-    allocated (zero-filled) when not given; pass one to keep the call
-    allocation-free."""
+    allocated when not given; pass one to keep the call allocation-free."""
     torch = _torch()
     B, Hq, D = q.shape
     _, Hkv, S_max, _ = k_cache.shape
@@ -193,6 +202,80 @@ def gqa_paged_decode(q, k_pool, v_pool, seq_lens, page_table, scale, out=None, w
     if rc != GQA_OK:
         raise GqaError(rc, _entry)
     return out
+
+
+def _fp8_types():
+    torch = _torch()
+    return tuple(t for t in (torch.uint8, getattr(torch, "float8_e4m3fn", None)) if t is not None)
+
+
+def gqa_decode_fp8(q, k_cache, v_cache, seq_lens, scale, k_scale, v_scale, out=None,
+                   workspace=None, num_splits=0, stream=None, _entry="gqa_decode_fp8"):
+    """Contiguous E4M3 cache: k/v [B,Hkv,S_max,D] uint8 (or float8_e4m3fn) bytes, one fp32
+    scale per tensor; otherwise as gqa_decode."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    _, Hkv, S_max, _ = k_cache.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, S_max, 0, num_splits)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    f8 = _fp8_types()
+    rc = getattr(load(), _entry)(
+        _dev_ptr(q, "q", _bf16_types()), _dev_ptr(k_cache, "k_cache", f8),
+        _dev_ptr(v_cache, "v_cache", f8), _dev_ptr(seq_lens, "seq_lens", (torch.int32,)), B, Hq,
+        Hkv, D, S_max, float(scale), float(k_scale), float(v_scale),
+        _dev_ptr(out, "out", (torch.float32,)),
+        None if workspace is None else workspace.data_ptr(), ws_bytes, int(num_splits),
+        _stream_ptr(stream, q.device))
+    if rc != GQA_OK:
+        raise GqaError(rc, _entry)
+    return out
+
+
+def gqa_paged_decode_fp8(q, k_pool, v_pool, seq_lens, page_table, scale, k_scale, v_scale,
+                         out=None, workspace=None, num_splits=0, stream=None,
+                         _entry="gqa_paged_decode_fp8"):
+    """Paged E4M3 cache: k/v pools [P,Hkv,page_size,D] uint8 (or float8_e4m3fn) bytes."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    P, Hkv, page_size, _ = k_pool.shape
+    max_pages = page_table.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, max_pages * page_size, page_size, num_splits)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    f8 = _fp8_types()
+    rc = getattr(load(), _entry)(
+        _dev_ptr(q, "q", _bf16_types()), _dev_ptr(k_pool, "k_pool", f8),
+        _dev_ptr(v_pool, "v_pool", f8), _dev_ptr(seq_lens, "seq_lens", (torch.int32,)),
+        _dev_ptr(page_table, "page_table", (torch.int32,)), B, Hq, Hkv, D, page_size, P,
+        max_pages, float(scale), float(k_scale), float(v_scale),
+        _dev_ptr(out, "out", (torch.float32,)),
+        None if workspace is None else workspace.data_ptr(), ws_bytes, int(num_splits),
+        _stream_ptr(stream, q.device))
+    if rc != GQA_OK:
+        raise GqaError(rc, _entry)
+    return out
+
+
+def gqa_decode_fp8_partials(q, k_cache, v_cache, seq_lens, scale, k_scale, v_scale, out=None,
+                            workspace=None, num_splits=0, stream=None):
+    """The split kernel of gqa_decode_fp8 alone (partials into `workspace`, which must be given)."""
+    if workspace is None:
+        raise ValueError("gqa_decode_fp8_partials needs the workspace the combine will read")
+    return gqa_decode_fp8(q, k_cache, v_cache, seq_lens, scale, k_scale, v_scale, out, workspace,
+                          num_splits, stream, _entry="gqa_decode_fp8_partials")
+
+
+def gqa_paged_decode_fp8_partials(q, k_pool, v_pool, seq_lens, page_table, scale, k_scale,
+                                  v_scale, out=None, workspace=None, num_splits=0, stream=None):
+    """The split kernel of gqa_paged_decode_fp8 alone."""
+    if workspace is None:
+        raise ValueError("gqa_paged_decode_fp8_partials needs the workspace the combine will read")
+    return gqa_paged_decode_fp8(q, k_pool, v_pool, seq_lens, page_table, scale, k_scale, v_scale,
+                                out, workspace, num_splits, stream,
+                                _entry="gqa_paged_decode_fp8_partials")
 
 
 def gqa_decode_partials(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None,

@@ -73,8 +73,8 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords (gfx9 famil
 // per slot (see "work partition" below for the slot numbering).
 struct SplitArgs {
     const uint16_t *q;
-    const uint16_t *k;
-    const uint16_t *v;
+    const unsigned char *k;     // bf16 or E4M3 cache, addressed in bytes
+    const unsigned char *v;
     const int32_t *seq_lens;
     const int32_t *page_table;  // paged only
     float *part_acc;
@@ -85,7 +85,8 @@ struct SplitArgs {
     int page_size, max_pages;   // paged
     int num_pages;              // paged
     int num_splits, split_tokens;
-    float qk_scale_log2;        // scale * log2(e)
+    float qk_scale_log2;        // scale * log2(e) (times k_scale for an E4M3 cache)
+    float v_scale;              // E4M3 cache: V's per-tensor scale
 };
 
 struct CombineArgs {
@@ -136,12 +137,6 @@ __device__ __forceinline__ float row_ror(float x, int n) {
     }
 }
 
-// Element e (0..2*N-1) of a vector of N dwords holding 2*N bf16 values.
-template <int N>
-__device__ __forceinline__ float bf16_elem(const unsigned int (&w)[N], int e) {
-    return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
-}
-
 template <int D>
 struct Shape {
     static constexpr int KB = D / 32;                  // 32-dim blocks of the QK contraction
@@ -151,12 +146,60 @@ struct Shape {
     static constexpr int VW = DPL / 2;                 // dwords per V chunk
 };
 
-// One wave's staged tile: NB blocks of 16 keys.
-template <int D, int NB>
+// Element type of the KV cache: bf16, or OCP FP8 E4M3 with per-tensor scales
+// (dequantised exactly to bf16 in registers: every E4M3 value is a bf16 value).
+constexpr int kKvBf16 = 0;
+constexpr int kKvFp8 = 1;
+
+// Head dims that contraction slot (k-block kb, lane group grp) of QK^T covers:
+// 8 consecutive dims.  The contraction order is free as long as K and Q agree;
+// for E4M3 each lane loads 16 consecutive bytes that feed two k-blocks.
+template <int KV>
+__device__ __forceinline__ constexpr int kslot_dim(int kb, int grp) {
+    return KV == kKvFp8 ? 64 * (kb >> 1) + 16 * grp + 8 * (kb & 1) : 32 * kb + 8 * grp;
+}
+
+// One wave's tile as loaded: NB blocks of 16 keys.
+//   k[blk][w]: key 16*blk + r; bf16: k-block w, dims kslot_dim(w, grp) ..;
+//              E4M3: 16 bytes for k-blocks 2w and 2w + 1.
+//   v[blk][j][c]: key 16*blk + 4*grp + j, dims 16*DPL*c + DPL*r .. (DPL values).
+template <int D, int NB, int KV>
 struct Tile {
-    u32x4_t k[NB][Shape<D>::KB];                       // key 16*blk + r, dims 32*kb + 8*grp ..
-    unsigned int v[NB][4][Shape<D>::VC][Shape<D>::VW]; // key 16*blk + 4*grp + j, dims 16*DPL*c + DPL*r ..
+    static constexpr int KW = KV == kKvFp8 ? Shape<D>::KB / 2 : Shape<D>::KB;  // 16-byte K loads
+    static constexpr int VWL = KV == kKvFp8 ? Shape<D>::VW / 2 : Shape<D>::VW; // V dwords as loaded
+    u32x4_t k[NB][KW];
+    unsigned int v[NB][4][Shape<D>::VC][VWL];
 };
+
+// 4 E4M3 bytes -> 4 bf16 values (exact), packed in two dwords in byte order.
+__device__ __forceinline__ u32x2_t e4m3x4_to_bf16(unsigned int w) {
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return u32x2_t{__builtin_bit_cast(unsigned int, lo), __builtin_bit_cast(unsigned int, hi)};
+}
+
+// The QK^T A operand of k-block kb for block blk of the tile, as bf16.
+template <int D, int NB, int KV>
+__device__ __forceinline__ bf16x8_t k_operand(const Tile<D, NB, KV> &t, int blk, int kb) {
+    if constexpr (KV == kKvFp8) {
+        const u32x4_t raw = t.k[blk][kb >> 1];
+        const u32x2_t a = e4m3x4_to_bf16((kb & 1) ? raw[2] : raw[0]);
+        const u32x2_t b = e4m3x4_to_bf16((kb & 1) ? raw[3] : raw[1]);
+        return __builtin_bit_cast(bf16x8_t, u32x4_t{a[0], a[1], b[0], b[1]});
+    } else {
+        return __builtin_bit_cast(bf16x8_t, t.k[blk][kb]);
+    }
+}
+
+// Dword w (of VW) of V chunk (blk, j, c) as bf16 pairs.
+template <int D, int NB, int KV>
+__device__ __forceinline__ unsigned int v_word(const Tile<D, NB, KV> &t, int blk, int j, int c, int w) {
+    if constexpr (KV == kKvFp8) {
+        return e4m3x4_to_bf16(t.v[blk][j][c][w >> 1])[w & 1];
+    } else {
+        return t.v[blk][j][c][w];
+    }
+}
 
 // Issue the loads of one tile.  `rk` / `rv` cover the rows of this tile's
 // (sequence, kv head) or page, ending at the last valid row; `row0` is the
@@ -171,35 +214,39 @@ constexpr int kNonTemporal = 2;
 // Cache policy of the partial stores: the "sc1" (device scope) bit.
 constexpr int kDeviceScope = 16;
 
-template <int D, int NB, int CPOL>
-__device__ __forceinline__ void load_tile(Tile<D, NB> &t, __amdgpu_buffer_rsrc_t rk,
+template <int D, int NB, int CPOL, int KV>
+__device__ __forceinline__ void load_tile(Tile<D, NB, KV> &t, __amdgpu_buffer_rsrc_t rk,
                                           __amdgpu_buffer_rsrc_t rv, int row0, int r, int grp,
                                           int parts) {
     using S = Shape<D>;
+    using T = Tile<D, NB, KV>;
+    constexpr int EB = KV == kKvFp8 ? 1 : 2;  // bytes per element
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
         const int krow = row0 + 16 * blk + r;
 #pragma unroll
-        for (int kb = 0; kb < S::KB && (parts & kLoadK); ++kb) {
-            const int off = (krow * D + 32 * kb + 8 * grp) * 2;
-            t.k[blk][kb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, CPOL));
+        for (int w = 0; w < T::KW && (parts & kLoadK); ++w) {
+            const int off = KV == kKvFp8 ? krow * D + 64 * w + 16 * grp : (krow * D + kslot_dim<KV>(w, grp)) * 2;
+            t.k[blk][w] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, CPOL));
         }
 #pragma unroll
         for (int j = 0; j < 4 && (parts & kLoadV); ++j) {
             const int vrow = row0 + 16 * blk + 4 * grp + j;
 #pragma unroll
             for (int c = 0; c < S::VC; ++c) {
-                const int off = (vrow * D + 16 * S::DPL * c + S::DPL * r) * 2;
-                if constexpr (S::VW == 4) {
+                const int off = (vrow * D + 16 * S::DPL * c + S::DPL * r) * EB;
+                if constexpr (T::VWL == 4) {
                     u32x4_t x = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, CPOL));
                     t.v[blk][j][c][0] = x[0];
                     t.v[blk][j][c][1] = x[1];
                     t.v[blk][j][c][2] = x[2];
                     t.v[blk][j][c][3] = x[3];
-                } else {
+                } else if constexpr (T::VWL == 2) {
                     u32x2_t x = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, CPOL));
                     t.v[blk][j][c][0] = x[0];
                     t.v[blk][j][c][1] = x[1];
+                } else {
+                    t.v[blk][j][c][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, CPOL);
                 }
             }
         }
@@ -236,8 +283,8 @@ constexpr int kStageStride = D == 64 ? D + 8 : D + 16;
 
 // kPvBf16: V rows of a tile (as loaded: key 16*blk + 4*grp + j, dims
 // 16*DPL*c + DPL*r ..) into the wave's LDS staging buffer.
-template <int D, int NB>
-__device__ __forceinline__ void stage_v(const Tile<D, NB> &t, int r, int grp, unsigned short *stage) {
+template <int D, int NB, int KV>
+__device__ __forceinline__ void stage_v(const Tile<D, NB, KV> &t, int r, int grp, unsigned short *stage) {
     using S = Shape<D>;
     constexpr int RS = kStageStride<D>;
 #pragma unroll
@@ -248,10 +295,10 @@ __device__ __forceinline__ void stage_v(const Tile<D, NB> &t, int r, int grp, un
             for (int c = 0; c < S::VC; ++c) {
                 unsigned short *dst = stage + (16 * blk + 4 * grp + j) * RS + 16 * S::DPL * c + S::DPL * r;
                 if constexpr (S::VW == 4) {
-                    *reinterpret_cast<u32x4_t *>(dst) =
-                        u32x4_t{t.v[blk][j][c][0], t.v[blk][j][c][1], t.v[blk][j][c][2], t.v[blk][j][c][3]};
+                    *reinterpret_cast<u32x4_t *>(dst) = u32x4_t{v_word(t, blk, j, c, 0), v_word(t, blk, j, c, 1),
+                                                                v_word(t, blk, j, c, 2), v_word(t, blk, j, c, 3)};
                 } else {
-                    *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{t.v[blk][j][c][0], t.v[blk][j][c][1]};
+                    *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{v_word(t, blk, j, c, 0), v_word(t, blk, j, c, 1)};
                 }
             }
 }
@@ -260,8 +307,8 @@ __device__ __forceinline__ void stage_v(const Tile<D, NB> &t, int r, int grp, un
 // `t0` in the sequence (keys at or beyond `t_end` masked).  On return
 // sc[blk][i] holds the probability of key 16*blk + 4*grp + i for head r
 // (relative to the new running max) and acc has been rescaled.
-template <int D, int NB>
-__device__ __forceinline__ void qk_softmax(const Tile<D, NB> &t, const bf16x8_t (&qb)[Shape<D>::KB],
+template <int D, int NB, int KV>
+__device__ __forceinline__ void qk_softmax(const Tile<D, NB, KV> &t, const bf16x8_t (&qb)[Shape<D>::KB],
                                            WaveState<D> &st, int t0, int t_end, int grp,
                                            float qk_scale_log2, f32x4_t (&sc)[NB]) {
     using S = Shape<D>;
@@ -270,8 +317,7 @@ __device__ __forceinline__ void qk_softmax(const Tile<D, NB> &t, const bf16x8_t 
         f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < S::KB; ++kb)
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[blk][kb]),
-                                                        qb[kb], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(t, blk, kb), qb[kb], c, 0, 0, 0);
         sc[blk] = c;
     }
     float mx = -INFINITY;
@@ -306,8 +352,8 @@ __device__ __forceinline__ void qk_softmax(const Tile<D, NB> &t, const bf16x8_t 
 }
 
 // PV for one tile with probabilities sc (see qk_softmax).
-template <int D, int NB, int PV>
-__device__ __forceinline__ void pv_tile(const Tile<D, NB> &t, const f32x4_t (&sc)[NB], WaveState<D> &st,
+template <int D, int NB, int PV, int KV>
+__device__ __forceinline__ void pv_tile(const Tile<D, NB, KV> &t, const f32x4_t (&sc)[NB], WaveState<D> &st,
                                         int r, int grp, const unsigned short *stage) {
     using S = Shape<D>;
     constexpr int RS = kStageStride<D>;
@@ -321,7 +367,7 @@ __device__ __forceinline__ void pv_tile(const Tile<D, NB> &t, const f32x4_t (&sc
                 for (int c = 0; c < S::VC; ++c) {
 #pragma unroll
                     for (int e = 0; e < S::DPL; ++e) {
-                        const float vf = bf16_elem(t.v[blk][j][c], e);
+                        const float vf = (e & 1) ? bf16_hi(v_word(t, blk, j, c, e >> 1)) : bf16_lo(v_word(t, blk, j, c, e >> 1));
                         st.acc[c * S::DPL + e] =
                             __builtin_amdgcn_mfma_f32_16x16x4f32(vf, p, st.acc[c * S::DPL + e], 0, 0, 0);
                     }
@@ -357,13 +403,13 @@ __device__ __forceinline__ void pv_tile(const Tile<D, NB> &t, const f32x4_t (&sc
 }
 
 // QK^T, online softmax and PV for one staged tile.
-template <int D, int NB, int PV>
-__device__ __forceinline__ void compute_tile(const Tile<D, NB> &t, const bf16x8_t (&qb)[Shape<D>::KB],
+template <int D, int NB, int PV, int KV>
+__device__ __forceinline__ void compute_tile(const Tile<D, NB, KV> &t, const bf16x8_t (&qb)[Shape<D>::KB],
                                              WaveState<D> &st, int t0, int t_end, int r, int grp,
                                              float qk_scale_log2, unsigned short *stage) {
-    if constexpr (PV == kPvBf16) stage_v<D, NB>(t, r, grp, stage);
+    if constexpr (PV == kPvBf16) stage_v(t, r, grp, stage);
     f32x4_t sc[NB];
-    qk_softmax<D, NB>(t, qb, st, t0, t_end, grp, qk_scale_log2, sc);
+    qk_softmax(t, qb, st, t0, t_end, grp, qk_scale_log2, sc);
     pv_tile<D, NB, PV>(t, sc, st, r, grp, stage);
 }
 
@@ -523,7 +569,7 @@ __device__ __forceinline__ long long share_of(long long x, long long N, long lon
 // through LDS into partial slot `slot` (or straight into `out` when direct).
 // Must be called by all threads of the workgroup; ends with a barrier, after
 // which LDS may be reused.
-template <int D, int NB, bool PAGED, int PV, bool DBUF, int CPOL>
+template <int D, int NB, bool PAGED, int PV, bool DBUF, int CPOL, int KV>
 __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB> &lds, int b, int kvh,
                                               int len, int t_begin, int t_end, size_t slot, bool direct) {
     using S = Shape<D>;
@@ -543,7 +589,7 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
 #pragma unroll
         for (int kb = 0; kb < S::KB; ++kb) {
             u32x4_t x = {0u, 0u, 0u, 0u};
-            if (r < a.G) x = *reinterpret_cast<const u32x4_t *>(qrow + 32 * kb + 8 * grp);
+            if (r < a.G) x = *reinterpret_cast<const u32x4_t *>(qrow + kslot_dim<KV>(kb, grp));
             qb[kb] = __builtin_bit_cast(bf16x8_t, x);
         }
     }
@@ -556,7 +602,8 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
 
     // Resources of the rows a tile reads.  Contiguous: the whole (b, kvh)
     // slab up to len.  Paged: the tile's page up to len (one table read).
-    const size_t slab = (size_t)D;
+    constexpr int EB = KV == kKvFp8 ? 1 : 2;  // bytes per cache element
+    const size_t slab = (size_t)D * EB;       // bytes per row
     // Paged: lane i holds the page of this wave's tile (64*chunk + i), read
     // once per 64 tiles instead of one dependent scalar load per tile.
     int page_vec = 0;
@@ -568,7 +615,7 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
         }
     };
     load_pages(0);
-    auto issue = [&](Tile<D, NB> &tile, int it, int parts) {
+    auto issue = [&](Tile<D, NB, KV> &tile, int it, int parts) {
         const int t0 = t_begin + (wave + kWaves * it) * TT;
         if constexpr (PAGED) {
             if (it > 0 && (it & 63) == 0) load_pages(it >> 6);
@@ -577,14 +624,14 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
             const int page = min(max(__builtin_amdgcn_readlane(page_vec, it & 63), 0), a.num_pages - 1);
             const int rows = min(a.page_size, len - pidx * a.page_size);
             const size_t base = ((size_t)page * a.Hkv + kvh) * (size_t)a.page_size * slab;
-            __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, rows * D * 2, kRsrcWord3);
-            __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, rows * D * 2, kRsrcWord3);
-            load_tile<D, NB, CPOL>(tile, rk, rv, row0, r, grp, parts);
+            __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, rows * D * EB, kRsrcWord3);
+            __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, rows * D * EB, kRsrcWord3);
+            load_tile<D, NB, CPOL, KV>(tile, rk, rv, row0, r, grp, parts);
         } else {
             const size_t base = ((size_t)b * a.Hkv + kvh) * (size_t)a.S_max * slab;
-            __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, len * D * 2, kRsrcWord3);
-            __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, len * D * 2, kRsrcWord3);
-            load_tile<D, NB, CPOL>(tile, rk, rv, t0, r, grp, parts);
+            __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, len * D * EB, kRsrcWord3);
+            __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, len * D * EB, kRsrcWord3);
+            load_tile<D, NB, CPOL, KV>(tile, rk, rv, t0, r, grp, parts);
         }
     };
     auto tile_start = [&](int it) { return t_begin + (wave + kWaves * it) * TT; };
@@ -592,14 +639,14 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
     unsigned short *stage = lds.stage(wave);
     if constexpr (DBUF) {
         // Two tile buffers: the next tile's loads are in flight during this tile's math.
-        Tile<D, NB> buf0, buf1;
+        Tile<D, NB, KV> buf0, buf1;
         if (my_tiles > 0) issue(buf0, 0, kLoadK | kLoadV);
         for (int it = 0; it < my_tiles; it += 2) {
             if (it + 1 < my_tiles) issue(buf1, it + 1, kLoadK | kLoadV);
-            compute_tile<D, NB, PV>(buf0, qb, st, tile_start(it), t_end, r, grp, a.qk_scale_log2, stage);
+            compute_tile<D, NB, PV, KV>(buf0, qb, st, tile_start(it), t_end, r, grp, a.qk_scale_log2, stage);
             if (it + 1 < my_tiles) {
                 if (it + 2 < my_tiles) issue(buf0, it + 2, kLoadK | kLoadV);
-                compute_tile<D, NB, PV>(buf1, qb, st, tile_start(it + 1), t_end, r, grp, a.qk_scale_log2, stage);
+                compute_tile<D, NB, PV, KV>(buf1, qb, st, tile_start(it + 1), t_end, r, grp, a.qk_scale_log2, stage);
             }
         }
     } else {
@@ -607,7 +654,7 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
         // tile's K loads go out once QK^T has consumed K, its V loads once this
         // tile's V is in LDS, so they fly during the rest of the tile's math.
         // Half the registers of the double buffer, so more waves fit per SIMD.
-        Tile<D, NB> buf;
+        Tile<D, NB, KV> buf;
         if (my_tiles > 0) issue(buf, 0, kLoadV | kLoadK);
         for (int it = 0; it < my_tiles; ++it) {
             const bool more = it + 1 < my_tiles;
@@ -616,21 +663,21 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
                 if (it == 0) {
                     // The first tile's K arrives before its V (issued first):
                     // QK^T and the softmax run while V is still in flight.
-                    qk_softmax<D, NB>(buf, qb, st, tile_start(it), t_end, grp, a.qk_scale_log2, sc);
+                    qk_softmax(buf, qb, st, tile_start(it), t_end, grp, a.qk_scale_log2, sc);
                     if (more) issue(buf, it + 1, kLoadK);
-                    stage_v<D, NB>(buf, r, grp, stage);
+                    stage_v(buf, r, grp, stage);
                     if (more) issue(buf, it + 1, kLoadV);
                 } else {
                     // Later tiles: stage V first, so that QK^T covers the LDS
                     // write latency before PV reads the staged V back.
-                    stage_v<D, NB>(buf, r, grp, stage);
+                    stage_v(buf, r, grp, stage);
                     if (more) issue(buf, it + 1, kLoadV);
-                    qk_softmax<D, NB>(buf, qb, st, tile_start(it), t_end, grp, a.qk_scale_log2, sc);
+                    qk_softmax(buf, qb, st, tile_start(it), t_end, grp, a.qk_scale_log2, sc);
                     if (more) issue(buf, it + 1, kLoadK);
                 }
-                pv_tile<D, NB, PV>(buf, sc, st, r, grp, stage);
+                pv_tile<D, NB, PV, KV>(buf, sc, st, r, grp, stage);
             } else {
-                compute_tile<D, NB, PV>(buf, qb, st, tile_start(it), t_end, r, grp, a.qk_scale_log2, stage);
+                compute_tile<D, NB, PV, KV>(buf, qb, st, tile_start(it), t_end, r, grp, a.qk_scale_log2, stage);
                 if (more) issue(buf, it + 1, kLoadK | kLoadV);
             }
         }
@@ -694,6 +741,7 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
             L += sw * lw[w];
             acc += sw * aw[w];
         }
+        if constexpr (KV == kKvFp8) acc *= a.v_scale;  // the partials hold dequantised V sums
         if (direct) {
             *reinterpret_cast<f32x4_t *>(out_rows + (size_t)g * D + d) =
                 L > 0.f ? acc / L : f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -715,7 +763,7 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
     __syncthreads();
 }
 
-template <int D, int NB, bool PAGED, int PV, bool DBUF, int PART, int CPOL>
+template <int D, int NB, bool PAGED, int PV, bool DBUF, int PART, int CPOL, int KV>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEu<D, DBUF>)))
 void gqa_split_kernel(const int32_t *seq_lens, int num_splits, int Hkv, int B, int cap, const SplitArgs args) {
     constexpr int TT = 16 * NB;
@@ -766,7 +814,7 @@ void gqa_split_kernel(const int32_t *seq_lens, int num_splits, int Hkv, int B, i
         while (cur < end) {
             const int take = (int)min((long long)(nb_tiles - off), end - cur);
             const size_t slot = (size_t)blockIdx.x + (size_t)b * a.Hkv + kvh;
-            process_range<D, NB, PAGED, PV, DBUF, CPOL>(a, lds, b, kvh, len, off * TT, min(len, (off + take) * TT),
+            process_range<D, NB, PAGED, PV, DBUF, CPOL, KV>(a, lds, b, kvh, len, off * TT, min(len, (off + take) * TT),
                                                   slot, false);
             cur += take;
             off += take;
@@ -797,7 +845,7 @@ void gqa_split_kernel(const int32_t *seq_lens, int num_splits, int Hkv, int B, i
         const int t_end = min(len, t_begin + a.split_tokens);
         const int nsplit = a.num_splits;
         const bool direct = nsplit == 1;
-        process_range<D, NB, PAGED, PV, DBUF, CPOL>(a, lds, b, kvh, len, t_begin, t_end,
+        process_range<D, NB, PAGED, PV, DBUF, CPOL, KV>(a, lds, b, kvh, len, t_begin, t_end,
                                               (size_t)bk * nsplit + split, direct);
     }
 }
@@ -1088,7 +1136,7 @@ hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const f
 }
 
 template <int D, int NB, bool PAGED>
-hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
+hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, int kv, hipStream_t stream) {
     if constexpr (NB * D > 256) {  // at most 16 KB of K+V (64 * NB * D bytes) per wave tile
         return hipErrorInvalidValue;
     } else {
@@ -1096,29 +1144,38 @@ hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, hipStream
         const int cap = PAGED ? a.max_pages * a.page_size : a.S_max;
         const bool even = plan.partition == kPartitionEven;
         const bool nt = plan.streaming != 0;
-        if (plan.pv_mode == kPvF32) {
-            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionEven, 0>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
-            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionFixed, 0>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
+        };
+        if (kv == kKvFp8) {
+            // The E4M3 cache always runs the default pipeline (bf16 PV, one register tile).
+            if (nt) even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, kNonTemporal, kKvFp8>)
+                         : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, kNonTemporal, kKvFp8>);
+            else even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, 0, kKvFp8>)
+                      : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, 0, kKvFp8>);
+        } else if (plan.pv_mode == kPvF32) {
+            even ? go(gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionEven, 0, kKvBf16>)
+                 : go(gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionFixed, 0, kKvBf16>);
         } else if (plan.double_buffer) {
-            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionEven, 0>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
-            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionFixed, 0>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
+            even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionEven, 0, kKvBf16>)
+                 : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionFixed, 0, kKvBf16>);
         } else if (nt) {
-            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, kNonTemporal>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
-            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, kNonTemporal>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
+            even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, kNonTemporal, kKvBf16>)
+                 : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, kNonTemporal, kKvBf16>);
         } else {
-            if (even) hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, 0>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
-            else hipLaunchKernelGGL((gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, 0>), grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
+            even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, 0, kKvBf16>)
+                 : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, 0, kKvBf16>);
         }
         return hipGetLastError();
     }
 }
 
 template <int D, bool PAGED>
-hipError_t launch_split(const gqa_plan_t &plan, const SplitArgs &a, hipStream_t stream) {
+hipError_t launch_split(const gqa_plan_t &plan, const SplitArgs &a, int kv, hipStream_t stream) {
     switch (plan.tile_tokens) {
-        case 16: return launch_split_nb<D, 1, PAGED>(plan, a, stream);
-        case 32: return launch_split_nb<D, 2, PAGED>(plan, a, stream);
-        case 64: return launch_split_nb<D, 4, PAGED>(plan, a, stream);
+        case 16: return launch_split_nb<D, 1, PAGED>(plan, a, kv, stream);
+        case 32: return launch_split_nb<D, 2, PAGED>(plan, a, kv, stream);
+        case 64: return launch_split_nb<D, 4, PAGED>(plan, a, kv, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1126,7 +1183,15 @@ hipError_t launch_split(const gqa_plan_t &plan, const SplitArgs &a, hipStream_t 
 constexpr int kPhaseSplit = 1;
 constexpr int kPhaseCombine = 2;
 
-gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, void *workspace,
+// Element type and per-tensor scales of the cache of one call.
+struct KvSpec {
+    int type;       // kKvBf16 or kKvFp8
+    float k_scale;  // E4M3 only
+    float v_scale;
+};
+constexpr KvSpec kBf16Cache{kKvBf16, 1.f, 1.f};
+
+gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, int kv, void *workspace,
                  hipStream_t stream, int phases) {
     if (!plan.direct) {
         WorkspaceLayout w = workspace_layout(a.Hq, a.Hkv, D, plan.slots);
@@ -1137,9 +1202,9 @@ gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, void *
     hipError_t e = hipSuccess;
     if (phases & kPhaseSplit) {
         switch (D) {
-            case 64: e = paged ? launch_split<64, true>(plan, a, stream) : launch_split<64, false>(plan, a, stream); break;
-            case 128: e = paged ? launch_split<128, true>(plan, a, stream) : launch_split<128, false>(plan, a, stream); break;
-            case 256: e = paged ? launch_split<256, true>(plan, a, stream) : launch_split<256, false>(plan, a, stream); break;
+            case 64: e = paged ? launch_split<64, true>(plan, a, kv, stream) : launch_split<64, false>(plan, a, kv, stream); break;
+            case 128: e = paged ? launch_split<128, true>(plan, a, kv, stream) : launch_split<128, false>(plan, a, kv, stream); break;
+            case 256: e = paged ? launch_split<256, true>(plan, a, kv, stream) : launch_split<256, false>(plan, a, kv, stream); break;
             default: return GQA_ERR_UNSUPPORTED;
         }
         if (e != hipSuccess) return GQA_ERR_HIP;
@@ -1278,13 +1343,14 @@ namespace {
 
 gqa_status_t decode_contig(const void *q, const void *k_cache, const void *v_cache,
                            const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
-                           float scale, float *out, void *workspace, size_t workspace_bytes,
-                           int num_splits, hipStream_t stream, int phases) {
+                           float scale, const KvSpec &kv, float *out, void *workspace,
+                           size_t workspace_bytes, int num_splits, hipStream_t stream, int phases) {
     gqa_status_t s = check_common(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, scale);
     if (s != GQA_OK) return s;
-    if (S_max < 0 || num_splits < 0) return GQA_ERR_SHAPE;
+    if (S_max < 0 || num_splits < 0 || !isfinite(kv.k_scale) || !isfinite(kv.v_scale)) return GQA_ERR_SHAPE;
     if (B == 0) return GQA_OK;
-    if (((int64_t)S_max + 64) * D * 2 > INT32_MAX) return GQA_ERR_SHAPE;  // 32-bit buffer offsets
+    const int eb = kv.type == kKvFp8 ? 1 : 2;
+    if (((int64_t)S_max + 64) * D * eb > INT32_MAX) return GQA_ERR_SHAPE;  // 32-bit buffer offsets
     if (workspace != nullptr && misaligned(workspace, 16)) return GQA_ERR_ALIGN;
     gqa_plan_t plan;
     s = plan_for_call(B, Hq, Hkv, D, S_max, 0, num_splits, &plan);
@@ -1294,31 +1360,33 @@ gqa_status_t decode_contig(const void *q, const void *k_cache, const void *v_cac
     if (B == 0) return GQA_OK;
     SplitArgs a{};
     a.q = static_cast<const uint16_t *>(q);
-    a.k = static_cast<const uint16_t *>(k_cache);
-    a.v = static_cast<const uint16_t *>(v_cache);
+    a.k = static_cast<const unsigned char *>(k_cache);
+    a.v = static_cast<const unsigned char *>(v_cache);
     a.seq_lens = seq_lens;
     a.out = out;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
     a.S_max = S_max;
     a.num_splits = plan.num_splits;
     a.split_tokens = plan.split_tokens;
-    a.qk_scale_log2 = scale * 1.4426950408889634f;
-    return run(plan, a, D, false, workspace, stream, phases);
+    a.qk_scale_log2 = scale * kv.k_scale * 1.4426950408889634f;
+    a.v_scale = kv.v_scale;
+    return run(plan, a, D, false, kv.type, workspace, stream, phases);
 }
 
 gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
                           const int32_t *seq_lens, const int32_t *page_table, int B, int Hq,
                           int Hkv, int D, int page_size, int num_pages, int max_pages,
-                          float scale, float *out, void *workspace, size_t workspace_bytes,
-                          int num_splits, hipStream_t stream, int phases) {
+                          float scale, const KvSpec &kv, float *out, void *workspace,
+                          size_t workspace_bytes, int num_splits, hipStream_t stream, int phases) {
     gqa_status_t s = check_common(q, k_pool, v_pool, seq_lens, out, B, Hq, Hkv, D, scale);
     if (s != GQA_OK) return s;
+    if (!isfinite(kv.k_scale) || !isfinite(kv.v_scale)) return GQA_ERR_SHAPE;
     if (B == 0) return (page_size > 0 && page_size % 16 == 0) ? GQA_OK : GQA_ERR_UNSUPPORTED;
     if (page_table == nullptr) return GQA_ERR_NULL;
     if (misaligned(page_table, 4)) return GQA_ERR_ALIGN;
     if (page_size <= 0 || num_pages <= 0 || max_pages <= 0 || num_splits < 0) return GQA_ERR_SHAPE;
     if (page_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
-    if ((int64_t)max_pages * page_size > INT32_MAX || (int64_t)page_size * D * 2 > INT32_MAX)
+    if ((int64_t)max_pages * page_size > INT32_MAX || (int64_t)page_size * D * 2 > INT32_MAX)  // 32-bit offsets
         return GQA_ERR_SHAPE;
     if (workspace != nullptr && misaligned(workspace, 16)) return GQA_ERR_ALIGN;
     gqa_plan_t plan;
@@ -1329,8 +1397,8 @@ gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
     if (B == 0) return GQA_OK;
     SplitArgs a{};
     a.q = static_cast<const uint16_t *>(q);
-    a.k = static_cast<const uint16_t *>(k_pool);
-    a.v = static_cast<const uint16_t *>(v_pool);
+    a.k = static_cast<const unsigned char *>(k_pool);
+    a.v = static_cast<const unsigned char *>(v_pool);
     a.seq_lens = seq_lens;
     a.page_table = page_table;
     a.out = out;
@@ -1340,8 +1408,9 @@ gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
     a.num_pages = num_pages;
     a.num_splits = plan.num_splits;
     a.split_tokens = plan.split_tokens;
-    a.qk_scale_log2 = scale * 1.4426950408889634f;
-    return run(plan, a, D, true, workspace, stream, phases);
+    a.qk_scale_log2 = scale * kv.k_scale * 1.4426950408889634f;
+    a.v_scale = kv.v_scale;
+    return run(plan, a, D, true, kv.type, workspace, stream, phases);
 }
 
 }  // namespace
@@ -1352,16 +1421,16 @@ gqa_status_t gqa_decode(const void *q, const void *k_cache, const void *v_cache,
                         const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
                         float scale, float *out, void *workspace, size_t workspace_bytes,
                         int num_splits, hipStream_t stream) {
-    return decode_contig(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale, out, workspace,
-                         workspace_bytes, num_splits, stream, kPhaseSplit | kPhaseCombine);
+    return decode_contig(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale, kBf16Cache, out,
+                         workspace, workspace_bytes, num_splits, stream, kPhaseSplit | kPhaseCombine);
 }
 
 gqa_status_t gqa_decode_partials(const void *q, const void *k_cache, const void *v_cache,
                                  const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
                                  float scale, float *out, void *workspace, size_t workspace_bytes,
                                  int num_splits, hipStream_t stream) {
-    return decode_contig(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale, out, workspace,
-                         workspace_bytes, num_splits, stream, kPhaseSplit);
+    return decode_contig(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale, kBf16Cache, out,
+                         workspace, workspace_bytes, num_splits, stream, kPhaseSplit);
 }
 
 gqa_status_t gqa_paged_decode(const void *q, const void *k_pool, const void *v_pool,
@@ -1370,8 +1439,8 @@ gqa_status_t gqa_paged_decode(const void *q, const void *k_pool, const void *v_p
                               float scale, float *out, void *workspace, size_t workspace_bytes,
                               int num_splits, hipStream_t stream) {
     return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, Hq, Hkv, D, page_size, num_pages,
-                        max_pages, scale, out, workspace, workspace_bytes, num_splits, stream,
-                        kPhaseSplit | kPhaseCombine);
+                        max_pages, scale, kBf16Cache, out, workspace, workspace_bytes, num_splits,
+                        stream, kPhaseSplit | kPhaseCombine);
 }
 
 gqa_status_t gqa_paged_decode_partials(const void *q, const void *k_pool, const void *v_pool,
@@ -1380,8 +1449,49 @@ gqa_status_t gqa_paged_decode_partials(const void *q, const void *k_pool, const 
                                        int max_pages, float scale, float *out, void *workspace,
                                        size_t workspace_bytes, int num_splits, hipStream_t stream) {
     return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, Hq, Hkv, D, page_size, num_pages,
-                        max_pages, scale, out, workspace, workspace_bytes, num_splits, stream,
-                        kPhaseSplit);
+                        max_pages, scale, kBf16Cache, out, workspace, workspace_bytes, num_splits,
+                        stream, kPhaseSplit);
+}
+
+gqa_status_t gqa_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
+                            float scale, float k_scale, float v_scale, float *out, void *workspace,
+                            size_t workspace_bytes, int num_splits, hipStream_t stream) {
+    return decode_contig(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale,
+                         KvSpec{kKvFp8, k_scale, v_scale}, out, workspace, workspace_bytes, num_splits,
+                         stream, kPhaseSplit | kPhaseCombine);
+}
+
+gqa_status_t gqa_paged_decode_fp8(const void *q, const void *k_pool, const void *v_pool,
+                                  const int32_t *seq_lens, const int32_t *page_table, int B, int Hq,
+                                  int Hkv, int D, int page_size, int num_pages, int max_pages,
+                                  float scale, float k_scale, float v_scale, float *out,
+                                  void *workspace, size_t workspace_bytes, int num_splits,
+                                  hipStream_t stream) {
+    return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, Hq, Hkv, D, page_size, num_pages,
+                        max_pages, scale, KvSpec{kKvFp8, k_scale, v_scale}, out, workspace,
+                        workspace_bytes, num_splits, stream, kPhaseSplit | kPhaseCombine);
+}
+
+gqa_status_t gqa_decode_fp8_partials(const void *q, const void *k_cache, const void *v_cache,
+                                     const int32_t *seq_lens, int B, int Hq, int Hkv, int D,
+                                     int S_max, float scale, float k_scale, float v_scale, float *out,
+                                     void *workspace, size_t workspace_bytes, int num_splits,
+                                     hipStream_t stream) {
+    return decode_contig(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale,
+                         KvSpec{kKvFp8, k_scale, v_scale}, out, workspace, workspace_bytes, num_splits,
+                         stream, kPhaseSplit);
+}
+
+gqa_status_t gqa_paged_decode_fp8_partials(const void *q, const void *k_pool, const void *v_pool,
+                                           const int32_t *seq_lens, const int32_t *page_table, int B,
+                                           int Hq, int Hkv, int D, int page_size, int num_pages,
+                                           int max_pages, float scale, float k_scale, float v_scale,
+                                           float *out, void *workspace, size_t workspace_bytes,
+                                           int num_splits, hipStream_t stream) {
+    return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, Hq, Hkv, D, page_size, num_pages,
+                        max_pages, scale, KvSpec{kKvFp8, k_scale, v_scale}, out, workspace,
+                        workspace_bytes, num_splits, stream, kPhaseSplit);
 }
 
 gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, const int32_t *seq_lens,
@@ -1413,7 +1523,7 @@ gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, c
     } else {
         a.S_max = max_seq_len;
     }
-    return run(plan, a, D, page_size > 0, const_cast<void *>(workspace), stream, kPhaseCombine);
+    return run(plan, a, D, page_size > 0, kKvBf16, const_cast<void *>(workspace), stream, kPhaseCombine);
 }
 
 const char *gqa_status_string(gqa_status_t status) {

@@ -20,7 +20,8 @@
  * Conventions shared by every call:
  *   - All tensor pointers are caller-owned DEVICE memory.  q, k, v, out and
  *     workspace must be 16-byte aligned; seq_lens and page_table 4-byte
- *     aligned.  bf16 tensors are passed as raw 16-bit patterns.
+ *     aligned.  bf16 tensors are passed as raw 16-bit patterns (E4M3 caches
+ *     as raw bytes, see gqa_decode_fp8).
  *   - Calls only enqueue work on `stream` (0 = the null stream): they never
  *     synchronise, never allocate and keep no state besides a cached CU count
  *     per device.  Outputs are ready when the stream reaches them.
@@ -165,6 +166,49 @@ gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes,
                                 const int32_t *seq_lens, int B, int Hq, int Hkv, int head_dim,
                                 int max_seq_len, int page_size, int num_splits, float *out,
                                 hipStream_t stream);
+
+/*
+ * FP8 (E4M3) KV cache: the quantized pool of sparkinfer PR #874, section
+ * "Cost and fallbacks" (an int8 pool dequantised before use), in the format
+ * native to gfx950.  k_cache / v_cache (or the pools) hold OCP FP8 E4M3 bytes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; subnormals at
+ * exponent 0; 0x7F / 0xFF are NaN) in the layouts of gqa_decode /
+ * gqa_paged_decode with one byte per element, 16-byte aligned.  An element's
+ * value is k_scale (resp. v_scale) times its E4M3 value; both scales must be
+ * finite.  Every E4M3 value is exactly a bf16 value, so K and V enter the
+ * same bf16 MFMA contractions as the bf16 cache; k_scale is folded into the
+ * softmax scale and v_scale into the partials.  All other arguments, the
+ * workspace (gqa_decode_workspace_bytes with the same shapes) and the
+ * behaviour are those of gqa_decode / gqa_paged_decode.
+ */
+gqa_status_t gqa_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *seq_lens, int B, int Hq, int Hkv, int head_dim,
+                            int S_max, float scale, float k_scale, float v_scale, float *out,
+                            void *workspace, size_t workspace_bytes, int num_splits,
+                            hipStream_t stream);
+
+gqa_status_t gqa_paged_decode_fp8(const void *q, const void *k_pool, const void *v_pool,
+                                  const int32_t *seq_lens, const int32_t *page_table, int B, int Hq,
+                                  int Hkv, int head_dim, int page_size, int num_pages, int max_pages,
+                                  float scale, float k_scale, float v_scale, float *out,
+                                  void *workspace, size_t workspace_bytes, int num_splits,
+                                  hipStream_t stream);
+
+/* The split kernel of gqa_decode_fp8 / gqa_paged_decode_fp8 alone (see the
+ * *_partials entry points above); gqa_decode_combine folds their partials. */
+gqa_status_t gqa_decode_fp8_partials(const void *q, const void *k_cache, const void *v_cache,
+                                     const int32_t *seq_lens, int B, int Hq, int Hkv, int head_dim,
+                                     int S_max, float scale, float k_scale, float v_scale, float *out,
+                                     void *workspace, size_t workspace_bytes, int num_splits,
+                                     hipStream_t stream);
+
+gqa_status_t gqa_paged_decode_fp8_partials(const void *q, const void *k_pool, const void *v_pool,
+                                           const int32_t *seq_lens, const int32_t *page_table, int B,
+                                           int Hq, int Hkv, int head_dim, int page_size,
+                                           int num_pages, int max_pages, float scale,
+                                           float k_scale, float v_scale, float *out,
+                                           void *workspace, size_t workspace_bytes,
+                                           int num_splits, hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char *gqa_status_string(gqa_status_t status);

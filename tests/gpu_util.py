@@ -20,6 +20,10 @@ def dev_bf16(a: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
 
 
+def dev_u8(a: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(device)
+
+
 def dev_i32(a: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
 
@@ -30,13 +34,23 @@ class DeviceCase:
     def __init__(self, case: W.Case, device="cuda"):
         self.case = case
         self.q = dev_bf16(case.q, device)
-        self.k = dev_bf16(case.k, device)
-        self.v = dev_bf16(case.v, device)
+        cache = dev_u8 if case.kv == "fp8" else dev_bf16
+        self.k = cache(case.k, device)
+        self.v = cache(case.v, device)
         self.seq_lens = dev_i32(case.seq_lens, device)
         self.page_table = dev_i32(case.page_table, device) if case.paged else None
 
     def run(self, num_splits=0, out=None, workspace=None, stream=None) -> torch.Tensor:
         c = self.case
+        if c.kv == "fp8":
+            if c.paged:
+                return gd.gqa_paged_decode_fp8(self.q, self.k, self.v, self.seq_lens,
+                                               self.page_table, c.scale, c.k_scale, c.v_scale,
+                                               out=out, workspace=workspace,
+                                               num_splits=num_splits, stream=stream)
+            return gd.gqa_decode_fp8(self.q, self.k, self.v, self.seq_lens, c.scale, c.k_scale,
+                                     c.v_scale, out=out, workspace=workspace,
+                                     num_splits=num_splits, stream=stream)
         if c.paged:
             return gd.gqa_paged_decode(self.q, self.k, self.v, self.seq_lens, self.page_table,
                                        c.scale, out=out, workspace=workspace,
@@ -52,6 +66,12 @@ class DeviceCase:
 
 def oracle_out(case: W.Case) -> np.ndarray:
     import oracle
+    if case.kv == "fp8":
+        if case.paged:
+            return oracle.paged_decode_fp8(case.q, case.k, case.v, case.seq_lens, case.page_table,
+                                           case.scale, case.k_scale, case.v_scale)
+        return oracle.decode_fp8(case.q, case.k, case.v, case.seq_lens, case.scale, case.k_scale,
+                                 case.v_scale)
     if case.paged:
         return oracle.paged_decode(case.q, case.k, case.v, case.seq_lens, case.page_table,
                                    case.scale)

@@ -217,3 +217,35 @@ def test_combine_rejects(lib, args, code):
     assert lib.gqa_decode_combine(kw["ws"], kw["ws_bytes"], kw["lens"], kw["B"], kw["Hq"],
                                   kw["Hkv"], kw["D"], kw["cap"], kw["ps"], kw["splits"], kw["out"],
                                   None) == code
+
+
+# ---- the E4M3 cache entry points: the same checks, plus finite per-tensor scales
+def call_decode_fp8(lib, q=A, k=A, v=A, lens=A, B=1, Hq=8, Hkv=2, D=128, S=64, scale=0.1, ks=1.0,
+                    vs=1.0, out=A, ws=A, ws_bytes=1 << 30, splits=2):
+    return lib.gqa_decode_fp8(q, k, v, lens, B, Hq, Hkv, D, S, scale, ks, vs, out, ws, ws_bytes,
+                              splits, None)
+
+
+def call_paged_fp8(lib, q=A, k=A, v=A, lens=A, table=A, B=1, Hq=8, Hkv=2, D=128, ps=32, P=10, mp=4,
+                   scale=0.1, ks=1.0, vs=1.0, out=A, ws=A, ws_bytes=1 << 30, splits=2):
+    return lib.gqa_paged_decode_fp8(q, k, v, lens, table, B, Hq, Hkv, D, ps, P, mp, scale, ks, vs,
+                                    out, ws, ws_bytes, splits, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), 1), (dict(v=None), 1), (dict(lens=None), 1), (dict(out=None), 1),
+    (dict(ks=float("nan")), 2), (dict(vs=float("inf")), 2), (dict(ks=float("-inf")), 2),
+    (dict(scale=float("nan")), 2), (dict(S=1 << 30), 2), (dict(Hq=9), 2),
+    (dict(D=96), 3), (dict(k=A + 8), 4), (dict(v=A + 1), 4), (dict(ws_bytes=16), 5),
+    (dict(B=0, q=None, k=None, v=None, lens=None, out=None, ws=None), 0),
+])
+def test_decode_fp8_rejects(lib, kw, code):
+    assert call_decode_fp8(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(table=None), 1), (dict(vs=float("nan")), 2), (dict(ps=0), 2), (dict(ps=24), 3),
+    (dict(table=A + 2), 4), (dict(ws_bytes=0), 5),
+])
+def test_paged_decode_fp8_rejects(lib, kw, code):
+    assert call_paged_fp8(lib, **kw) == code

@@ -284,5 +284,31 @@ WORKLOADS = {
 HEADLINE = "gqa6_d256_ctx4096"
 
 
-def make(name: str, seed: int = 0) -> Case:
-    return WORKLOADS[name](seed)
+# per-tensor scales of the E4M3 form of each workload: 1/16 keeps N(0,1) values well inside the
+# format's range; the peaky keys (x8) take 1/8
+FP8_SCALES = {"long_gqa8_d128_ctx128k_peaky": (1 / 8, 1 / 16)}
+
+
+def to_fp8(case: Case, k_scale: float = 1 / 16, v_scale: float = 1 / 16) -> Case:
+    """The same call over an E4M3 cache: K and V (bf16 values) divided by their scale and rounded
+    to the nearest E4M3 value; q, lengths and page table unchanged."""
+    def enc(bits, scale):
+        out = np.empty(bits.shape, np.uint8)
+        src, dst = bits.reshape(-1), out.reshape(-1)
+        step = 1 << 22
+        for i in range(0, src.size, step):
+            dst[i:i + step] = f32_to_e4m3_bytes(bf16_bits_to_f32(src[i:i + step]) / np.float32(scale))
+        return out
+    return dataclasses.replace(case, name="fp8_" + case.name, k=enc(case.k, k_scale),
+                               v=enc(case.v, v_scale), kv="fp8", k_scale=float(np.float32(k_scale)),
+                               v_scale=float(np.float32(v_scale)))
+
+
+def make(name: str, seed: int = 0, kv: str = "bf16") -> Case:
+    """A named workload; kv="fp8" gives its E4M3-cache form (see to_fp8)."""
+    case = WORKLOADS[name](seed)
+    if kv == "fp8":
+        return to_fp8(case, *FP8_SCALES.get(name, (1 / 16, 1 / 16)))
+    if kv != "bf16":
+        raise ValueError(f"unknown cache type {kv!r}")
+    return case
