@@ -58,9 +58,12 @@ def load(path: str | None = None):
     lib.oracle_decode_fp8.argtypes = [u16p, u8p, u8p, i32p, ci, ci, ci, ci, ci, cf, cf, cf, ci, f64p]
     lib.oracle_paged_decode_fp8.argtypes = [u16p, u8p, u8p, i32p, i32p, ci, ci, ci, ci, ci, ci, ci,
                                             cf, cf, cf, ci, f64p]
+    lib.oracle_decode_mq.argtypes = [u16p, u16p, u16p, i32p, ci, ci, ci, ci, ci, ci, cf, ci, f64p]
+    lib.oracle_paged_decode_mq.argtypes = [u16p, u16p, u16p, i32p, i32p, ci, ci, ci, ci, ci, ci,
+                                           ci, ci, cf, ci, f64p]
     for fn in (lib.oracle_decode, lib.oracle_decode_split, lib.oracle_paged_decode,
                lib.oracle_paged_decode_split, lib.oracle_max_threads, lib.oracle_decode_fp8,
-               lib.oracle_paged_decode_fp8):
+               lib.oracle_paged_decode_fp8, lib.oracle_decode_mq, lib.oracle_paged_decode_mq):
         fn.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ci]
     lib.oracle_set_threads.restype = None
@@ -176,6 +179,47 @@ def paged_decode_fp8(q, k_pool, v_pool, seq_lens, page_table, scale, k_scale, v_
                                      _ptr(out, ctypes.c_double))
     if rc != 0:
         raise ValueError(f"oracle_paged_decode_fp8 failed with code {rc}")
+    return out
+
+
+def decode_mq(q, k, v, seq_lens, scale, *, chunk: int = 0, lib=None) -> np.ndarray:
+    """Multi-query decode, contiguous bf16 cache: q [B,M,Hq,D]; query i of sequence b attends
+    to keys 0 .. len-M+i.  Returns [B,M,Hq,D]."""
+    lib = lib or load()
+    q, k, v, seq_lens = _u16(q), _u16(k), _u16(v), _i32(seq_lens)
+    B, M, Hq, D = q.shape
+    Bk, Hkv, S_max, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D or seq_lens.shape != (B,):
+        raise ValueError("shape mismatch")
+    out = np.empty((B, M, Hq, D), dtype=np.float64)
+    rc = lib.oracle_decode_mq(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                              _ptr(v, ctypes.c_uint16), _ptr(seq_lens, ctypes.c_int32), B, M, Hq,
+                              Hkv, D, S_max, ctypes.c_float(scale), int(chunk),
+                              _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle_decode_mq failed with code {rc}")
+    return out
+
+
+def paged_decode_mq(q, k_pool, v_pool, seq_lens, page_table, scale, *, chunk: int = 0,
+                    lib=None) -> np.ndarray:
+    """Multi-query decode over a paged bf16 cache: q [B,M,Hq,D]."""
+    lib = lib or load()
+    q, k_pool, v_pool = _u16(q), _u16(k_pool), _u16(v_pool)
+    seq_lens, page_table = _i32(seq_lens), _i32(page_table)
+    B, M, Hq, D = q.shape
+    P, Hkv, ps, Dk = k_pool.shape
+    if v_pool.shape != k_pool.shape or Dk != D or seq_lens.shape != (B,) or \
+            page_table.ndim != 2 or page_table.shape[0] != B:
+        raise ValueError("shape mismatch")
+    out = np.empty((B, M, Hq, D), dtype=np.float64)
+    rc = lib.oracle_paged_decode_mq(_ptr(q, ctypes.c_uint16), _ptr(k_pool, ctypes.c_uint16),
+                                    _ptr(v_pool, ctypes.c_uint16), _ptr(seq_lens, ctypes.c_int32),
+                                    _ptr(page_table, ctypes.c_int32), B, M, Hq, Hkv, D, ps, P,
+                                    page_table.shape[1], ctypes.c_float(scale), int(chunk),
+                                    _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle_paged_decode_mq failed with code {rc}")
     return out
 
 

@@ -36,6 +36,15 @@
  * E4M3 value of the byte (sign bit, 4-bit exponent with bias 7, 3-bit
  * mantissa; exponent 0 is subnormal, m/8 * 2^-6; byte 0x7F / 0xFF is NaN).
  *
+ * Multi-query decode (speculative verification of M drafted tokens, the
+ * block of the sparkinfer PR #874 speculative-decode report, section
+ * "ok"; causal masking as in the prefill kernel of the AstrAI csrc commit
+ * log): each sequence carries M query tokens, the last M positions of the
+ * sequence, whose keys and values are already in the cache.  Query i
+ * (0-based) attends to the keys 0 .. len - M + i, so row (b, i, h) is the
+ * single-query definition over the first n_i = len - M + i + 1 keys (a row
+ * with n_i <= 0 is zero).  q and out are [B][M][Hq][D].
+ *
  * Cache layouts (the pages fix only the index order K[b, h/G, t]):
  *   contiguous: K, V are [B][Hkv][S_max][D]
  *   paged:      K, V pools are [num_pages][Hkv][page_size][D]; token t of
@@ -141,9 +150,9 @@ static void range_stats(const kv_layout *L, const uint16_t *q, int b, int kvh, i
  *     out = (sum_i w_i acc_i) / (sum_i w_i l_i),   i ascending.
  */
 static int decode_all(const kv_layout *L, const uint16_t *q, const int32_t *seq_lens, int B,
-                      int Hq, double scale, int chunk, double *out) {
+                      int M, int Hq, double scale, int chunk, double *out) {
     const int Hkv = L->Hkv, D = L->D;
-    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return 1;
+    if (B < 0 || M <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return 1;
     const int G = Hq / Hkv;
     int maxlen = 0;
     for (int b = 0; b < B; ++b) {
@@ -161,13 +170,14 @@ static int decode_all(const kv_layout *L, const uint16_t *q, const int32_t *seq_
             failed = 1;
         } else {
 #pragma omp for schedule(dynamic, 1)
-            for (long long bh = 0; bh < (long long)B * Hq; ++bh) {
-                const int b = (int)(bh / Hq), h = (int)(bh % Hq);
+            for (long long row = 0; row < (long long)B * M * Hq; ++row) {
+                const int b = (int)(row / ((long long)M * Hq));
+                const int i = (int)(row / Hq % M), h = (int)(row % Hq);
                 const int kvh = h / G;
-                const int n = seq_lens[b];
-                const uint16_t *qrow = q + ((size_t)b * Hq + h) * (size_t)D;
-                double *o = out + ((size_t)b * Hq + h) * (size_t)D;
-                if (n == 0) {
+                const int n = seq_lens[b] - M + i + 1;     /* keys this query row attends to */
+                const uint16_t *qrow = q + (((size_t)b * M + i) * Hq + h) * (size_t)D;
+                double *o = out + (((size_t)b * M + i) * Hq + h) * (size_t)D;
+                if (n <= 0) {
                     for (int d = 0; d < D; ++d) o[d] = 0.0;
                     continue;
                 }
@@ -212,7 +222,7 @@ int oracle_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
     kv_layout L = {k, v, NULL, Hkv, D, S_max, 0, 0, 0, 1.0, 1.0};
     for (int b = 0; b < B; ++b)
         if (seq_lens[b] > S_max) return 2;
-    return decode_all(&L, q, seq_lens, B, Hq, (double)scale, 0, out);
+    return decode_all(&L, q, seq_lens, B, 1, Hq, (double)scale, 0, out);
 }
 
 int oracle_decode_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -222,7 +232,7 @@ int oracle_decode_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     if (chunk <= 0) return 1;
     for (int b = 0; b < B; ++b)
         if (seq_lens[b] > S_max) return 2;
-    return decode_all(&L, q, seq_lens, B, Hq, (double)scale, chunk, out);
+    return decode_all(&L, q, seq_lens, B, 1, Hq, (double)scale, chunk, out);
 }
 
 int oracle_paged_decode(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
@@ -239,7 +249,7 @@ int oracle_paged_decode(const uint16_t *q, const uint16_t *k_pool, const uint16_
             if (p < 0 || p >= num_pages) return 2;
         }
     }
-    return decode_all(&L, q, seq_lens, B, Hq, (double)scale, 0, out);
+    return decode_all(&L, q, seq_lens, B, 1, Hq, (double)scale, 0, out);
 }
 
 int oracle_paged_decode_split(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
@@ -256,7 +266,7 @@ int oracle_paged_decode_split(const uint16_t *q, const uint16_t *k_pool, const u
             if (p < 0 || p >= num_pages) return 2;
         }
     }
-    return decode_all(&L, q, seq_lens, B, Hq, (double)scale, chunk, out);
+    return decode_all(&L, q, seq_lens, B, 1, Hq, (double)scale, chunk, out);
 }
 
 /* The same over an E4M3 cache with per-tensor scales (chunk > 0: split mode). */
@@ -266,7 +276,7 @@ int oracle_decode_fp8(const uint16_t *q, const uint8_t *k, const uint8_t *v, con
     kv_layout L = {k, v, NULL, Hkv, D, S_max, 0, 0, 1, (double)k_scale, (double)v_scale};
     for (int b = 0; b < B; ++b)
         if (seq_lens[b] > S_max) return 2;
-    return decode_all(&L, q, seq_lens, B, Hq, (double)scale, chunk, out);
+    return decode_all(&L, q, seq_lens, B, 1, Hq, (double)scale, chunk, out);
 }
 
 int oracle_paged_decode_fp8(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
@@ -284,7 +294,34 @@ int oracle_paged_decode_fp8(const uint16_t *q, const uint8_t *k_pool, const uint
             if (p < 0 || p >= num_pages) return 2;
         }
     }
-    return decode_all(&L, q, seq_lens, B, Hq, (double)scale, chunk, out);
+    return decode_all(&L, q, seq_lens, B, 1, Hq, (double)scale, chunk, out);
+}
+
+/* Multi-query decode over a bf16 cache: q and out are [B][M][Hq][D]. */
+int oracle_decode_mq(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     const int32_t *seq_lens, int B, int M, int Hq, int Hkv, int D, int S_max,
+                     float scale, int chunk, double *out) {
+    kv_layout L = {k, v, NULL, Hkv, D, S_max, 0, 0, 0, 1.0, 1.0};
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] > S_max) return 2;
+    return decode_all(&L, q, seq_lens, B, M, Hq, (double)scale, chunk, out);
+}
+
+int oracle_paged_decode_mq(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                           const int32_t *seq_lens, const int32_t *page_table, int B, int M, int Hq,
+                           int Hkv, int D, int page_size, int num_pages, int max_pages, float scale,
+                           int chunk, double *out) {
+    kv_layout L = {k_pool, v_pool, page_table, Hkv, D, 0, page_size, max_pages, 0, 1.0, 1.0};
+    if (page_size <= 0 || max_pages < 0) return 1;
+    for (int b = 0; b < B; ++b) {
+        if (seq_lens[b] > page_size * max_pages) return 2;
+        int used = (seq_lens[b] + page_size - 1) / page_size;
+        for (int i = 0; i < used; ++i) {
+            int p = page_table[(size_t)b * max_pages + i];
+            if (p < 0 || p >= num_pages) return 2;
+        }
+    }
+    return decode_all(&L, q, seq_lens, B, M, Hq, (double)scale, chunk, out);
 }
 
 /* Threads the OpenMP runtime will use for the next call (1 without OpenMP). */

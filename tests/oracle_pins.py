@@ -342,10 +342,48 @@ def pin_fp8_split_invariance(lib):
         _close(got, ref, what=f"fp8 split chunk={chunk}")
 
 
+# --------------------------------------------------------------------- multi-query rows
+def pin_mq_rows_are_single_query_calls(lib):
+    """Row (b, i) of a multi-query call is exactly the single-query call of query i over the
+    first len - M + i + 1 keys (the causal limit), for contiguous and paged caches."""
+    c = W.mq_case(3, 4, 8, 2, 64, 40, seq_lens=[40, 4, 21], seed=75)
+    got = oracle.decode_mq(c.q, c.k, c.v, c.seq_lens, c.scale, lib=lib)
+    for b in range(c.B):
+        for i in range(c.M):
+            n = int(c.seq_lens[b]) - c.M + i + 1
+            ref = oracle.decode(c.q[b:b + 1, i], c.k[b:b + 1], c.v[b:b + 1],
+                                np.array([n], np.int32), c.scale, lib=lib)
+            assert np.array_equal(got[b, i], ref[0]), f"mq row b={b} i={i}"
+    p = W.mq_paged_case(2, 3, 8, 2, 64, 16, 20, [37, 3], max_len=64, seed=76)
+    got = oracle.paged_decode_mq(p.q, p.k, p.v, p.seq_lens, p.page_table, p.scale, lib=lib)
+    for b in range(p.B):
+        for i in range(p.M):
+            n = int(p.seq_lens[b]) - p.M + i + 1
+            ref = oracle.paged_decode(p.q[b:b + 1, i], p.k, p.v, np.array([n], np.int32),
+                                      p.page_table[b:b + 1], p.scale, lib=lib)
+            assert np.array_equal(got[b, i], ref[0]), f"paged mq row b={b} i={i}"
+
+
+def pin_mq_future_keys_ignored(lib):
+    """Changing the keys and values a query may not see (positions > len - M + i) leaves its
+    row unchanged, and M = 1 is the single-query call."""
+    c = W.mq_case(1, 5, 4, 1, 64, 30, seq_lens=[30], seed=77)
+    base = oracle.decode_mq(c.q, c.k, c.v, c.seq_lens, c.scale, lib=lib)
+    k, v = c.k.copy(), c.v.copy()
+    k[:, :, 27:] = _bits(np.full(k[:, :, 27:].shape, 3.0, np.float32))
+    v[:, :, 27:] = _bits(np.full(v[:, :, 27:].shape, -2.0, np.float32))
+    moved = oracle.decode_mq(c.q, k, v, c.seq_lens, c.scale, lib=lib)
+    assert np.array_equal(moved[0, :2], base[0, :2]), "rows 0-1 must not see keys >= 27"
+    assert not np.array_equal(moved[0, 2:], base[0, 2:]), "rows 2-4 see key 27 and later"
+    one = W.mq_case(2, 1, 8, 2, 64, 33, seq_lens=[33, 9], seed=78)
+    assert np.array_equal(oracle.decode_mq(one.q, one.k, one.v, one.seq_lens, one.scale, lib=lib)[:, 0],
+                          oracle.decode(one.q[:, 0], one.k, one.v, one.seq_lens, one.scale, lib=lib))
+
+
 ALL_PINS = [
     pin_golden_closed_forms, pin_torch_sdpa, pin_brute_force, pin_len_one_is_v0,
     pin_uniform_weights_give_mean, pin_dominant_key, pin_scale_moves_into_q, pin_v_is_linear,
     pin_token_permutation, pin_head_mapping, pin_nan_tail_ignored, pin_split_invariance,
     pin_paged_equals_gathered, pin_page_permutation, pin_fp8_values, pin_fp8_matches_bf16,
-    pin_fp8_split_invariance,
+    pin_fp8_split_invariance, pin_mq_rows_are_single_query_calls, pin_mq_future_keys_ignored,
 ]

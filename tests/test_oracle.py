@@ -38,8 +38,13 @@ MUTANTS = {
     "split_weight_dropped": ("Lsum += w * l;", "Lsum += l;"),
     "split_max_ignored": ("double w = (m == -INFINITY) ? 0.0 : exp(m - M);",
                           "double w = (m == -INFINITY) ? 0.0 : exp(m);"),
-    "q_row_of_other_head": ("q + ((size_t)b * Hq + h) * (size_t)D;",
-                            "q + ((size_t)b * Hq + kvh) * (size_t)D;"),
+    "q_row_of_other_head": ("q + (((size_t)b * M + i) * Hq + h) * (size_t)D;",
+                            "q + (((size_t)b * M + i) * Hq + kvh) * (size_t)D;"),
+    # multi-query rows
+    "mq_causal_off_by_one": ("const int n = seq_lens[b] - M + i + 1;", "const int n = seq_lens[b] - M + i;"),
+    "mq_not_causal": ("const int n = seq_lens[b] - M + i + 1;", "const int n = seq_lens[b];"),
+    "mq_query_order_reversed": ("q + (((size_t)b * M + i) * Hq + h) * (size_t)D;",
+                                "q + (((size_t)b * M + (M - 1 - i)) * Hq + h) * (size_t)D;"),
     "k_dim_stride_transposed": ("dot += widen_bf16(q[d]) * k_elem(L, kbase + d);",
                                 "dot += widen_bf16(q[d]) * k_elem(L, kbase + (d * 7) % L->D);"),
     # the E4M3 cache

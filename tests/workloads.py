@@ -116,6 +116,7 @@ class Case:
     kv: str = "bf16"              # "bf16": k, v are uint16 bf16 bits; "fp8": uint8 E4M3 bytes
     k_scale: float = 1.0          # fp8: per-tensor scales (float32 values)
     v_scale: float = 1.0
+    M: int = 1                    # query tokens per sequence; M > 1: q is [B, M, Hq, D]
 
     @property
     def paged(self) -> bool:
@@ -150,7 +151,7 @@ class Case:
     def algorithmic_bytes(self) -> int:
         """sum(len) * Hkv * D * 2 (K and V) * element bytes + q (bf16) + out (fp32)."""
         return (int(self.seq_lens.astype(np.int64).sum()) * self.Hkv * self.D * 2 * self.kv_bytes
-                + self.B * self.Hq * self.D * 2 + self.B * self.Hq * self.D * 4)
+                + self.B * self.M * self.Hq * self.D * (2 + 4))
 
 
 def default_scale(D: int) -> float:
@@ -215,6 +216,36 @@ def fp8_paged_case(B, Hq, Hkv, D, page_size, num_pages, seq_lens=None, *, max_le
     return Case(name, B, Hq, Hkv, D, default_scale(D) if scale is None else float(np.float32(scale)),
                 q, k, v, lens, table, page_size, kv="fp8", k_scale=float(np.float32(k_scale)),
                 v_scale=float(np.float32(v_scale)))
+
+
+def mq_case(B, M, Hq, Hkv, D, S_max, seq_lens=None, *, seed=0, scale=None, tail=None,
+            name="mq") -> Case:
+    """Multi-query decode over a contiguous cache: q [B, M, Hq, D], the last M positions of each
+    sequence.  tail "nan" poisons rows >= len."""
+    rng = np.random.default_rng(seed)
+    q = _normal_bf16(rng, (B, M, Hq, D))
+    k = _normal_bf16(rng, (B, Hkv, S_max, D))
+    v = _normal_bf16(rng, (B, Hkv, S_max, D))
+    lens = np.full(B, S_max, np.int32) if seq_lens is None else np.asarray(seq_lens, np.int32)
+    if tail == "nan":
+        for b in range(B):
+            k[b, :, lens[b]:, :] = 0x7FC0
+            v[b, :, lens[b]:, :] = 0x7FC0
+    return Case(name, B, Hq, Hkv, D, default_scale(D) if scale is None else float(np.float32(scale)),
+                q, k, v, lens, M=M)
+
+
+def mq_paged_case(B, M, Hq, Hkv, D, page_size, num_pages, seq_lens, *, max_len, seed=0,
+                  scale=None, name="mq_paged") -> Case:
+    """Multi-query decode over a paged cache."""
+    rng = np.random.default_rng(seed)
+    q = _normal_bf16(rng, (B, M, Hq, D))
+    k = _normal_bf16(rng, (num_pages, Hkv, page_size, D))
+    v = _normal_bf16(rng, (num_pages, Hkv, page_size, D))
+    lens = np.asarray(seq_lens, np.int32)
+    table = assign_pages(rng, lens, page_size, num_pages, max(1, (max_len + page_size - 1) // page_size))
+    return Case(name, B, Hq, Hkv, D, default_scale(D) if scale is None else float(np.float32(scale)),
+                q, k, v, lens, table, page_size, M=M)
 
 
 def assign_pages(rng: np.random.Generator, lens, page_size: int, num_pages: int,
