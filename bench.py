@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's heuristic")
+    ap.add_argument("--queries", type=int, default=1,
+                    help="query tokens per sequence (multi-query decode, gqa_decode_mq); "
+                         "M * G must be <= 16")
     ap.add_argument("--kv", choices=("bf16", "fp8"), default="bf16",
                     help="cache element type: bf16 (the headline), or the workload's OCP FP8 E4M3 "
                          "form with per-tensor scales (gqa_decode_fp8)")
@@ -167,6 +170,10 @@ def main():
     gd.load()
     name = args.workload or W.HEADLINE
     case = W.make(name, kv=args.kv)
+    if args.queries > 1:
+        if args.kv != "bf16":
+            sys.exit("--queries > 1 runs on the bf16 cache")
+        case = W.with_queries(case, args.queries)
     base = DeviceCase(case)
     algo_bytes = case.algorithmic_bytes()
     kv_bytes = case.k.nbytes + case.v.nbytes
@@ -180,12 +187,13 @@ def main():
         d.page_table = None if base.page_table is None else base.page_table.clone()
         sets[i] = d
     cap = case.capacity
-    plan = gd.gqa_decode_plan(case.B, case.Hq, case.Hkv, case.D, cap, case.page_size,
+    plan = gd.gqa_decode_plan(case.B, case.M * case.Hq, case.Hkv, case.D, cap, case.page_size,
                               args.splits, torch.cuda.get_device_properties(0).multi_processor_count)
-    need = gd.gqa_decode_workspace_bytes(case.B, case.Hq, case.Hkv, case.D, cap, case.page_size,
+    need = gd.gqa_decode_workspace_bytes(case.B, case.M * case.Hq, case.Hkv, case.D, cap, case.page_size,
                                          args.splits)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
-    outs = [torch.empty((case.B, case.Hq, case.D), dtype=torch.float32, device="cuda")
+    oshape = (case.B, case.Hq, case.D) if case.M == 1 else (case.B, case.M, case.Hq, case.D)
+    outs = [torch.empty(oshape, dtype=torch.float32, device="cuda")
             for _ in range(R)]
     def full(i, stream):
         sets[i % R].run(args.splits, out=outs[i % R], workspace=ws, stream=stream)
@@ -257,8 +265,11 @@ def main():
     gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
     # The dominant kernel alone (the split-KV partial kernel; K launches in one graph), and the
     # combine alone, each on the stream they are launched on.
-    split_ms = graph_time(split_only, args.steps)
-    combine_ms = graph_time(combine_only, args.steps) if not plan.direct else 0.0
+    if case.M == 1:
+        split_ms = graph_time(split_only, args.steps)
+        combine_ms = graph_time(combine_only, args.steps) if not plan.direct else 0.0
+    else:   # multi-query calls have no split-only entry point: the roofline uses whole calls
+        split_ms, combine_ms = ms_per_step, 0.0
     split_gbs = algo_bytes / (split_ms * 1e-3) / 1e9
 
     cpu = None
@@ -268,7 +279,12 @@ def main():
         t0 = time.perf_counter()
         calls = 0
         while True:
-            if case.kv == "fp8" and case.paged:
+            if case.M > 1 and case.paged:
+                oracle.paged_decode_mq(case.q, case.k, case.v, case.seq_lens, case.page_table,
+                                       case.scale)
+            elif case.M > 1:
+                oracle.decode_mq(case.q, case.k, case.v, case.seq_lens, case.scale)
+            elif case.kv == "fp8" and case.paged:
                 oracle.paged_decode_fp8(case.q, case.k, case.v, case.seq_lens, case.page_table,
                                         case.scale, case.k_scale, case.v_scale)
             elif case.kv == "fp8":
@@ -306,7 +322,8 @@ def main():
         "dtype": "bf16" if args.kv == "bf16" else "fp8-e4m3 KV, bf16 q and MFMA",
         "data": "synthetic (seeded N(0,1) bf16 q/K/V)" if args.kv == "bf16" else
                 "synthetic (seeded N(0,1) bf16 q; K/V the same draws rounded to E4M3 at scale 1/16)",
-        "config": {"workload": name, "batch": case.B, "q_heads": case.Hq, "kv_heads": case.Hkv,
+        "config": {"workload": name, "batch": case.B, "queries_per_sequence": case.M,
+                   "q_heads": case.Hq, "kv_heads": case.Hkv,
                    "head_dim": case.D, "capacity": cap, "page_size": case.page_size,
                    "sum_len": int(case.seq_lens.sum()), "algorithmic_bytes": algo_bytes,
                    "plan": plan.as_dict(), "rotated_sets": R, "parallelism": "single GPU"},
@@ -315,7 +332,8 @@ def main():
                      "traffic": traffic,
                      "kernel_us": round(split_ms * 1e3, 3),
                      "combine_us": round(combine_ms * 1e3, 3),
-                     "timed": "K launches of the split kernel alone in one HIP graph, HIP events"},
+                     "timed": "K launches of the split kernel alone in one HIP graph, HIP events"
+                              if case.M == 1 else "K whole multi-query calls in one HIP graph"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

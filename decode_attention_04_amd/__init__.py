@@ -29,7 +29,8 @@ STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_
 EXPORTED = ("gqa_decode_plan", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_paged_decode",
             "gqa_decode_partials", "gqa_paged_decode_partials", "gqa_decode_combine",
             "gqa_decode_fp8", "gqa_paged_decode_fp8", "gqa_decode_fp8_partials",
-            "gqa_paged_decode_fp8_partials", "gqa_status_string")
+            "gqa_paged_decode_fp8_partials", "gqa_decode_mq", "gqa_paged_decode_mq",
+            "gqa_status_string")
 
 
 class GqaError(RuntimeError):
@@ -87,6 +88,11 @@ def load(path: str = LIB_PATH):
     lib.gqa_decode_fp8_partials.restype = ci
     lib.gqa_paged_decode_fp8_partials.argtypes = lib.gqa_paged_decode_fp8.argtypes
     lib.gqa_paged_decode_fp8_partials.restype = ci
+    lib.gqa_decode_mq.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, vp, sz, ci, vp]
+    lib.gqa_decode_mq.restype = ci
+    lib.gqa_paged_decode_mq.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, cf, vp,
+                                        vp, sz, ci, vp]
+    lib.gqa_paged_decode_mq.restype = ci
     lib.gqa_status_string.argtypes = [ci]
     lib.gqa_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -276,6 +282,54 @@ def gqa_paged_decode_fp8_partials(q, k_pool, v_pool, seq_lens, page_table, scale
     return gqa_paged_decode_fp8(q, k_pool, v_pool, seq_lens, page_table, scale, k_scale, v_scale,
                                 out, workspace, num_splits, stream,
                                 _entry="gqa_paged_decode_fp8_partials")
+
+
+def gqa_decode_mq(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None, num_splits=0,
+                  stream=None):
+    """Multi-query decode: q [B,M,Hq,D] bf16 (the last M positions of each sequence, query i
+    attending to keys 0 .. len-M+i), k/v [B,Hkv,S_max,D]; returns out fp32 [B,M,Hq,D]."""
+    torch = _torch()
+    B, M, Hq, D = q.shape
+    _, Hkv, S_max, _ = k_cache.shape
+    if out is None:
+        out = torch.empty((B, M, Hq, D), dtype=torch.float32, device=q.device)
+    need = gqa_decode_workspace_bytes(B, M * Hq, Hkv, D, S_max, 0, num_splits)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    bf = _bf16_types()
+    rc = load().gqa_decode_mq(
+        _dev_ptr(q, "q", bf), _dev_ptr(k_cache, "k_cache", bf), _dev_ptr(v_cache, "v_cache", bf),
+        _dev_ptr(seq_lens, "seq_lens", (torch.int32,)), B, M, Hq, Hkv, D, S_max, float(scale),
+        _dev_ptr(out, "out", (torch.float32,)),
+        None if workspace is None else workspace.data_ptr(), ws_bytes, int(num_splits),
+        _stream_ptr(stream, q.device))
+    if rc != GQA_OK:
+        raise GqaError(rc, "gqa_decode_mq")
+    return out
+
+
+def gqa_paged_decode_mq(q, k_pool, v_pool, seq_lens, page_table, scale, out=None, workspace=None,
+                        num_splits=0, stream=None):
+    """Multi-query decode over a paged cache: q [B,M,Hq,D]."""
+    torch = _torch()
+    B, M, Hq, D = q.shape
+    P, Hkv, page_size, _ = k_pool.shape
+    max_pages = page_table.shape[1]
+    if out is None:
+        out = torch.empty((B, M, Hq, D), dtype=torch.float32, device=q.device)
+    need = gqa_decode_workspace_bytes(B, M * Hq, Hkv, D, max_pages * page_size, page_size,
+                                      num_splits)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    bf = _bf16_types()
+    rc = load().gqa_paged_decode_mq(
+        _dev_ptr(q, "q", bf), _dev_ptr(k_pool, "k_pool", bf), _dev_ptr(v_pool, "v_pool", bf),
+        _dev_ptr(seq_lens, "seq_lens", (torch.int32,)),
+        _dev_ptr(page_table, "page_table", (torch.int32,)), B, M, Hq, Hkv, D, page_size, P,
+        max_pages, float(scale), _dev_ptr(out, "out", (torch.float32,)),
+        None if workspace is None else workspace.data_ptr(), ws_bytes, int(num_splits),
+        _stream_ptr(stream, q.device))
+    if rc != GQA_OK:
+        raise GqaError(rc, "gqa_paged_decode_mq")
+    return out
 
 
 def gqa_decode_partials(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None,

@@ -80,7 +80,8 @@ struct SplitArgs {
     float *part_acc;
     float *part_ml;
     float *out;                 // [B][Hq][D]
-    int B, Hq, Hkv, G;
+    int B, Hq, Hkv, G;          // G: query heads per kv head
+    int M, R;                   // query tokens per sequence (the last M positions); R = M * G rows
     int S_max;                  // contiguous capacity
     int page_size, max_pages;   // paged
     int num_pages;              // paged
@@ -94,9 +95,10 @@ struct CombineArgs {
     const float *part_ml;
     float *out;
     const int32_t *seq_lens;  // even partition only
-    int D, G, Hq, num_splits;
+    int D, G, Hq, num_splits; // G, Hq: output rows per (sequence, kv head) and per sequence
     int B, Hkv, cap, tile;    // even partition: how the split kernel cut the tiles
     int shares;               // even partition: workgroups of the split kernel
+    int M, Gh;                // query tokens per sequence, query heads per kv head (G = M * Gh)
 };
 
 __device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
@@ -304,7 +306,8 @@ __device__ __forceinline__ void stage_v(const Tile<D, NB, KV> &t, int r, int grp
 }
 
 // QK^T and the online-softmax update for one tile whose first key has index
-// `t0` in the sequence (keys at or beyond `t_end` masked).  On return
+// `t0` in the sequence (keys at or beyond `t_end`, this lane's row limit,
+// masked).  On return
 // sc[blk][i] holds the probability of key 16*blk + 4*grp + i for head r
 // (relative to the new running max) and acc has been rescaled.
 template <int D, int NB, int KV>
@@ -332,15 +335,18 @@ __device__ __forceinline__ void qk_softmax(const Tile<D, NB, KV> &t, const bf16x
         }
     }
     mx = max_rows(mx);
-    // The tile holds at least one unmasked key, so m_new is finite.
     const float m_new = fmaxf(st.m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 on the first tile
+    // m_new is -inf only while every key this row has seen is masked (a
+    // multi-query row whose causal limit lies before the tile): exponentials
+    // are then taken against 0, every p is 0 and the state stays empty.
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_ref);  // 0 on the first tile
     float psum = 0.f;
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float p = __builtin_amdgcn_exp2f(sc[blk][i] - m_new);
+            const float p = __builtin_amdgcn_exp2f(sc[blk][i] - m_ref);
             sc[blk][i] = p;
             psum += p;
         }
@@ -582,14 +588,19 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
     const int ntiles = t_end > t_begin ? (t_end - t_begin + TT - 1) / TT : 0;
     const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
-    // Q of the G heads of this kv head, exact bf16, in the QK B operand layout.
+    // Q of the R = M * G query rows of this kv head (row r = i * G + g: query
+    // token i, head kvh * G + g), exact bf16, in the QK B operand layout.
+    const int qi = r / a.G;
+    const int qg = r - qi * a.G;
+    // Multi-query: query token i is position len - M + i and sees keys < len - M + i + 1.
+    const int row_end = min(t_end, len - a.M + qi + 1);
     bf16x8_t qb[S::KB];
     {
-        const uint16_t *qrow = a.q + ((size_t)b * a.Hq + (size_t)kvh * a.G + r) * D;
+        const uint16_t *qrow = a.q + (((size_t)b * a.M + qi) * a.Hq + (size_t)kvh * a.G + qg) * D;
 #pragma unroll
         for (int kb = 0; kb < S::KB; ++kb) {
             u32x4_t x = {0u, 0u, 0u, 0u};
-            if (r < a.G) x = *reinterpret_cast<const u32x4_t *>(qrow + kslot_dim<KV>(kb, grp));
+            if (r < a.R) x = *reinterpret_cast<const u32x4_t *>(qrow + kslot_dim<KV>(kb, grp));
             qb[kb] = __builtin_bit_cast(bf16x8_t, x);
         }
     }
@@ -643,10 +654,10 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
         if (my_tiles > 0) issue(buf0, 0, kLoadK | kLoadV);
         for (int it = 0; it < my_tiles; it += 2) {
             if (it + 1 < my_tiles) issue(buf1, it + 1, kLoadK | kLoadV);
-            compute_tile<D, NB, PV, KV>(buf0, qb, st, tile_start(it), t_end, r, grp, a.qk_scale_log2, stage);
+            compute_tile<D, NB, PV, KV>(buf0, qb, st, tile_start(it), row_end, r, grp, a.qk_scale_log2, stage);
             if (it + 1 < my_tiles) {
                 if (it + 2 < my_tiles) issue(buf0, it + 2, kLoadK | kLoadV);
-                compute_tile<D, NB, PV, KV>(buf1, qb, st, tile_start(it + 1), t_end, r, grp, a.qk_scale_log2, stage);
+                compute_tile<D, NB, PV, KV>(buf1, qb, st, tile_start(it + 1), row_end, r, grp, a.qk_scale_log2, stage);
             }
         }
     } else {
@@ -663,7 +674,7 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
                 if (it == 0) {
                     // The first tile's K arrives before its V (issued first):
                     // QK^T and the softmax run while V is still in flight.
-                    qk_softmax(buf, qb, st, tile_start(it), t_end, grp, a.qk_scale_log2, sc);
+                    qk_softmax(buf, qb, st, tile_start(it), row_end, grp, a.qk_scale_log2, sc);
                     if (more) issue(buf, it + 1, kLoadK);
                     stage_v(buf, r, grp, stage);
                     if (more) issue(buf, it + 1, kLoadV);
@@ -672,12 +683,12 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
                     // write latency before PV reads the staged V back.
                     stage_v(buf, r, grp, stage);
                     if (more) issue(buf, it + 1, kLoadV);
-                    qk_softmax(buf, qb, st, tile_start(it), t_end, grp, a.qk_scale_log2, sc);
+                    qk_softmax(buf, qb, st, tile_start(it), row_end, grp, a.qk_scale_log2, sc);
                     if (more) issue(buf, it + 1, kLoadK);
                 }
                 pv_tile<D, NB, PV, KV>(buf, sc, st, r, grp, stage);
             } else {
-                compute_tile<D, NB, PV, KV>(buf, qb, st, tile_start(it), t_end, r, grp, a.qk_scale_log2, stage);
+                compute_tile<D, NB, PV, KV>(buf, qb, st, tile_start(it), row_end, r, grp, a.qk_scale_log2, stage);
                 if (more) issue(buf, it + 1, kLoadK | kLoadV);
             }
         }
@@ -686,8 +697,8 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
     // This wave's sum for head r: the four lanes r, r+16, r+32, r+48.
     const float lsum = sum_rows(st.l);
 
-    // Publish the wave's state into its own region; rows g >= G are never read.
-    if (r < a.G) {
+    // Publish the wave's state into its own region; rows r >= R are never read.
+    if (r < a.R) {
         if (grp == 0) {
             lds.m[wave][r] = st.m;
             lds.l[wave][r] = lsum;
@@ -713,8 +724,7 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
     __syncthreads();
 
     // Fold the waves in ascending order: this range's partial (or the output).
-    const int G = a.G;
-    float *out_rows = a.out + ((size_t)b * a.Hq + (size_t)kvh * G) * D;
+    const int G = a.R;
     float *my_acc = a.part_acc + slot * G * D;
     float *my_ml = a.part_ml + slot * G * 2;
     for (int col = threadIdx.x; col < G * (D / 4); col += 64 * kWaves) {
@@ -743,8 +753,9 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
         }
         if constexpr (KV == kKvFp8) acc *= a.v_scale;  // the partials hold dequantised V sums
         if (direct) {
-            *reinterpret_cast<f32x4_t *>(out_rows + (size_t)g * D + d) =
-                L > 0.f ? acc / L : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const int i = g / a.G;  // row g = query token i, head kvh * G + (g - i * G)
+            float *orow = a.out + (((size_t)b * a.M + i) * a.Hq + (size_t)kvh * a.G + (g - i * a.G)) * D;
+            *reinterpret_cast<f32x4_t *>(orow + d) = L > 0.f ? acc / L : f32x4_t{0.f, 0.f, 0.f, 0.f};
         } else {
             // Device-scope (write-through) stores: the combine kernel reads the
             // partials from other XCDs, and the kernel-end L2 writeback then has
@@ -1018,7 +1029,13 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
                 O += wt * wo[w][c];
             }
         }
-        *reinterpret_cast<f32x4_t *>(a.out + bh * D + d0 + 4 * c) =
+        // row h = kvh * G + i * Gh + gh of sequence b is out[b][i][kvh * Gh + gh]
+        size_t orow = bh;
+        if (a.M > 1) {
+            const int rho = h % G, i = rho / a.Gh;
+            orow = ((size_t)b * a.M + i) * (size_t)(a.Hq / a.M) + (size_t)(h / G) * a.Gh + (rho - i * a.Gh);
+        }
+        *reinterpret_cast<f32x4_t *>(a.out + orow * D + d0 + 4 * c) =
             L > 0.f ? O / L : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 }
@@ -1109,15 +1126,17 @@ int env_splits() {
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const float *part_ml,
-                          float *out, const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int cap,
-                          hipStream_t stream) {
-    CombineArgs ca{part_acc, part_ml, out, seq_lens, D, Hq / Hkv, Hq, plan.num_splits,
-                   B, Hkv, cap, plan.tile_tokens, plan.grid};
+                          float *out, const int32_t *seq_lens, int B, int M, int Hq, int Hkv, int D,
+                          int cap, hipStream_t stream) {
+    // rows: M query tokens x Hq heads per sequence, M * G per (sequence, kv head)
+    const int rows = M * Hq;
+    CombineArgs ca{part_acc, part_ml, out, seq_lens, D, rows / Hkv, rows, plan.num_splits,
+                   B, Hkv, cap, plan.tile_tokens, plan.grid, M, Hq / Hkv};
     // The widest dim chunk (NCOL = 16, 8 or 4 columns of 4 dims) that still
     // gives at least 128 workgroups: narrower chunks put more threads on the
     // pieces of a column (measured best for few heads with many pieces).
     // GQA_DECODE_COMBINE_COLS = 4, 8 or 16 overrides it.
-    const int64_t heads = (int64_t)B * Hq;
+    const int64_t heads = (int64_t)B * rows;
     int ncol = env_int("GQA_DECODE_COMBINE_COLS", 0);
     if (ncol != 4 && ncol != 8 && ncol != 16) {
         ncol = 16;
@@ -1194,7 +1213,7 @@ constexpr KvSpec kBf16Cache{kKvBf16, 1.f, 1.f};
 gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, int kv, void *workspace,
                  hipStream_t stream, int phases) {
     if (!plan.direct) {
-        WorkspaceLayout w = workspace_layout(a.Hq, a.Hkv, D, plan.slots);
+        WorkspaceLayout w = workspace_layout(a.M * a.Hq, a.Hkv, D, plan.slots);
         char *base = static_cast<char *>(workspace);
         a.part_acc = reinterpret_cast<float *>(base + w.part_acc);
         a.part_ml = reinterpret_cast<float *>(base + w.part_ml);
@@ -1211,7 +1230,7 @@ gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, int kv
     }
     if (plan.direct || !(phases & kPhaseCombine)) return GQA_OK;
     const int cap = paged ? a.max_pages * a.page_size : a.S_max;
-    e = launch_combine(plan, a.part_acc, a.part_ml, a.out, a.seq_lens, a.B, a.Hq, a.Hkv, D, cap, stream);
+    e = launch_combine(plan, a.part_acc, a.part_ml, a.out, a.seq_lens, a.B, a.M, a.Hq, a.Hkv, D, cap, stream);
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
@@ -1341,19 +1360,30 @@ size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_seq_len
 
 namespace {
 
+// Checks of the query-token count M (1 for single-token decode): M * G query
+// rows per kv head must fit the 16 MFMA columns.
+gqa_status_t check_queries(int B, int M, int Hq, int Hkv, int D) {
+    if (M < 1) return GQA_ERR_SHAPE;
+    if (Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && (int64_t)M * (Hq / Hkv) > kMaxHeadsPerKv)
+        return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)B * M * Hq * D > INT32_MAX) return GQA_ERR_SHAPE;
+    return GQA_OK;
+}
+
 gqa_status_t decode_contig(const void *q, const void *k_cache, const void *v_cache,
-                           const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
+                           const int32_t *seq_lens, int B, int M, int Hq, int Hkv, int D, int S_max,
                            float scale, const KvSpec &kv, float *out, void *workspace,
                            size_t workspace_bytes, int num_splits, hipStream_t stream, int phases) {
     gqa_status_t s = check_common(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, scale);
     if (s != GQA_OK) return s;
+    if ((s = check_queries(B, M, Hq, Hkv, D)) != GQA_OK) return s;
     if (S_max < 0 || num_splits < 0 || !isfinite(kv.k_scale) || !isfinite(kv.v_scale)) return GQA_ERR_SHAPE;
     if (B == 0) return GQA_OK;
     const int eb = kv.type == kKvFp8 ? 1 : 2;
     if (((int64_t)S_max + 64) * D * eb > INT32_MAX) return GQA_ERR_SHAPE;  // 32-bit buffer offsets
     if (workspace != nullptr && misaligned(workspace, 16)) return GQA_ERR_ALIGN;
     gqa_plan_t plan;
-    s = plan_for_call(B, Hq, Hkv, D, S_max, 0, num_splits, &plan);
+    s = plan_for_call(B, M * Hq, Hkv, D, S_max, 0, num_splits, &plan);
     if (s != GQA_OK) return s;
     if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
         return workspace == nullptr ? GQA_ERR_NULL : GQA_ERR_WORKSPACE;
@@ -1364,7 +1394,7 @@ gqa_status_t decode_contig(const void *q, const void *k_cache, const void *v_cac
     a.v = static_cast<const unsigned char *>(v_cache);
     a.seq_lens = seq_lens;
     a.out = out;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.M = M; a.R = M * (Hq / Hkv);
     a.S_max = S_max;
     a.num_splits = plan.num_splits;
     a.split_tokens = plan.split_tokens;
@@ -1374,12 +1404,13 @@ gqa_status_t decode_contig(const void *q, const void *k_cache, const void *v_cac
 }
 
 gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
-                          const int32_t *seq_lens, const int32_t *page_table, int B, int Hq,
+                          const int32_t *seq_lens, const int32_t *page_table, int B, int M, int Hq,
                           int Hkv, int D, int page_size, int num_pages, int max_pages,
                           float scale, const KvSpec &kv, float *out, void *workspace,
                           size_t workspace_bytes, int num_splits, hipStream_t stream, int phases) {
     gqa_status_t s = check_common(q, k_pool, v_pool, seq_lens, out, B, Hq, Hkv, D, scale);
     if (s != GQA_OK) return s;
+    if ((s = check_queries(B, M, Hq, Hkv, D)) != GQA_OK) return s;
     if (!isfinite(kv.k_scale) || !isfinite(kv.v_scale)) return GQA_ERR_SHAPE;
     if (B == 0) return (page_size > 0 && page_size % 16 == 0) ? GQA_OK : GQA_ERR_UNSUPPORTED;
     if (page_table == nullptr) return GQA_ERR_NULL;
@@ -1390,7 +1421,7 @@ gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
         return GQA_ERR_SHAPE;
     if (workspace != nullptr && misaligned(workspace, 16)) return GQA_ERR_ALIGN;
     gqa_plan_t plan;
-    s = plan_for_call(B, Hq, Hkv, D, max_pages * page_size, page_size, num_splits, &plan);
+    s = plan_for_call(B, M * Hq, Hkv, D, max_pages * page_size, page_size, num_splits, &plan);
     if (s != GQA_OK) return s;
     if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
         return workspace == nullptr ? GQA_ERR_NULL : GQA_ERR_WORKSPACE;
@@ -1402,7 +1433,7 @@ gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
     a.seq_lens = seq_lens;
     a.page_table = page_table;
     a.out = out;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.M = M; a.R = M * (Hq / Hkv);
     a.page_size = page_size;
     a.max_pages = max_pages;
     a.num_pages = num_pages;
@@ -1421,7 +1452,7 @@ gqa_status_t gqa_decode(const void *q, const void *k_cache, const void *v_cache,
                         const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
                         float scale, float *out, void *workspace, size_t workspace_bytes,
                         int num_splits, hipStream_t stream) {
-    return decode_contig(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale, kBf16Cache, out,
+    return decode_contig(q, k_cache, v_cache, seq_lens, B, 1, Hq, Hkv, D, S_max, scale, kBf16Cache, out,
                          workspace, workspace_bytes, num_splits, stream, kPhaseSplit | kPhaseCombine);
 }
 
@@ -1429,7 +1460,7 @@ gqa_status_t gqa_decode_partials(const void *q, const void *k_cache, const void 
                                  const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
                                  float scale, float *out, void *workspace, size_t workspace_bytes,
                                  int num_splits, hipStream_t stream) {
-    return decode_contig(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale, kBf16Cache, out,
+    return decode_contig(q, k_cache, v_cache, seq_lens, B, 1, Hq, Hkv, D, S_max, scale, kBf16Cache, out,
                          workspace, workspace_bytes, num_splits, stream, kPhaseSplit);
 }
 
@@ -1438,7 +1469,7 @@ gqa_status_t gqa_paged_decode(const void *q, const void *k_pool, const void *v_p
                               int Hkv, int D, int page_size, int num_pages, int max_pages,
                               float scale, float *out, void *workspace, size_t workspace_bytes,
                               int num_splits, hipStream_t stream) {
-    return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, Hq, Hkv, D, page_size, num_pages,
+    return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, 1, Hq, Hkv, D, page_size, num_pages,
                         max_pages, scale, kBf16Cache, out, workspace, workspace_bytes, num_splits,
                         stream, kPhaseSplit | kPhaseCombine);
 }
@@ -1448,7 +1479,7 @@ gqa_status_t gqa_paged_decode_partials(const void *q, const void *k_pool, const 
                                        int Hq, int Hkv, int D, int page_size, int num_pages,
                                        int max_pages, float scale, float *out, void *workspace,
                                        size_t workspace_bytes, int num_splits, hipStream_t stream) {
-    return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, Hq, Hkv, D, page_size, num_pages,
+    return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, 1, Hq, Hkv, D, page_size, num_pages,
                         max_pages, scale, kBf16Cache, out, workspace, workspace_bytes, num_splits,
                         stream, kPhaseSplit);
 }
@@ -1457,7 +1488,7 @@ gqa_status_t gqa_decode_fp8(const void *q, const void *k_cache, const void *v_ca
                             const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
                             float scale, float k_scale, float v_scale, float *out, void *workspace,
                             size_t workspace_bytes, int num_splits, hipStream_t stream) {
-    return decode_contig(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale,
+    return decode_contig(q, k_cache, v_cache, seq_lens, B, 1, Hq, Hkv, D, S_max, scale,
                          KvSpec{kKvFp8, k_scale, v_scale}, out, workspace, workspace_bytes, num_splits,
                          stream, kPhaseSplit | kPhaseCombine);
 }
@@ -1468,7 +1499,7 @@ gqa_status_t gqa_paged_decode_fp8(const void *q, const void *k_pool, const void 
                                   float scale, float k_scale, float v_scale, float *out,
                                   void *workspace, size_t workspace_bytes, int num_splits,
                                   hipStream_t stream) {
-    return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, Hq, Hkv, D, page_size, num_pages,
+    return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, 1, Hq, Hkv, D, page_size, num_pages,
                         max_pages, scale, KvSpec{kKvFp8, k_scale, v_scale}, out, workspace,
                         workspace_bytes, num_splits, stream, kPhaseSplit | kPhaseCombine);
 }
@@ -1478,7 +1509,7 @@ gqa_status_t gqa_decode_fp8_partials(const void *q, const void *k_cache, const v
                                      int S_max, float scale, float k_scale, float v_scale, float *out,
                                      void *workspace, size_t workspace_bytes, int num_splits,
                                      hipStream_t stream) {
-    return decode_contig(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale,
+    return decode_contig(q, k_cache, v_cache, seq_lens, B, 1, Hq, Hkv, D, S_max, scale,
                          KvSpec{kKvFp8, k_scale, v_scale}, out, workspace, workspace_bytes, num_splits,
                          stream, kPhaseSplit);
 }
@@ -1489,9 +1520,27 @@ gqa_status_t gqa_paged_decode_fp8_partials(const void *q, const void *k_pool, co
                                            int max_pages, float scale, float k_scale, float v_scale,
                                            float *out, void *workspace, size_t workspace_bytes,
                                            int num_splits, hipStream_t stream) {
-    return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, Hq, Hkv, D, page_size, num_pages,
+    return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, 1, Hq, Hkv, D, page_size, num_pages,
                         max_pages, scale, KvSpec{kKvFp8, k_scale, v_scale}, out, workspace,
                         workspace_bytes, num_splits, stream, kPhaseSplit);
+}
+
+gqa_status_t gqa_decode_mq(const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *seq_lens, int B, int M, int Hq, int Hkv, int D, int S_max,
+                           float scale, float *out, void *workspace, size_t workspace_bytes,
+                           int num_splits, hipStream_t stream) {
+    return decode_contig(q, k_cache, v_cache, seq_lens, B, M, Hq, Hkv, D, S_max, scale, kBf16Cache, out,
+                         workspace, workspace_bytes, num_splits, stream, kPhaseSplit | kPhaseCombine);
+}
+
+gqa_status_t gqa_paged_decode_mq(const void *q, const void *k_pool, const void *v_pool,
+                                 const int32_t *seq_lens, const int32_t *page_table, int B, int M,
+                                 int Hq, int Hkv, int D, int page_size, int num_pages, int max_pages,
+                                 float scale, float *out, void *workspace, size_t workspace_bytes,
+                                 int num_splits, hipStream_t stream) {
+    return decode_paged(q, k_pool, v_pool, seq_lens, page_table, B, M, Hq, Hkv, D, page_size, num_pages,
+                        max_pages, scale, kBf16Cache, out, workspace, workspace_bytes, num_splits,
+                        stream, kPhaseSplit | kPhaseCombine);
 }
 
 gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, const int32_t *seq_lens,
@@ -1516,7 +1565,7 @@ gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, c
     SplitArgs a{};
     a.out = out;
     a.seq_lens = seq_lens;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.M = 1; a.R = Hq / Hkv;
     if (page_size > 0) {
         a.page_size = page_size;
         a.max_pages = max_seq_len / page_size;

@@ -210,6 +210,31 @@ gqa_status_t gqa_paged_decode_fp8_partials(const void *q, const void *k_pool, co
                                            void *workspace, size_t workspace_bytes,
                                            int num_splits, hipStream_t stream);
 
+/*
+ * Multi-query decode (verification of M drafted tokens in speculative
+ * decoding: the drafted block of the sparkinfer PR #874 speculative-decode
+ * report; causal masking as in the prefill kernel of the AstrAI csrc commit
+ * log).  Each sequence carries M query tokens, its last M positions, whose
+ * keys and values are already in the cache: query i (0-based) attends to
+ * keys 0 .. seq_lens[b] - M + i.
+ *   q   bf16 [B][M][Hq][head_dim];  out fp32 [B][M][Hq][head_dim]
+ *   M >= 1 and M * (Hq / Hkv) <= 16 (the M*G query rows of a kv head share
+ *   every K/V byte; GQA_ERR_UNSUPPORTED otherwise).  A row with
+ *   seq_lens[b] - M + i + 1 <= 0 is zero.
+ *   workspace: gqa_decode_workspace_bytes(B, M * Hq, Hkv, head_dim, ...).
+ * Everything else as gqa_decode / gqa_paged_decode (M = 1 is gqa_decode).
+ */
+gqa_status_t gqa_decode_mq(const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *seq_lens, int B, int M, int Hq, int Hkv, int head_dim,
+                           int S_max, float scale, float *out, void *workspace,
+                           size_t workspace_bytes, int num_splits, hipStream_t stream);
+
+gqa_status_t gqa_paged_decode_mq(const void *q, const void *k_pool, const void *v_pool,
+                                 const int32_t *seq_lens, const int32_t *page_table, int B, int M,
+                                 int Hq, int Hkv, int head_dim, int page_size, int num_pages,
+                                 int max_pages, float scale, float *out, void *workspace,
+                                 size_t workspace_bytes, int num_splits, hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char *gqa_status_string(gqa_status_t status);
 

@@ -42,6 +42,13 @@ class DeviceCase:
 
     def run(self, num_splits=0, out=None, workspace=None, stream=None) -> torch.Tensor:
         c = self.case
+        if c.M > 1:
+            if c.paged:
+                return gd.gqa_paged_decode_mq(self.q, self.k, self.v, self.seq_lens, self.page_table,
+                                              c.scale, out=out, workspace=workspace,
+                                              num_splits=num_splits, stream=stream)
+            return gd.gqa_decode_mq(self.q, self.k, self.v, self.seq_lens, c.scale, out=out,
+                                    workspace=workspace, num_splits=num_splits, stream=stream)
         if c.kv == "fp8":
             if c.paged:
                 return gd.gqa_paged_decode_fp8(self.q, self.k, self.v, self.seq_lens,
@@ -66,6 +73,11 @@ class DeviceCase:
 
 def oracle_out(case: W.Case) -> np.ndarray:
     import oracle
+    if case.M > 1:
+        if case.paged:
+            return oracle.paged_decode_mq(case.q, case.k, case.v, case.seq_lens, case.page_table,
+                                          case.scale)
+        return oracle.decode_mq(case.q, case.k, case.v, case.seq_lens, case.scale)
     if case.kv == "fp8":
         if case.paged:
             return oracle.paged_decode_fp8(case.q, case.k, case.v, case.seq_lens, case.page_table,

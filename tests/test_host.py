@@ -249,3 +249,26 @@ def test_decode_fp8_rejects(lib, kw, code):
 ])
 def test_paged_decode_fp8_rejects(lib, kw, code):
     assert call_paged_fp8(lib, **kw) == code
+
+
+# ---- multi-query decode: M query tokens per sequence, M * G <= 16 rows per kv head
+def call_decode_mq(lib, q=A, k=A, v=A, lens=A, B=1, M=4, Hq=8, Hkv=2, D=128, S=64, scale=0.1,
+                   out=A, ws=A, ws_bytes=1 << 30, splits=2):
+    return lib.gqa_decode_mq(q, k, v, lens, B, M, Hq, Hkv, D, S, scale, out, ws, ws_bytes, splits,
+                             None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=0), 2), (dict(M=-3), 2), (dict(M=5), 3), (dict(M=17, Hq=2, Hkv=2), 3),
+    (dict(B=1 << 17, M=4, Hq=16, Hkv=4, D=256, S=64), 2),   # B*M*Hq*D past 32 bits
+    (dict(q=None), 1), (dict(q=A + 8), 4), (dict(ws_bytes=16), 5),
+    (dict(B=0, q=None, k=None, v=None, lens=None, out=None, ws=None), 0),
+])
+def test_decode_mq_rejects(lib, kw, code):
+    assert call_decode_mq(lib, **kw) == code
+
+
+def test_mq_workspace_is_the_plan_of_m_times_hq_rows():
+    need = gd.gqa_decode_plan(1, 4 * 8, 2, 128, 64, 0, 2, 256).workspace_bytes
+    assert need > 0
+    assert call_decode_mq(None or gd.load(), ws_bytes=need - 1) == 5

@@ -335,6 +335,14 @@ def to_fp8(case: Case, k_scale: float = 1 / 16, v_scale: float = 1 / 16) -> Case
                                v_scale=float(np.float32(v_scale)))
 
 
+def with_queries(case: Case, M: int, seed: int = 1000) -> Case:
+    """The same cache with M query tokens per sequence (multi-query decode): q [B, M, Hq, D]
+    drawn like q (seeded N(0,1) bf16) from default_rng(seed)."""
+    rng = np.random.default_rng(seed)
+    return dataclasses.replace(case, name=f"{case.name}_m{M}", q=_normal_bf16(rng, (case.B, M, case.Hq, case.D)),
+                               M=M)
+
+
 def make(name: str, seed: int = 0, kv: str = "bf16") -> Case:
     """A named workload; kv="fp8" gives its E4M3-cache form (see to_fp8)."""
     case = WORKLOADS[name](seed)
