@@ -82,6 +82,7 @@ struct SplitArgs {
     float *out;                 // [B][Hq][D]
     int B, Hq, Hkv, G;          // G: query heads per kv head
     int M, R;                   // query tokens per sequence (the last M positions); R = M * G rows
+    int qdiv;                   // ceil(256 / G): row r belongs to query token (r * qdiv) >> 8
     int S_max;                  // contiguous capacity
     int page_size, max_pages;   // paged
     int num_pages;              // paged
@@ -154,11 +155,16 @@ constexpr int kKvBf16 = 0;
 constexpr int kKvFp8 = 1;
 
 // Head dims that contraction slot (k-block kb, lane group grp) of QK^T covers:
-// 8 consecutive dims.  The contraction order is free as long as K and Q agree;
-// for E4M3 each lane loads 16 consecutive bytes that feed two k-blocks.
+// 8 consecutive dims starting at kslot_lane(grp) + kslot_block(kb).  The
+// contraction order is free as long as K and Q agree; for E4M3 each lane loads
+// 16 consecutive bytes that feed two k-blocks.
 template <int KV>
-__device__ __forceinline__ constexpr int kslot_dim(int kb, int grp) {
-    return KV == kKvFp8 ? 64 * (kb >> 1) + 16 * grp + 8 * (kb & 1) : 32 * kb + 8 * grp;
+__device__ __forceinline__ constexpr int kslot_lane(int grp) {
+    return KV == kKvFp8 ? 16 * grp : 8 * grp;
+}
+template <int KV>
+__device__ __forceinline__ constexpr int kslot_block(int kb) {
+    return KV == kKvFp8 ? 64 * (kb >> 1) + 8 * (kb & 1) : 32 * kb;
 }
 
 // One wave's tile as loaded: NB blocks of 16 keys.
@@ -228,7 +234,8 @@ __device__ __forceinline__ void load_tile(Tile<D, NB, KV> &t, __amdgpu_buffer_rs
         const int krow = row0 + 16 * blk + r;
 #pragma unroll
         for (int w = 0; w < T::KW && (parts & kLoadK); ++w) {
-            const int off = KV == kKvFp8 ? krow * D + 64 * w + 16 * grp : (krow * D + kslot_dim<KV>(w, grp)) * 2;
+            const int off = KV == kKvFp8 ? krow * D + 64 * w + 16 * grp
+                                         : (krow * D + kslot_lane<KV>(grp) + kslot_block<KV>(w)) * 2;
             t.k[blk][w] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, CPOL));
         }
 #pragma unroll
@@ -590,17 +597,19 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
 
     // Q of the R = M * G query rows of this kv head (row r = i * G + g: query
     // token i, head kvh * G + g), exact bf16, in the QK B operand layout.
-    const int qi = r / a.G;
+    // i = r / G by a multiply (qdiv = ceil(256 / G): exact for r, G <= 16);
+    // the row index fits 32 bits (B * M * Hq * D <= INT32_MAX, checked on the host).
+    const int qi = (r * a.qdiv) >> 8;
     const int qg = r - qi * a.G;
     // Multi-query: query token i is position len - M + i and sees keys < len - M + i + 1.
     const int row_end = min(t_end, len - a.M + qi + 1);
     bf16x8_t qb[S::KB];
     {
-        const uint16_t *qrow = a.q + (((size_t)b * a.M + qi) * a.Hq + (size_t)kvh * a.G + qg) * D;
+        const int qrow = ((b * a.M + qi) * a.Hq + kvh * a.G + qg) * D + kslot_lane<KV>(grp);
 #pragma unroll
         for (int kb = 0; kb < S::KB; ++kb) {
             u32x4_t x = {0u, 0u, 0u, 0u};
-            if (r < a.R) x = *reinterpret_cast<const u32x4_t *>(qrow + kslot_dim<KV>(kb, grp));
+            if (r < a.R) x = *reinterpret_cast<const u32x4_t *>(a.q + qrow + kslot_block<KV>(kb));
             qb[kb] = __builtin_bit_cast(bf16x8_t, x);
         }
     }
@@ -1394,7 +1403,7 @@ gqa_status_t decode_contig(const void *q, const void *k_cache, const void *v_cac
     a.v = static_cast<const unsigned char *>(v_cache);
     a.seq_lens = seq_lens;
     a.out = out;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.M = M; a.R = M * (Hq / Hkv);
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.M = M; a.R = M * (Hq / Hkv); a.qdiv = (256 + a.G - 1) / a.G;
     a.S_max = S_max;
     a.num_splits = plan.num_splits;
     a.split_tokens = plan.split_tokens;
@@ -1433,7 +1442,7 @@ gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
     a.seq_lens = seq_lens;
     a.page_table = page_table;
     a.out = out;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.M = M; a.R = M * (Hq / Hkv);
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.M = M; a.R = M * (Hq / Hkv); a.qdiv = (256 + a.G - 1) / a.G;
     a.page_size = page_size;
     a.max_pages = max_pages;
     a.num_pages = num_pages;
@@ -1565,7 +1574,7 @@ gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, c
     SplitArgs a{};
     a.out = out;
     a.seq_lens = seq_lens;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.M = 1; a.R = Hq / Hkv;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.M = 1; a.R = Hq / Hkv; a.qdiv = (256 + a.G - 1) / a.G;
     if (page_size > 0) {
         a.page_size = page_size;
         a.max_pages = max_seq_len / page_size;
