@@ -17,7 +17,7 @@ FLAGS = [
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # the kernels' leading scalar arguments are preloaded into SGPRs at launch
-    "-mllvm", "-amdgpu-kernarg-preload-count=7",
+    "-mllvm", "-amdgpu-kernarg-preload-count=10",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -312,6 +312,24 @@ __device__ __forceinline__ void stage_v(const Tile<D, NB, KV> &t, int r, int grp
             }
 }
 
+// Zero the V rows of a tile at or past key `len` (the tile's first key is t0):
+// a tile loaded against the cache capacity instead of the length holds
+// whatever lies beyond the sequence there, and p = 0 must meet a finite V.
+template <int D, int NB, int KV>
+__device__ __forceinline__ void zero_v_past(Tile<D, NB, KV> &t, int t0, int len, int grp) {
+    using T = Tile<D, NB, KV>;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool keep = t0 + 16 * blk + 4 * grp + j < len;
+#pragma unroll
+            for (int c = 0; c < Shape<D>::VC; ++c)
+#pragma unroll
+                for (int w = 0; w < T::VWL; ++w) t.v[blk][j][c][w] = keep ? t.v[blk][j][c][w] : 0u;
+        }
+}
+
 // QK^T and the online-softmax update for one tile whose first key has index
 // `t0` in the sequence (keys at or beyond `t_end`, this lane's row limit,
 // masked).  On return
@@ -454,9 +472,10 @@ __device__ __forceinline__ void lse_merge(float &m, float &l, f32x4_t &o, float 
 }
 
 // Minimum waves per SIMD the compiler must leave room for: the single-buffer
-// variants rely on more resident waves for their latency hiding.
-template <int D, bool DBUF>
-constexpr int kMinWavesPerEu = DBUF ? 1 : (D >= 256 ? 2 : 4);
+// variants rely on more resident waves for their latency hiding; a 16 KB
+// tile (D * NB = 256) needs the registers of two waves per SIMD.
+template <int D, int NB, bool DBUF>
+constexpr int kMinWavesPerEu = DBUF ? 1 : (D * NB >= 256 ? 2 : 4);
 
 // ------------------------------------------------------------ work partition
 //
@@ -574,6 +593,33 @@ __device__ __forceinline__ long long share_of(long long x, long long N, long lon
     return ((x + 1) * P + N - 1) / N - 1;
 }
 
+// Q of the R = M * G query rows of kv head kvh of sequence b (row r = i * G + g:
+// query token i, head kvh * G + g), exact bf16, in the QK^T B operand layout.
+// i = r / G by a multiply (qdiv = ceil(256 / G): exact for r, G <= 16); the
+// row index fits 32 bits (B * M * Hq * D <= INT32_MAX, checked on the host).
+// Columns r >= R load row R - 1 (no branch around the loads) and are zeroed.
+template <int D, int KV>
+__device__ __forceinline__ void load_q(const SplitArgs &a, int b, int kvh, int r, int grp,
+                                       bf16x8_t (&qb)[Shape<D>::KB]) {
+    const int rq = min(r, a.R - 1);
+    const int qi = (rq * a.qdiv) >> 8;
+    const int qg = rq - qi * a.G;
+    const int qrow = ((b * a.M + qi) * a.Hq + kvh * a.G + qg) * D + kslot_lane<KV>(grp);
+#pragma unroll
+    for (int kb = 0; kb < Shape<D>::KB; ++kb) {
+        u32x4_t x = *reinterpret_cast<const u32x4_t *>(a.q + qrow + kslot_block<KV>(kb));
+        if (r >= a.R) x = u32x4_t{0u, 0u, 0u, 0u};
+        qb[kb] = __builtin_bit_cast(bf16x8_t, x);
+    }
+}
+
+// What a wave loads before its key range is known (see gqa_split_kernel).
+template <int D, int NB, int KV>
+struct Prefetch {
+    Tile<D, NB, KV> tile;
+    bf16x8_t qb[Shape<D>::KB];
+};
+
 // --------------------------------------------------------- one key range
 //
 // The workgroup's four waves process keys [t_begin, t_end) of segment
@@ -581,10 +627,14 @@ __device__ __forceinline__ long long share_of(long long x, long long N, long lon
 // keeps its own (m, l, acc), and the waves are folded in ascending order
 // through LDS into partial slot `slot` (or straight into `out` when direct).
 // Must be called by all threads of the workgroup; ends with a barrier, after
-// which LDS may be reused.
-template <int D, int NB, bool PAGED, int PV, bool DBUF, int CPOL, int KV>
+// which LDS may be reused.  SPEC: Q and the wave's first tile are already in
+// `pre`, the tile loaded against the cache capacity before the length was
+// known (contiguous cache, single register tile only).
+template <int D, int NB, bool PAGED, int PV, bool DBUF, int CPOL, int KV, bool SPEC = false>
 __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB> &lds, int b, int kvh,
-                                              int len, int t_begin, int t_end, size_t slot, bool direct) {
+                                              int len, int t_begin, int t_end, size_t slot, bool direct,
+                                              const Prefetch<D, NB, KV> *pre = nullptr) {
+    static_assert(!SPEC || (!PAGED && !DBUF && PV == kPvBf16), "speculative first tile: default contiguous pipeline");
     using S = Shape<D>;
     constexpr int TT = 16 * NB;  // keys per wave tile
     const int lane = threadIdx.x & 63;
@@ -595,24 +645,17 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
     const int ntiles = t_end > t_begin ? (t_end - t_begin + TT - 1) / TT : 0;
     const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
-    // Q of the R = M * G query rows of this kv head (row r = i * G + g: query
-    // token i, head kvh * G + g), exact bf16, in the QK B operand layout.
-    // i = r / G by a multiply (qdiv = ceil(256 / G): exact for r, G <= 16);
-    // the row index fits 32 bits (B * M * Hq * D <= INT32_MAX, checked on the host).
-    const int qi = (r * a.qdiv) >> 8;
-    const int qg = r - qi * a.G;
-    // Multi-query: query token i is position len - M + i and sees keys < len - M + i + 1.
-    const int row_end = min(t_end, len - a.M + qi + 1);
     bf16x8_t qb[S::KB];
-    {
-        const int qrow = ((b * a.M + qi) * a.Hq + kvh * a.G + qg) * D + kslot_lane<KV>(grp);
+    if constexpr (SPEC) {
 #pragma unroll
-        for (int kb = 0; kb < S::KB; ++kb) {
-            u32x4_t x = {0u, 0u, 0u, 0u};
-            if (r < a.R) x = *reinterpret_cast<const u32x4_t *>(a.q + qrow + kslot_block<KV>(kb));
-            qb[kb] = __builtin_bit_cast(bf16x8_t, x);
-        }
+        for (int kb = 0; kb < S::KB; ++kb) qb[kb] = pre->qb[kb];
+    } else {
+        load_q<D, KV>(a, b, kvh, r, grp, qb);
     }
+    // Multi-query: query token i (row r = i * G + g) is position len - M + i
+    // and sees keys < len - M + i + 1 (rows r >= R: any limit, never written).
+    const int qi = (min(r, a.R - 1) * a.qdiv) >> 8;
+    const int row_end = min(t_end, len - a.M + qi + 1);
 
     WaveState<D> st;
 #pragma unroll
@@ -675,7 +718,11 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
         // tile's V is in LDS, so they fly during the rest of the tile's math.
         // Half the registers of the double buffer, so more waves fit per SIMD.
         Tile<D, NB, KV> buf;
-        if (my_tiles > 0) issue(buf, 0, kLoadV | kLoadK);
+        if constexpr (SPEC) {
+            buf = pre->tile;
+        } else {
+            if (my_tiles > 0) issue(buf, 0, kLoadV | kLoadK);
+        }
         for (int it = 0; it < my_tiles; ++it) {
             const bool more = it + 1 < my_tiles;
             if constexpr (PV == kPvBf16) {
@@ -685,6 +732,10 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
                     // QK^T and the softmax run while V is still in flight.
                     qk_softmax(buf, qb, st, tile_start(it), row_end, grp, a.qk_scale_log2, sc);
                     if (more) issue(buf, it + 1, kLoadK);
+                    if constexpr (SPEC) {
+                        // rows past len were read from the capacity; K's are masked above
+                        if (tile_start(it) + TT > len) zero_v_past(buf, tile_start(it), len, grp);
+                    }
                     stage_v(buf, r, grp, stage);
                     if (more) issue(buf, it + 1, kLoadV);
                 } else {
@@ -784,17 +835,28 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
 }
 
 template <int D, int NB, bool PAGED, int PV, bool DBUF, int PART, int CPOL, int KV>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEu<D, DBUF>)))
-void gqa_split_kernel(const int32_t *seq_lens, int num_splits, int Hkv, int B, int cap, const SplitArgs args) {
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEu<D, NB, DBUF>)))
+void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const unsigned char *v, const uint16_t *q,
+                      int num_splits, int Hkv, int B, int cap, int split_tokens, int qpack, const SplitArgs args) {
     constexpr int TT = 16 * NB;
     __shared__ FoldLds<D, NB> lds;
-    // The leading scalar arguments arrive preloaded in SGPRs, so the length
-    // loads below issue without waiting for the kernel-argument fetch.
+    // The leading scalar arguments arrive preloaded in SGPRs, so the length,
+    // Q and first-tile loads below issue without waiting for the kernel-argument
+    // fetch.  qpack = G | M << 5 | R << 10 | qdiv << 15.
     SplitArgs a = args;
     a.seq_lens = seq_lens;
+    a.k = k;
+    a.v = v;
+    a.q = q;
     a.num_splits = num_splits;
     a.Hkv = Hkv;
     a.B = B;
+    a.split_tokens = split_tokens;
+    a.G = qpack & 31;
+    a.M = (qpack >> 5) & 31;
+    a.R = (qpack >> 10) & 31;
+    a.qdiv = qpack >> 15;
+    a.Hq = Hkv * a.G;
 
     if constexpr (PART == kPartitionEven) {
         // This workgroup's equal share of all tiles, walked piece by piece.
@@ -852,21 +914,44 @@ void gqa_split_kernel(const int32_t *seq_lens, int num_splits, int Hkv, int B, i
         }
         return;
     } else {
-        const int split = blockIdx.x % num_splits;
-        const int bk = blockIdx.x / num_splits;
-        const int kvh = bk % Hkv;
-        const int b = bk / Hkv;
+        const int b = blockIdx.x / (num_splits * Hkv);  // one division before the length load
         const int len_v = load_len_vmem(seq_lens, b);
         __builtin_amdgcn_sched_barrier(0);  // the length load goes out first
+        const int bk = blockIdx.x / num_splits;
+        const int split = blockIdx.x - bk * num_splits;
+        const int kvh = bk - b * Hkv;
+        const int t_begin = split * a.split_tokens;
+        const int nsplit = a.num_splits;
+        const bool direct = nsplit == 1;
+        // Contiguous cache: the wave's first tile does not wait for the length.
+        // It is loaded against the capacity (rows below S_max are the caller's
+        // memory) while the length is in flight; rows past the length are
+        // masked (K) and zeroed (V) once it is known.
+        constexpr bool kSpec = !PAGED && !DBUF && PV == kPvBf16;
+        Prefetch<D, NB, KV> pre;
+        if constexpr (kSpec) {
+            // No branch around the loads (so the wait for the length does not
+            // wait for them too): a tile at or past the capacity reads zeros
+            // through the buffer bounds, and its offsets stay below
+            // (S_max + 64) * D * bytes, which fits 32 bits.
+            constexpr int EB = KV == kKvFp8 ? 1 : 2;
+            const int t0 = t_begin + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * TT;
+            const int lane = threadIdx.x & 63;
+            load_q<D, KV>(a, b, kvh, lane & 15, lane >> 4, pre.qb);
+            const size_t base = ((size_t)b * a.Hkv + kvh) * (size_t)cap * D * EB;
+            const __amdgpu_buffer_rsrc_t rk =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, cap * D * EB, kRsrcWord3);
+            const __amdgpu_buffer_rsrc_t rv =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, cap * D * EB, kRsrcWord3);
+            load_tile<D, NB, CPOL, KV>(pre.tile, rk, rv, t0, lane & 15, lane >> 4, kLoadK | kLoadV);
+            __builtin_amdgcn_sched_barrier(0);  // ... and goes out before the wait for the length
+        }
         // Out-of-range lengths / page ids are clamped so that no access can leave
         // the caller's buffers (the results for such inputs are unspecified).
         const int len = min(max(__builtin_amdgcn_readfirstlane(len_v), 0), cap);
-        const int t_begin = split * a.split_tokens;
         const int t_end = min(len, t_begin + a.split_tokens);
-        const int nsplit = a.num_splits;
-        const bool direct = nsplit == 1;
-        process_range<D, NB, PAGED, PV, DBUF, CPOL, KV>(a, lds, b, kvh, len, t_begin, t_end,
-                                              (size_t)bk * nsplit + split, direct);
+        process_range<D, NB, PAGED, PV, DBUF, CPOL, KV, kSpec>(a, lds, b, kvh, len, t_begin, t_end,
+                                                               (size_t)bk * nsplit + split, direct, &pre);
     }
 }
 
@@ -1172,8 +1257,10 @@ hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, int kv, h
         const int cap = PAGED ? a.max_pages * a.page_size : a.S_max;
         const bool even = plan.partition == kPartitionEven;
         const bool nt = plan.streaming != 0;
+        const int qpack = a.G | a.M << 5 | a.R << 10 | a.qdiv << 15;  // each field <= 16, qdiv <= 256
         auto go = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, grid, block, 0, stream, a.seq_lens, a.num_splits, a.Hkv, a.B, cap, a);
+            hipLaunchKernelGGL(kernel, grid, block, 0, stream, a.seq_lens, a.k, a.v, a.q, a.num_splits, a.Hkv, a.B,
+                               cap, a.split_tokens, qpack, a);
         };
         if (kv == kKvFp8) {
             // The E4M3 cache always runs the default pipeline (bf16 PV, one register tile).
