@@ -456,6 +456,7 @@ struct FoldLds {
     float m[kWaves][kMaxHeadsPerKv];
     float l[kWaves][kMaxHeadsPerKv];
     alignas(16) unsigned char region[kWaves][kRegion];
+    f32x4_t p[kWaves][NB][64];  // one-tile ranges: each wave's probabilities, in its lane layout
     __device__ float *acc(int w) { return reinterpret_cast<float *>(region[w]); }
     __device__ unsigned short *stage(int w) { return reinterpret_cast<unsigned short *>(region[w]); }
 };
@@ -471,11 +472,12 @@ __device__ __forceinline__ void lse_merge(float &m, float &l, f32x4_t &o, float 
     m = mn;
 }
 
-// Minimum waves per SIMD the compiler must leave room for: the single-buffer
-// variants rely on more resident waves for their latency hiding; a 16 KB
-// tile (D * NB = 256) needs the registers of two waves per SIMD.
+// Minimum waves per SIMD the compiler must leave room for (256 VGPRs each at
+// two): the plans launch at most two workgroups of four waves per CU in the
+// even partition and one per CU for a single sequence, and both key-range
+// paths of a kernel must fit without spills at every head_dim and tile.
 template <int D, int NB, bool DBUF>
-constexpr int kMinWavesPerEu = DBUF ? 1 : (D * NB >= 256 ? 2 : 4);
+constexpr int kMinWavesPerEu = DBUF ? 1 : 2;
 
 // ------------------------------------------------------------ work partition
 //
@@ -834,6 +836,164 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
     __syncthreads();
 }
 
+// --------------------------------------------------- one tile per wave
+//
+// A key range of at most four tiles (the short splits that fill the CUs for a
+// single sequence): the four waves take one tile each, exchange their
+// probabilities and maxima through LDS, and then each wave computes PV over
+// all four tiles for its own quarter of the head dims.  There is no fold of
+// four accumulators afterwards: each wave writes its quarter of the range's
+// partial (or of the output) straight from the MFMA registers.
+//   m = max_w m_w,  c_w = 2^(m_w - m),  l = sum_w c_w l_w,
+//   acc[:, quarter] = sum_w (c_w P_w) V_w[:, quarter]   (ascending w).
+// Tile loads as in process_range; `pf` holds Q and the tile when SPEC.
+template <int D, int NB, bool PAGED, int CPOL, int KV, bool SPEC>
+__device__ __forceinline__ void process_single(const SplitArgs &a, FoldLds<D, NB> &lds, int b, int kvh, int len,
+                                               int t_begin, int t_end, size_t slot, bool direct,
+                                               Prefetch<D, NB, KV> &pf) {
+    using S = Shape<D>;
+    constexpr int TT = 16 * NB;
+    constexpr int NQ = D / 64;  // 16-dim blocks per quarter of the head dims
+    constexpr int RS = kStageStride<D>;
+    constexpr int EB = KV == kKvFp8 ? 1 : 2;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int r = lane & 15;
+    const int grp = lane >> 4;
+    const int t0 = t_begin + wave * TT;
+    const bool has = t0 < t_end;  // this wave's tile holds keys of the range
+    const int qi = (min(r, a.R - 1) * a.qdiv) >> 8;
+    const int row_end = min(t_end, len - a.M + qi + 1);
+
+    Tile<D, NB, KV> &tile = pf.tile;
+    if constexpr (!SPEC) {
+        load_q<D, KV>(a, b, kvh, r, grp, pf.qb);
+        if (has) {
+            if constexpr (PAGED) {
+                const int pidx = t0 / a.page_size;
+                const int page = min(max(a.page_table[(size_t)b * a.max_pages + pidx], 0), a.num_pages - 1);
+                const int rows = min(a.page_size, len - pidx * a.page_size);
+                const size_t base = ((size_t)page * a.Hkv + kvh) * (size_t)a.page_size * D * EB;
+                const __amdgpu_buffer_rsrc_t rk =
+                    __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, rows * D * EB, kRsrcWord3);
+                const __amdgpu_buffer_rsrc_t rv =
+                    __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, rows * D * EB, kRsrcWord3);
+                load_tile<D, NB, CPOL, KV>(tile, rk, rv, t0 - pidx * a.page_size, r, grp, kLoadK | kLoadV);
+            } else {
+                const size_t base = ((size_t)b * a.Hkv + kvh) * (size_t)a.S_max * D * EB;
+                const __amdgpu_buffer_rsrc_t rk =
+                    __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, len * D * EB, kRsrcWord3);
+                const __amdgpu_buffer_rsrc_t rv =
+                    __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, len * D * EB, kRsrcWord3);
+                load_tile<D, NB, CPOL, KV>(tile, rk, rv, t0, r, grp, kLoadK | kLoadV);
+            }
+        }
+    }
+
+    // This wave's tile: probabilities against its own maximum, V staged.
+    WaveState<D> st;  // fresh state: acc unused here
+#pragma unroll
+    for (int i = 0; i < S::NACC; ++i) st.acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    st.m = -INFINITY;
+    st.l = 0.f;
+    f32x4_t sc[NB];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) sc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    unsigned short *stage = lds.stage(wave);
+    if (has) {
+        qk_softmax(tile, pf.qb, st, t0, row_end, grp, a.qk_scale_log2, sc);
+        if (SPEC && t0 + TT > len) zero_v_past(tile, t0, len, grp);  // read against the capacity
+        stage_v(tile, r, grp, stage);
+    }
+    const float lsum = sum_rows(st.l);
+    if (grp == 0) {
+        lds.m[wave][r] = st.m;
+        lds.l[wave][r] = lsum;
+    }
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) lds.p[wave][blk][lane] = sc[blk];
+    __syncthreads();
+
+    // The range's maximum and sum for head r, and each tile's weight.
+    float mw[kWaves], lw[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        mw[w] = lds.m[w][r];
+        lw[w] = lds.l[w][r];
+    }
+    float M = mw[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mw[w]);
+    float L = 0.f;
+    float cw[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        // a tile without keys has m = -inf, l = 0 and is skipped below
+        cw[w] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+        L += cw[w] * lw[w];
+    }
+
+    // PV over the four tiles for this wave's quarter of the dims.
+    f32x4_t acc[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        if (t_begin + w * TT >= t_end) continue;  // uniform: that wave staged nothing
+        const unsigned short *wst = lds.stage(w);
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            const f32x4_t pw = lds.p[w][blk][lane] * cw[w];
+            bf16x4_t hi, lo;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                hi[i] = (__bf16)pw[i];
+                lo[i] = (__bf16)(pw[i] - (float)hi[i]);
+            }
+            const unsigned short *src = wst + (16 * blk + 4 * grp + (r >> 2)) * RS + 4 * (r & 3);
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                const int nb = wave * NQ + j;
+                const bf16x4_t av = __builtin_bit_cast(
+                    bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(src + 16 * nb)));
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, hi, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, lo, acc[j], 0, 0, 0);
+            }
+        }
+    }
+    if constexpr (KV == kKvFp8) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) acc[j] *= a.v_scale;  // dequantised V sums
+    }
+
+    // Lane (r, grp) holds row r, dims 16*nb + 4*grp .. + 3 of each block nb.
+    if (r < a.R) {
+        const int G = a.R;
+        if (direct) {
+            const int i = r / a.G;  // row r = query token i, head kvh * G + (r - i * G)
+            float *orow = a.out + (((size_t)b * a.M + i) * a.Hq + (size_t)kvh * a.G + (r - i * a.G)) * D;
+#pragma unroll
+            for (int j = 0; j < NQ; ++j)
+                *reinterpret_cast<f32x4_t *>(orow + 16 * (wave * NQ + j) + 4 * grp) =
+                    L > 0.f ? acc[j] / L : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        } else {
+            // device-scope stores, as in process_range
+            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(a.part_acc + slot * G * D), (short)0, G * D * 4, kRsrcWord3);
+#pragma unroll
+            for (int j = 0; j < NQ; ++j)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[j]), ra,
+                                                       (r * D + 16 * (wave * NQ + j) + 4 * grp) * 4, 0, kDeviceScope);
+            if (wave == 0 && grp == 0) {
+                const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(a.part_ml + slot * G * 2), (short)0, G * 2 * 4, kRsrcWord3);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(M), __float_as_uint(L)}, rm, r * 8, 0,
+                                                      kDeviceScope);
+            }
+        }
+    }
+}
+
 template <int D, int NB, bool PAGED, int PV, bool DBUF, int PART, int CPOL, int KV>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEu<D, NB, DBUF>)))
 void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const unsigned char *v, const uint16_t *q,
@@ -950,8 +1110,13 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
         // the caller's buffers (the results for such inputs are unspecified).
         const int len = min(max(__builtin_amdgcn_readfirstlane(len_v), 0), cap);
         const int t_end = min(len, t_begin + a.split_tokens);
-        process_range<D, NB, PAGED, PV, DBUF, CPOL, KV, kSpec>(a, lds, b, kvh, len, t_begin, t_end,
-                                                               (size_t)bk * nsplit + split, direct, &pre);
+        const size_t slot = (size_t)bk * nsplit + split;
+        if (!DBUF && PV == kPvBf16 && a.split_tokens <= kWaves * TT) {
+            process_single<D, NB, PAGED, CPOL, KV, kSpec>(a, lds, b, kvh, len, t_begin, t_end, slot, direct, pre);
+        } else {
+            process_range<D, NB, PAGED, PV, DBUF, CPOL, KV, kSpec>(a, lds, b, kvh, len, t_begin, t_end, slot, direct,
+                                                                   &pre);
+        }
     }
 }
 
