@@ -461,17 +461,6 @@ struct FoldLds {
     __device__ unsigned short *stage(int w) { return reinterpret_cast<unsigned short *>(region[w]); }
 };
 
-// Folds partial (m2, l2, o2) into the running (m, l, o) with the log-sum-exp rescale.
-__device__ __forceinline__ void lse_merge(float &m, float &l, f32x4_t &o, float m2, float l2, f32x4_t o2) {
-    const float mn = fmaxf(m, m2);
-    if (mn == -INFINITY) return;
-    const float wa = __builtin_amdgcn_exp2f(m - mn);
-    const float wb = __builtin_amdgcn_exp2f(m2 - mn);
-    l = l * wa + l2 * wb;
-    o = o * wa + o2 * wb;
-    m = mn;
-}
-
 // Minimum waves per SIMD the compiler must leave room for (256 VGPRs each at
 // two): the plans launch at most two workgroups of four waves per CU in the
 // even partition and one per CU for a single sequence, and both key-range
@@ -1125,46 +1114,18 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
 // pieces s with s % NSG == sg (NSG = 256 / NCOL).  It loads U of its pieces
 // at a time and folds each round into its running (m, l, o) against the
 // round's maximum (independent exponentials, not a chain of merges).  The
-// NSG folds of a column are then merged with the log-sum-exp rescale in a
-// fixed tree: inside each wave over the lanes that share c (row rotations,
-// then the row-pair and half-wave swaps), then the four waves in order
-// through LDS.  Every step has a fixed order, so the result is
-// bit-reproducible.
+// NSG folds of a column are then combined max first: the column's maximum M
+// over the workgroup (a max tree inside each wave over the lanes that share c,
+// row rotations then the row-pair and half-wave swaps, and the four waves
+// through LDS), each fold rescaled once by 2^(m - M), and the rescaled (l, o)
+// summed by the same tree and then the four waves in order.  Every step has a
+// fixed order, so the result is bit-reproducible.
 constexpr int kCombineThreads = 256;
 
 struct Fold {
     float m, l;
     f32x4_t o;
 };
-
-__device__ __forceinline__ void merge_into(Fold &x, const Fold &y) { lse_merge(x.m, x.l, x.o, y.m, y.l, y.o); }
-
-// Merges the fold of lane (i - n) mod 16 of the row into this lane's.
-__device__ __forceinline__ void merge_ror(Fold &x, int n) {
-    Fold y;
-    y.m = row_ror(x.m, n);
-    y.l = row_ror(x.l, n);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) y.o[i] = row_ror(x.o[i], n);
-    merge_into(x, y);
-}
-
-// Merges the folds of the two rows of a row pair (16-lane rows 2k, 2k+1), or
-// of the two halves of the wave: both lanes of a pair compute the same value.
-template <bool HALVES>
-__device__ __forceinline__ void merge_swap(Fold &x) {
-    auto pair = [](float v) { return HALVES ? halves32(v) : rows16(v); };
-    const LanePair m = pair(x.m), l = pair(x.l);
-    Fold lo{m.lo, l.lo, {}}, hi{m.hi, l.hi, {}};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const LanePair o = pair(x.o[i]);
-        lo.o[i] = o.lo;
-        hi.o[i] = o.hi;
-    }
-    merge_into(lo, hi);
-    x = lo;
-}
 
 template <int NCOL, int PART>
 __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const float *part_acc, const float *part_ml,
@@ -1258,35 +1219,60 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
         }
     }
 
-    // Lanes of one column inside a wave: c, c + NCOL, ... (64 / NCOL of them).
-    if constexpr (NCOL == 4) merge_ror(run, 4);
-    if constexpr (NCOL <= 8) merge_ror(run, 8);
-    merge_swap<false>(run);
-    merge_swap<true>(run);
-
-    // The four waves, in order (lane c of each wave holds its column c).
+    // The column's maximum: lanes of one column inside a wave are c, c + NCOL,
+    // ... (64 / NCOL of them), then the four waves through LDS.
     __shared__ float wm[kWaves][NCOL], wl[kWaves][NCOL];
     __shared__ f32x4_t wo[kWaves][NCOL];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float mx = run.m;
+    if constexpr (NCOL == 4) mx = fmaxf(mx, row_ror(mx, 4));
+    if constexpr (NCOL <= 8) mx = fmaxf(mx, row_ror(mx, 8));
+    {
+        LanePair q = rows16(mx);
+        q = halves32(fmaxf(q.lo, q.hi));
+        mx = fmaxf(q.lo, q.hi);
+    }
+    if (lane < NCOL) wm[wave][lane] = mx;
+    __syncthreads();
+    float M = wm[0][c];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w][c]);
+
+    // Each fold rescaled to M once (an empty fold, m = -inf, weighs 0), then
+    // the sums: the same tree inside the wave, the waves in order.
+    const float wt = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(run.m - M);
+    float sl = run.l * wt;
+    f32x4_t so = run.o * wt;
+    auto add_ror = [&](int n) {
+        sl += row_ror(sl, n);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) so[i] += row_ror(so[i], n);
+    };
+    if constexpr (NCOL == 4) add_ror(4);
+    if constexpr (NCOL <= 8) add_ror(8);
+    auto add_swap = [&](auto pair) {
+        LanePair q = pair(sl);
+        sl = q.lo + q.hi;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            q = pair(so[i]);
+            so[i] = q.lo + q.hi;
+        }
+    };
+    add_swap([](float v) { return rows16(v); });
+    add_swap([](float v) { return halves32(v); });
     if (lane < NCOL) {
-        wm[wave][lane] = run.m;
-        wl[wave][lane] = run.l;
-        wo[wave][lane] = run.o;
+        wl[wave][lane] = sl;
+        wo[wave][lane] = so;
     }
     __syncthreads();
     if (threadIdx.x < NCOL) {
-        float M = wm[0][c];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w][c]);
         float L = 0.f;
         f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-        if (M != -INFINITY) {
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float wt = __builtin_amdgcn_exp2f(wm[w][c] - M);
-                L += wt * wl[w][c];
-                O += wt * wo[w][c];
-            }
+        for (int w = 0; w < kWaves; ++w) {
+            L += wl[w][c];
+            O += wo[w][c];
         }
         // row h = kvh * G + i * Gh + gh of sequence b is out[b][i][kvh * Gh + gh]
         size_t orow = bh;
