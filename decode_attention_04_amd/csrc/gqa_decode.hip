@@ -134,6 +134,7 @@ __device__ __forceinline__ float sum_rows(float x) {
 // x of lane (i - n) mod 16 in this lane's row of 16.
 __device__ __forceinline__ float row_ror(float x, int n) {
     switch (n) {
+        case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));
         case 4: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
         case 8: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
         default: return x;
@@ -1139,7 +1140,7 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
     a.G = G_arg;
     a.Hq = Hq;
     a.D = D_arg;
-    static_assert(NCOL == 4 || NCOL == 8 || NCOL == 16, "lanes of one column must share rows of 16");
+    static_assert(NCOL == 2 || NCOL == 4 || NCOL == 8 || NCOL == 16, "lanes of one column must share rows of 16");
     constexpr int NSG = kCombineThreads / NCOL;
     constexpr int U = 4;  // pieces per thread per round of loads
     const int D = a.D;
@@ -1225,7 +1226,8 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
     __shared__ f32x4_t wo[kWaves][NCOL];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float mx = run.m;
-    if constexpr (NCOL == 4) mx = fmaxf(mx, row_ror(mx, 4));
+    if constexpr (NCOL <= 2) mx = fmaxf(mx, row_ror(mx, 2));
+    if constexpr (NCOL <= 4) mx = fmaxf(mx, row_ror(mx, 4));
     if constexpr (NCOL <= 8) mx = fmaxf(mx, row_ror(mx, 8));
     {
         LanePair q = rows16(mx);
@@ -1248,7 +1250,8 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
 #pragma unroll
         for (int i = 0; i < 4; ++i) so[i] += row_ror(so[i], n);
     };
-    if constexpr (NCOL == 4) add_ror(4);
+    if constexpr (NCOL <= 2) add_ror(2);
+    if constexpr (NCOL <= 4) add_ror(4);
     if constexpr (NCOL <= 8) add_ror(8);
     auto add_swap = [&](auto pair) {
         LanePair q = pair(sl);
@@ -1377,15 +1380,15 @@ hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const f
     const int rows = M * Hq;
     CombineArgs ca{part_acc, part_ml, out, seq_lens, D, rows / Hkv, rows, plan.num_splits,
                    B, Hkv, cap, plan.tile_tokens, plan.grid, M, Hq / Hkv};
-    // The widest dim chunk (NCOL = 16, 8 or 4 columns of 4 dims) that still
-    // gives at least 128 workgroups: narrower chunks put more threads on the
-    // pieces of a column (measured best for few heads with many pieces).
-    // GQA_DECODE_COMBINE_COLS = 4, 8 or 16 overrides it.
+    // The widest dim chunk (NCOL = 16, 8, 4 or 2 columns of 4 dims) that
+    // still gives at least 128 workgroups: narrower chunks put more threads on
+    // the pieces of a column (measured best for few heads with many pieces).
+    // GQA_DECODE_COMBINE_COLS = 2, 4, 8 or 16 overrides it.
     const int64_t heads = (int64_t)B * rows;
     int ncol = env_int("GQA_DECODE_COMBINE_COLS", 0);
-    if (ncol != 4 && ncol != 8 && ncol != 16) {
+    if (ncol != 2 && ncol != 4 && ncol != 8 && ncol != 16) {
         ncol = 16;
-        while (ncol > 4 && heads * (D / (4 * ncol)) < 128) ncol /= 2;
+        while (ncol > 2 && heads * (D / (4 * ncol)) < 128) ncol /= 2;
     }
     const unsigned grid = (unsigned)(heads * (D / (4 * ncol)));
     auto go = [&](auto kernel) {
@@ -1395,7 +1398,8 @@ hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const f
     const bool even = plan.partition == kPartitionEven;
     if (ncol == 16) even ? go(gqa_combine_kernel<16, kPartitionEven>) : go(gqa_combine_kernel<16, kPartitionFixed>);
     else if (ncol == 8) even ? go(gqa_combine_kernel<8, kPartitionEven>) : go(gqa_combine_kernel<8, kPartitionFixed>);
-    else even ? go(gqa_combine_kernel<4, kPartitionEven>) : go(gqa_combine_kernel<4, kPartitionFixed>);
+    else if (ncol == 4) even ? go(gqa_combine_kernel<4, kPartitionEven>) : go(gqa_combine_kernel<4, kPartitionFixed>);
+    else even ? go(gqa_combine_kernel<2, kPartitionEven>) : go(gqa_combine_kernel<2, kPartitionFixed>);
     return hipGetLastError();
 }
 

@@ -195,7 +195,7 @@ def test_shared_workspace_across_plans():
         compare(od.cpu().numpy(), ra, "plan A, 37 splits")
 
 
-@pytest.mark.parametrize("cols", ["4", "8", "16"])
+@pytest.mark.parametrize("cols", ["2", "4", "8", "16"])
 def test_combine_column_widths(monkeypatch, cols):
     """Every combine width (lanes of a column merged by row rotations, row-pair and
     half-wave swaps, then the waves) matches the oracle and is bit-exact across runs,
