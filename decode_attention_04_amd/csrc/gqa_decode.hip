@@ -500,6 +500,19 @@ __device__ __forceinline__ int load_len_vmem(const int32_t *seq_lens, int b) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, b * 4, 0, 0);
 }
 
+// seq_lens[b] for a b that may be B (no such sequence: 0), through the buffer bounds.
+__device__ __forceinline__ int load_len_or_zero(const int32_t *seq_lens, int b, int B) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)seq_lens, (short)0, B * 4, kRsrcWord3);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, b * 4, 0, 0);
+}
+
+// page_table[b][i] for a b that may be B and an i that may be past max_pages (0 then).
+__device__ __forceinline__ int load_page_or_zero(const int32_t *page_table, int b, int i, int B, int max_pages) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(page_table + (size_t)b * max_pages), (short)0, b < B ? max_pages * 4 : 0, kRsrcWord3);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0);
+}
+
 // Sum over the wave of an int (every lane gets the result).
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
@@ -621,11 +634,13 @@ struct Prefetch {
 // Must be called by all threads of the workgroup; ends with a barrier, after
 // which LDS may be reused.  SPEC: Q and the wave's first tile are already in
 // `pre`, the tile loaded against the cache capacity before the length was
-// known (contiguous cache, single register tile only).
+// known (contiguous cache, single register tile only).  Paged: with have_pages,
+// pages0 already holds the page ids of the wave's first 64 tiles (t_begin = 0).
 template <int D, int NB, bool PAGED, int PV, bool DBUF, int CPOL, int KV, bool SPEC = false>
 __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB> &lds, int b, int kvh,
                                               int len, int t_begin, int t_end, size_t slot, bool direct,
-                                              const Prefetch<D, NB, KV> *pre = nullptr) {
+                                              const Prefetch<D, NB, KV> *pre = nullptr, bool have_pages = false,
+                                              int pages0 = 0) {
     static_assert(!SPEC || (!PAGED && !DBUF && PV == kPvBf16), "speculative first tile: default contiguous pipeline");
     using S = Shape<D>;
     constexpr int TT = 16 * NB;  // keys per wave tile
@@ -669,7 +684,11 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
             if (t0 < min(t_end, cap)) page_vec = a.page_table[(size_t)b * a.max_pages + t0 / a.page_size];
         }
     };
-    load_pages(0);
+    if (have_pages) {
+        page_vec = pages0;
+    } else {
+        load_pages(0);
+    }
     auto issue = [&](Tile<D, NB, KV> &tile, int it, int parts) {
         const int t0 = t_begin + (wave + kWaves * it) * TT;
         if constexpr (PAGED) {
@@ -1043,23 +1062,49 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
         const int rel = (int)(cur - loc.before);  // < Hkv * nb_tiles
         int kvh = __builtin_amdgcn_readfirstlane(rel / nb_tiles);
         int off = __builtin_amdgcn_readfirstlane(rel - kvh * nb_tiles);
+        // Paged: a share that runs on into the next segment (tile 0 of
+        // (b, kvh + 1) or (b + 1, 0)) loads that segment's length and the page
+        // ids of its first tiles when the current piece starts, so that the
+        // next piece's first loads do not wait for them (measured: 3% faster on
+        // batches of short paged sequences; no gain, and a loss, contiguous).
+        bool have_pages = false;
+        int pages = 0;
         while (cur < end) {
             const int take = (int)min((long long)(nb_tiles - off), end - cur);
             const size_t slot = (size_t)blockIdx.x + (size_t)b * a.Hkv + kvh;
+            const bool has_next = cur + take < end;
+            const bool same_b = kvh + 1 < a.Hkv;
+            const int nb = same_b ? b : b + 1;
+            int next_len = len;
+            int next_pages = 0;
+            if (PAGED && has_next) {
+                if (!same_b) next_len = load_len_or_zero(a.seq_lens, nb, a.B);
+                next_pages = load_page_or_zero(a.page_table, nb,
+                                               ((int)(threadIdx.x >> 6) + kWaves * lane) * TT / a.page_size, a.B,
+                                               a.max_pages);
+            }
             process_range<D, NB, PAGED, PV, DBUF, CPOL, KV>(a, lds, b, kvh, len, off * TT, min(len, (off + take) * TT),
-                                                  slot, false);
+                                                            slot, false, nullptr, have_pages, pages);
             cur += take;
             off += take;
+            have_pages = false;
             if (off == nb_tiles && cur < end) {
                 off = 0;
-                if (++kvh == a.Hkv) {
+                const int nlen = PAGED ? min(max(__builtin_amdgcn_readfirstlane(next_len), 0), cap) : 0;
+                if (nlen > 0) {  // the segment loaded ahead
+                    b = nb;
+                    kvh = same_b ? kvh + 1 : 0;
+                    len = nlen;
+                    pages = next_pages;
+                    have_pages = true;
+                } else if (++kvh == a.Hkv) {
                     kvh = 0;
                     do {  // sequences of length 0 hold no tiles
                         ++b;
                         len = b < a.B ? __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens, b, cap)) : 1;
                     } while (len == 0);
-                    nb_tiles = (len + TT - 1) / TT;
                 }
+                nb_tiles = (len + TT - 1) / TT;
             }
         }
         return;
