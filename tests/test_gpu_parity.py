@@ -129,7 +129,8 @@ def test_paged_matrix(ps, D):
     case = W.paged_case(len(lens), 16, 4, D, ps, 200, seq_lens=lens, max_len=704, seed=ps + D)
     dc = DeviceCase(case)
     ref = oracle_out(case)
-    for splits in (0, 1, 5):
+    # 100 splits (clamped to the tile count): one tile per wave, the lock-step path
+    for splits in (0, 1, 5, 100):
         compare(dc.run_host(splits), ref, f"paged ps={ps} D={D} splits={splits}")
 
 
@@ -149,9 +150,11 @@ def test_paged_equals_contiguous_bitwise():
             v_pool[pg] = c.v[b, :, i * ps:(i + 1) * ps]
             table[b, i] = pg
     p = W.Case("paged_copy", B, Hq, Hkv, D, c.scale, c.q, k_pool, v_pool, c.seq_lens, table, ps)
-    a = DeviceCase(c).run_host()
-    b = DeviceCase(p).run_host()
-    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # even shares; fixed splits of several tiles; one tile per wave (64 splits of 16 keys)
+    for splits in (0, 7, 64):
+        a = DeviceCase(c).run_host(splits)
+        b = DeviceCase(p).run_host(splits)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"splits={splits}"
 
 
 def test_paged_page_permutation_bitwise():
