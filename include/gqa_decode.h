@@ -108,6 +108,9 @@ size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int max_
  *   v_cache  bf16 [B][Hkv][S_max][head_dim]
  *   seq_lens int32 [B], each in [0, S_max]
  *   out      fp32 [B][Hq][head_dim]  (written)
+ *   The whole [S_max] extent of every (b, kv head) must be readable: rows at
+ *   or past seq_lens[b] may be loaded (one tile's worth, before the length is
+ *   known) but never contribute to the result, whatever they hold (NaN too).
  *   workspace: at least gqa_decode_workspace_bytes(B, Hq, Hkv, head_dim,
  *              S_max, 0, num_splits) bytes; may be NULL when that is 0.
  *              It needs no initialisation: it carries one call's partials
