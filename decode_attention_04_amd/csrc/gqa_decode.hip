@@ -1333,6 +1333,115 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
     }
 }
 
+// Combine for plans whose segments have few pieces (even shares of a batch,
+// a few fixed splits): one thread per (output row, 4 dims).  Each wave takes
+// 64 consecutive columns of one sequence; a thread loads the pieces of its
+// column kNarrowPieces at a time (one round when the segment has no more) and
+// folds each round in ascending order against the round's maximum.  No tree,
+// no LDS, no barrier.
+constexpr int kNarrowPieces = 16;
+
+template <int PART>
+__global__ __launch_bounds__(kCombineThreads) void gqa_combine_narrow_kernel(const float *part_acc,
+                                                                               const float *part_ml, int num_splits,
+                                                                               int G_arg, int Hq, int D_arg,
+                                                                               const CombineArgs args) {
+    CombineArgs a = args;
+    a.part_acc = part_acc;
+    a.part_ml = part_ml;
+    a.num_splits = num_splits;
+    a.G = G_arg;
+    a.Hq = Hq;
+    a.D = D_arg;
+    const int D = a.D;
+    const int cols = a.Hq * (D / 4);  // columns of one sequence
+    const int waves_per_b = (cols + 63) / 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = blockIdx.x * kWaves + (int)(threadIdx.x >> 6);
+    const int b = __builtin_amdgcn_readfirstlane(wave / waves_per_b);
+    if (b >= a.B) return;  // the whole wave
+    const int col = (wave - b * waves_per_b) * 64 + lane;
+    const bool active = col < cols;
+    const int h = active ? col / (D / 4) : 0;
+    const int d = 4 * (col - h * (D / 4));
+    const int G = a.G;
+    const size_t bk = (size_t)b * (a.Hq / G) + h / G;  // segment b * Hkv + kvh
+    const int g = h % G;
+    size_t lo;
+    int S;
+    long long N = 0, P = 1, w0 = 0;
+    bool maybe_empty = false;
+    if constexpr (PART == kPartitionFixed) {
+        S = a.num_splits;
+        lo = bk * S;
+    } else {
+        long long before, total;
+        prefix_tiles(a.seq_lens, a.B, a.Hkv, a.cap, a.tile, b, lane, before, total);
+        const int n = (clamp_len(a.seq_lens, b, a.cap) + a.tile - 1) / a.tile;
+        N = total;
+        P = a.shares;
+        maybe_empty = N < P;
+        if (n == 0) {
+            S = 0;
+            lo = 0;
+        } else {
+            const long long z = before + (long long)(h / G) * n;
+            w0 = share_of(z, N, P);
+            S = (int)(share_of(z + n - 1, N, P) - w0 + 1);
+            lo = (size_t)(w0 + (long long)bk);
+        }
+    }
+    if (!active) S = 0;
+    const float *ml = a.part_ml + (lo * G + g) * 2;
+    const float *acc = a.part_acc + (lo * G + g) * D + d;
+    const size_t ml_stride = (size_t)G * 2, acc_stride = (size_t)G * D;
+
+    float M = -INFINITY, L = 0.f;
+    f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += kNarrowPieces) {
+        float mv[kNarrowPieces], lv[kNarrowPieces];
+        f32x4_t av[kNarrowPieces];
+#pragma unroll
+        for (int u = 0; u < kNarrowPieces; ++u) {
+            const int s = s0 + u;
+            mv[u] = -INFINITY;
+            lv[u] = 0.f;
+            av[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // even partition: a share that holds no tile wrote nothing
+            const bool used = !maybe_empty || share_begin(w0 + s, N, P) < share_begin(w0 + s + 1, N, P);
+            if (s < S && used) {
+                const u32x2_t x = *reinterpret_cast<const u32x2_t *>(ml + s * ml_stride);
+                mv[u] = __uint_as_float(x[0]);
+                lv[u] = __uint_as_float(x[1]);
+                av[u] = *reinterpret_cast<const f32x4_t *>(acc + s * acc_stride);
+            }
+        }
+        float mr = M;
+#pragma unroll
+        for (int u = 0; u < kNarrowPieces; ++u) mr = fmaxf(mr, mv[u]);
+        if (mr != -INFINITY) {
+            const float wr = __builtin_amdgcn_exp2f(M - mr);
+            L *= wr;
+            O *= wr;
+#pragma unroll
+            for (int u = 0; u < kNarrowPieces; ++u) {
+                const float w = __builtin_amdgcn_exp2f(mv[u] - mr);
+                L += w * lv[u];
+                O += w * av[u];
+            }
+            M = mr;
+        }
+    }
+    if (!active) return;
+    // row h = kvh * G + i * Gh + gh of sequence b is out[b][i][kvh * Gh + gh]
+    size_t orow = (size_t)b * a.Hq + h;
+    if (a.M > 1) {
+        const int rho = h % G, i = rho / a.Gh;
+        orow = ((size_t)b * a.M + i) * (size_t)(a.Hq / a.M) + (size_t)(h / G) * a.Gh + (rho - i * a.Gh);
+    }
+    *reinterpret_cast<f32x4_t *>(a.out + orow * D + d) = L > 0.f ? O / L : f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
 // ------------------------------------------------------------------ host side
 
 constexpr int kMaxDevices = 64;
@@ -1430,6 +1539,21 @@ hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const f
     // the pieces of a column (measured best for few heads with many pieces).
     // GQA_DECODE_COMBINE_COLS = 2, 4, 8 or 16 overrides it.
     const int64_t heads = (int64_t)B * rows;
+    const bool even = plan.partition == kPartitionEven;
+    // Few pieces per segment (at full length): one thread per column folds
+    // them (no tree).  GQA_DECODE_COMBINE=tree keeps the tree for A/B runs.
+    const char *cmb = getenv("GQA_DECODE_COMBINE");
+    const bool tree_only = cmb != nullptr && strcmp(cmb, "tree") == 0;
+    if (!tree_only && plan.max_pieces <= kNarrowPieces) {
+        const int64_t waves = (int64_t)B * ((rows * (D / 4) + 63) / 64);
+        const unsigned grid = (unsigned)((waves + kWaves - 1) / kWaves);
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(kCombineThreads), 0, stream, ca.part_acc, ca.part_ml,
+                               ca.num_splits, ca.G, ca.Hq, ca.D, ca);
+        };
+        even ? go(gqa_combine_narrow_kernel<kPartitionEven>) : go(gqa_combine_narrow_kernel<kPartitionFixed>);
+        return hipGetLastError();
+    }
     int ncol = env_int("GQA_DECODE_COMBINE_COLS", 0);
     if (ncol != 2 && ncol != 4 && ncol != 8 && ncol != 16) {
         ncol = 16;
@@ -1440,7 +1564,6 @@ hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const f
         hipLaunchKernelGGL(kernel, dim3(grid), dim3(kCombineThreads), 0, stream, ca.part_acc, ca.part_ml,
                            ca.num_splits, ca.G, ca.Hq, ca.D, ca);
     };
-    const bool even = plan.partition == kPartitionEven;
     if (ncol == 16) even ? go(gqa_combine_kernel<16, kPartitionEven>) : go(gqa_combine_kernel<16, kPartitionFixed>);
     else if (ncol == 8) even ? go(gqa_combine_kernel<8, kPartitionEven>) : go(gqa_combine_kernel<8, kPartitionFixed>);
     else if (ncol == 4) even ? go(gqa_combine_kernel<4, kPartitionEven>) : go(gqa_combine_kernel<4, kPartitionFixed>);

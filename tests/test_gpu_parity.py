@@ -198,6 +198,30 @@ def test_shared_workspace_across_plans():
         compare(od.cpu().numpy(), ra, "plan A, 37 splits")
 
 
+@pytest.mark.parametrize("mode", ["default", "tree"])
+def test_combine_thread_per_column(monkeypatch, mode):
+    """Plans with few pieces per segment at full length use one thread per output column
+    (default); GQA_DECODE_COMBINE=tree forces the tree.  Both match the oracle and are
+    bit-exact across runs: even shares whose short sequences make the long ones span more
+    than 16 shares (several rounds of loads per thread), paged shares, a few fixed splits,
+    and multi-query rows."""
+    say(f"[parity] combine {mode}")
+    if mode == "tree":
+        monkeypatch.setenv("GQA_DECODE_COMBINE", "tree")
+    lens = [4096, 3, 0, 17, 1, 2000] + [1] * 10
+    cases = [
+        (W.contig_case(16, 16, 4, 128, 4096, seq_lens=lens, seed=62), 0),
+        (W.paged_case(16, 32, 8, 128, 32, 3000, max_len=4096, seed=63), 0),
+        (W.contig_case(3, 24, 4, 256, 1500, seq_lens=[1500, 700, 3], seed=64, scale=1 / 16), 5),
+        (W.mq_case(16, 2, 16, 4, 128, 3000, seq_lens=[3000, 4, 0, 999, 1500, 2] + [2500] * 10, seed=65), 0),
+    ]
+    for case, splits in cases:
+        dc = DeviceCase(case)
+        runs = [dc.run_host(splits) for _ in range(2)]
+        compare(runs[0], oracle_out(case), f"{mode} {case.name} splits={splits}")
+        assert np.array_equal(runs[0].view(np.uint32), runs[1].view(np.uint32))
+
+
 @pytest.mark.parametrize("cols", ["2", "4", "8", "16"])
 def test_combine_column_widths(monkeypatch, cols):
     """Every combine width (lanes of a column merged by row rotations, row-pair and
