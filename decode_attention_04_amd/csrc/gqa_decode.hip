@@ -1340,9 +1340,10 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
 // folds each round in ascending order against the round's maximum.  No tree,
 // no LDS, no barrier.
 constexpr int kNarrowPieces = 16;
+constexpr int kNarrowThreads = 64;  // one wave per workgroup: the waves spread over every CU
 
 template <int PART>
-__global__ __launch_bounds__(kCombineThreads) void gqa_combine_narrow_kernel(const float *part_acc,
+__global__ __launch_bounds__(kNarrowThreads) void gqa_combine_narrow_kernel(const float *part_acc,
                                                                                const float *part_ml, int num_splits,
                                                                                int G_arg, int Hq, int D_arg,
                                                                                const CombineArgs args) {
@@ -1357,7 +1358,7 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_narrow_kernel(con
     const int cols = a.Hq * (D / 4);  // columns of one sequence
     const int waves_per_b = (cols + 63) / 64;
     const int lane = threadIdx.x & 63;
-    const int wave = blockIdx.x * kWaves + (int)(threadIdx.x >> 6);
+    const int wave = blockIdx.x;
     const int b = __builtin_amdgcn_readfirstlane(wave / waves_per_b);
     if (b >= a.B) return;  // the whole wave
     const int col = (wave - b * waves_per_b) * 64 + lane;
@@ -1546,10 +1547,9 @@ hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const f
     const bool tree_only = cmb != nullptr && strcmp(cmb, "tree") == 0;
     if (!tree_only && plan.max_pieces <= kNarrowPieces) {
         const int64_t waves = (int64_t)B * ((rows * (D / 4) + 63) / 64);
-        const unsigned grid = (unsigned)((waves + kWaves - 1) / kWaves);
         auto go = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, dim3(grid), dim3(kCombineThreads), 0, stream, ca.part_acc, ca.part_ml,
-                               ca.num_splits, ca.G, ca.Hq, ca.D, ca);
+            hipLaunchKernelGGL(kernel, dim3((unsigned)waves), dim3(kNarrowThreads), 0, stream, ca.part_acc,
+                               ca.part_ml, ca.num_splits, ca.G, ca.Hq, ca.D, ca);
         };
         even ? go(gqa_combine_narrow_kernel<kPartitionEven>) : go(gqa_combine_narrow_kernel<kPartitionFixed>);
         return hipGetLastError();
