@@ -87,6 +87,7 @@ struct SplitArgs {
     int page_size, max_pages;   // paged
     int num_pages;              // paged
     int num_splits, split_tokens;
+    int piece_cost;             // even partition: tiles a piece's start and fold are worth
     float qk_scale_log2;        // scale * log2(e) (times k_scale for an E4M3 cache)
     float v_scale;              // E4M3 cache: V's per-tensor scale
 };
@@ -100,6 +101,7 @@ struct CombineArgs {
     int B, Hkv, cap, tile;    // even partition: how the split kernel cut the tiles
     int shares;               // even partition: workgroups of the split kernel
     int M, Gh;                // query tokens per sequence, query heads per kv head (G = M * Gh)
+    int piece_cost;           // even partition: as in SplitArgs
 };
 
 __device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
@@ -536,25 +538,30 @@ __device__ __forceinline__ long long uniform64(long long x) {
     return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
-// Tile counts of the sequences: total tiles of all segments, and (for a
-// target tile position `x` < total) the sequence b whose segments hold it and
-// the number of tiles before that sequence's first segment.  Every lane of
-// the wave returns the same values.
+// A segment of n tiles spans n + K positions of the tile axis that even shares
+// cut (none when n = 0): K stands for what starting and folding a piece costs,
+// so that a share covering several short segments takes fewer tiles.
+__device__ __forceinline__ int seg_span(int n, int K) { return n > 0 ? n + K : 0; }
+
+// Positions of the sequences on that axis: the total of all segments, and
+// (for a target position `x` < total) the sequence b whose segments hold it
+// and the positions before that sequence's first segment.  Every lane of the
+// wave returns the same values.
 struct SegmentLocation {
-    long long total;   // N: tiles of all segments
-    int b;             // sequence holding tile x
+    long long total;   // N: positions of all segments
+    int b;             // sequence holding position x
     int len;           // its (clamped) length
-    long long before;  // tiles of all segments of sequences < b
+    long long before;  // positions of all segments of sequences < b
 };
 
 __device__ __forceinline__ SegmentLocation locate_tile(const int32_t *seq_lens, int B, int Hkv, int cap,
-                                                       int TT, long long x, int lane) {
+                                                       int TT, int K, long long x, int lane) {
     SegmentLocation loc{0, -1, 0, 0};
     long long run = 0;  // tiles of sequences before this chunk
     for (int c0 = 0; c0 < B; c0 += 64) {
         const int bb = c0 + lane;
         const int ln = bb < B ? clamp_len(seq_lens, bb, cap) : 0;
-        const int n = (ln + TT - 1) / TT;
+        const int n = seg_span((ln + TT - 1) / TT, K);
         const int incl = wave_scan(n, lane);
         const long long lo = (run + incl - n) * Hkv, hi = (run + incl) * Hkv;
         const unsigned long long hit = __ballot(bb < B && lo <= x && x < hi);
@@ -575,13 +582,13 @@ __device__ __forceinline__ SegmentLocation locate_tile(const int32_t *seq_lens, 
     return loc;
 }
 
-// Tiles of all segments before sequence b's first one, and of all segments.
-__device__ __forceinline__ void prefix_tiles(const int32_t *seq_lens, int B, int Hkv, int cap, int TT, int b,
+// Axis positions of all segments before sequence b's first one, and of all segments.
+__device__ __forceinline__ void prefix_tiles(const int32_t *seq_lens, int B, int Hkv, int cap, int TT, int K, int b,
                                              int lane, long long &before, long long &total) {
     long long run = 0, pre = 0;
     for (int c0 = 0; c0 < B; c0 += 64) {
         const int bb = c0 + lane;
-        const int n = bb < B ? (clamp_len(seq_lens, bb, cap) + TT - 1) / TT : 0;
+        const int n = bb < B ? seg_span((clamp_len(seq_lens, bb, cap) + TT - 1) / TT, K) : 0;
         const int cnt = wave_sum(bb < b ? n : 0);
         pre += cnt;
         run += wave_sum(n);
@@ -1028,15 +1035,17 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
     a.Hq = Hkv * a.G;
 
     if constexpr (PART == kPartitionEven) {
-        // This workgroup's equal share of all tiles, walked piece by piece.
+        // This workgroup's equal share of the tile axis (each segment's tiles
+        // plus K positions for its start and fold), walked piece by piece.
         const int lane = threadIdx.x & 63;
         const long long P = gridDim.x;
+        const int K = a.piece_cost;
         SegmentLocation loc;
         long long cur, end;
         if (a.B <= 64) {
             // one load of the lengths: the total, then this share's start
             const int ln = lane < a.B ? clamp_len(a.seq_lens, lane, cap) : 0;
-            const int n = (ln + TT - 1) / TT;
+            const int n = seg_span((ln + TT - 1) / TT, K);
             const int incl = wave_scan(n, lane);
             const long long N = uniform64((long long)__shfl(incl, 63, 64) * a.Hkv);
             cur = share_begin(blockIdx.x, N, P);
@@ -1050,18 +1059,18 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
             loc.len = __builtin_amdgcn_readfirstlane(__shfl(ln, l, 64));
             loc.before = uniform64((long long)__shfl(incl - n, l, 64) * a.Hkv);
         } else {
-            loc = locate_tile(a.seq_lens, a.B, a.Hkv, cap, TT, -1, lane);  // the total only
+            loc = locate_tile(a.seq_lens, a.B, a.Hkv, cap, TT, K, -1, lane);  // the total only
             cur = share_begin(blockIdx.x, loc.total, P);
             end = share_begin(blockIdx.x + 1, loc.total, P);
             if (cur >= end) return;
-            loc = locate_tile(a.seq_lens, a.B, a.Hkv, cap, TT, cur, lane);
+            loc = locate_tile(a.seq_lens, a.B, a.Hkv, cap, TT, K, cur, lane);
         }
         int b = loc.b;
         int len = loc.len;
-        int nb_tiles = (len + TT - 1) / TT;
-        const int rel = (int)(cur - loc.before);  // < Hkv * nb_tiles
-        int kvh = __builtin_amdgcn_readfirstlane(rel / nb_tiles);
-        int off = __builtin_amdgcn_readfirstlane(rel - kvh * nb_tiles);
+        int nb_tiles = (len + TT - 1) / TT;  // tiles of the segment; it spans nb_tiles + K positions
+        const int rel = (int)(cur - loc.before);  // < Hkv * (nb_tiles + K)
+        int kvh = __builtin_amdgcn_readfirstlane(rel / (nb_tiles + K));
+        int off = __builtin_amdgcn_readfirstlane(rel - kvh * (nb_tiles + K));
         // Paged: a share that runs on into the next segment (tile 0 of
         // (b, kvh + 1) or (b + 1, 0)) loads that segment's length and the page
         // ids of its first tiles when the current piece starts, so that the
@@ -1070,27 +1079,37 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
         bool have_pages = false;
         int pages = 0;
         while (cur < end) {
-            const int take = (int)min((long long)(nb_tiles - off), end - cur);
-            const size_t slot = (size_t)blockIdx.x + (size_t)b * a.Hkv + kvh;
-            const bool has_next = cur + take < end;
+            // off < nb_tiles + K here
             const bool same_b = kvh + 1 < a.Hkv;
             const int nb = same_b ? b : b + 1;
-            int next_len = len;
+            int next_len = 0;
             int next_pages = 0;
-            if (PAGED && has_next) {
-                if (!same_b) next_len = load_len_or_zero(a.seq_lens, nb, a.B);
-                next_pages = load_page_or_zero(a.page_table, nb,
-                                               ((int)(threadIdx.x >> 6) + kWaves * lane) * TT / a.page_size, a.B,
-                                               a.max_pages);
+            bool fetched = false;  // next_len / next_pages were loaded for segment (nb, ...)
+            if (off < nb_tiles) {
+                const int take = (int)min((long long)(nb_tiles - off), end - cur);
+                const size_t slot = (size_t)blockIdx.x + (size_t)b * a.Hkv + kvh;
+                const bool has_next = off + take == nb_tiles && cur + take + K < end;
+                if (PAGED && has_next) {
+                    next_len = same_b ? len : load_len_or_zero(a.seq_lens, nb, a.B);
+                    next_pages = load_page_or_zero(a.page_table, nb,
+                                                   ((int)(threadIdx.x >> 6) + kWaves * lane) * TT / a.page_size, a.B,
+                                                   a.max_pages);
+                    fetched = true;
+                }
+                process_range<D, NB, PAGED, PV, DBUF, CPOL, KV>(a, lds, b, kvh, len, off * TT,
+                                                                min(len, (off + take) * TT), slot, false, nullptr,
+                                                                have_pages, pages);
+                cur += take;
+                off += take;
             }
-            process_range<D, NB, PAGED, PV, DBUF, CPOL, KV>(a, lds, b, kvh, len, off * TT, min(len, (off + take) * TT),
-                                                            slot, false, nullptr, have_pages, pages);
-            cur += take;
-            off += take;
             have_pages = false;
-            if (off == nb_tiles && cur < end) {
+            if (off >= nb_tiles) {  // the segment's tiles are done: step over its K positions
+                cur += nb_tiles + K - off;
+                off = nb_tiles + K;
+            }
+            if (cur < end) {
                 off = 0;
-                const int nlen = PAGED ? min(max(__builtin_amdgcn_readfirstlane(next_len), 0), cap) : 0;
+                const int nlen = fetched ? min(max(__builtin_amdgcn_readfirstlane(next_len), 0), cap) : 0;
                 if (nlen > 0) {  // the segment loaded ahead
                     b = nb;
                     kvh = same_b ? kvh + 1 : 0;
@@ -1211,7 +1230,7 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
     } else {
         long long before, total;
         const int lane = threadIdx.x & 63;
-        prefix_tiles(a.seq_lens, a.B, a.Hkv, a.cap, a.tile, (int)b, lane, before, total);
+        prefix_tiles(a.seq_lens, a.B, a.Hkv, a.cap, a.tile, a.piece_cost, (int)b, lane, before, total);
         const int n = (clamp_len(a.seq_lens, (int)b, a.cap) + a.tile - 1) / a.tile;
         N = total;
         P = a.shares;
@@ -1220,7 +1239,8 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
             S = 0;
             lo = 0;
         } else {
-            const long long z = before + (long long)(h / G) * n;
+            // the segment's tiles are axis positions [z, z + n) (its K extra ones follow)
+            const long long z = before + (long long)(h / G) * seg_span(n, a.piece_cost);
             w0 = share_of(z, N, P);
             S = (int)(share_of(z + n - 1, N, P) - w0 + 1);
             lo = (size_t)(w0 + (long long)bk);
@@ -1377,7 +1397,7 @@ __global__ __launch_bounds__(kNarrowThreads) void gqa_combine_narrow_kernel(cons
         lo = bk * S;
     } else {
         long long before, total;
-        prefix_tiles(a.seq_lens, a.B, a.Hkv, a.cap, a.tile, b, lane, before, total);
+        prefix_tiles(a.seq_lens, a.B, a.Hkv, a.cap, a.tile, a.piece_cost, b, lane, before, total);
         const int n = (clamp_len(a.seq_lens, b, a.cap) + a.tile - 1) / a.tile;
         N = total;
         P = a.shares;
@@ -1386,7 +1406,8 @@ __global__ __launch_bounds__(kNarrowThreads) void gqa_combine_narrow_kernel(cons
             S = 0;
             lo = 0;
         } else {
-            const long long z = before + (long long)(h / G) * n;
+            // the segment's tiles are axis positions [z, z + n) (its K extra ones follow)
+            const long long z = before + (long long)(h / G) * seg_span(n, a.piece_cost);
             w0 = share_of(z, N, P);
             S = (int)(share_of(z + n - 1, N, P) - w0 + 1);
             lo = (size_t)(w0 + (long long)bk);
@@ -1446,6 +1467,7 @@ __global__ __launch_bounds__(kNarrowThreads) void gqa_combine_narrow_kernel(cons
 // ------------------------------------------------------------------ host side
 
 constexpr int kMaxDevices = 64;
+constexpr int kDefaultPieceCost = 4;
 std::atomic<int> g_cu_count[kMaxDevices];
 
 int env_int(const char *name, int fallback) {
@@ -1505,6 +1527,19 @@ WorkspaceLayout workspace_layout(int Hq, int Hkv, int D, int64_t slots) {
     return w;
 }
 
+// Even shares: axis positions a piece's start and fold are worth, added to
+// every segment's tiles (a piece's first-tile latency plus its fold take about
+// as long as K tiles of streaming).  GQA_DECODE_PIECE_COST overrides it for
+// A/B runs; the split and combine kernels of one call read the same value.
+int piece_cost() {
+    const char *s = getenv("GQA_DECODE_PIECE_COST");
+    if (s != nullptr && *s != '\0') {
+        const int v = atoi(s);
+        if (v >= 0 && v <= 1024) return v;
+    }
+    return kDefaultPieceCost;
+}
+
 // Tile buffering: one register tile per wave refilled early (the default;
 // it leaves room for twice the waves), or GQA_DECODE_DBUF=1 for two.
 int env_dbuf() {
@@ -1534,7 +1569,7 @@ hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const f
     // rows: M query tokens x Hq heads per sequence, M * G per (sequence, kv head)
     const int rows = M * Hq;
     CombineArgs ca{part_acc, part_ml, out, seq_lens, D, rows / Hkv, rows, plan.num_splits,
-                   B, Hkv, cap, plan.tile_tokens, plan.grid, M, Hq / Hkv};
+                   B, Hkv, cap, plan.tile_tokens, plan.grid, M, Hq / Hkv, piece_cost()};
     // The widest dim chunk (NCOL = 16, 8, 4 or 2 columns of 4 dims) that
     // still gives at least 128 workgroups: narrower chunks put more threads on
     // the pieces of a column (measured best for few heads with many pieces).
@@ -1631,6 +1666,7 @@ constexpr KvSpec kBf16Cache{kKvBf16, 1.f, 1.f};
 
 gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, int kv, void *workspace,
                  hipStream_t stream, int phases) {
+    a.piece_cost = piece_cost();
     if (!plan.direct) {
         WorkspaceLayout w = workspace_layout(a.M * a.Hq, a.Hkv, D, plan.slots);
         char *base = static_cast<char *>(workspace);
