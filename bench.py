@@ -187,8 +187,9 @@ def main():
         d.page_table = None if base.page_table is None else base.page_table.clone()
         sets[i] = d
     cap = case.capacity
-    plan = gd.gqa_decode_plan(case.B, case.M * case.Hq, case.Hkv, case.D, cap, case.page_size,
-                              args.splits, torch.cuda.get_device_properties(0).multi_processor_count)
+    plan_fn = gd.gqa_decode_plan_fp8 if case.kv == "fp8" else gd.gqa_decode_plan
+    plan = plan_fn(case.B, case.M * case.Hq, case.Hkv, case.D, cap, case.page_size,
+                   args.splits, torch.cuda.get_device_properties(0).multi_processor_count)
     need = gd.gqa_decode_workspace_bytes(case.B, case.M * case.Hq, case.Hkv, case.D, cap, case.page_size,
                                          args.splits)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
@@ -218,9 +219,11 @@ def main():
             gd.gqa_decode_partials(d.q, d.k, d.v, d.seq_lens, case.scale, out=outs[i % R],
                                    workspace=ws, num_splits=args.splits, stream=stream)
 
+    combine_fn = gd.gqa_decode_combine_fp8 if case.kv == "fp8" else gd.gqa_decode_combine
+
     def combine_only(i, stream):
-        gd.gqa_decode_combine(ws, sets[i % R].seq_lens, outs[i % R], case.B, case.Hq, case.Hkv,
-                              case.D, cap, case.page_size, args.splits, stream=stream)
+        combine_fn(ws, sets[i % R].seq_lens, outs[i % R], case.B, case.Hq, case.Hkv,
+                   case.D, cap, case.page_size, args.splits, stream=stream)
 
     cur = torch.cuda.current_stream()
 

@@ -10,6 +10,9 @@ Entry points mirror include/gqa_decode.h:
     gqa_paged_decode(q, k_pool, v_pool, seq_lens, page_table, scale, ...)
     gqa_decode_workspace_bytes(B, Hq, Hkv, head_dim, max_seq_len, page_size, num_splits)
     gqa_decode_plan(B, Hq, Hkv, head_dim, max_seq_len, page_size, num_splits, cu_count)
+    gqa_decode_partials / gqa_paged_decode_partials + gqa_decode_combine (the two kernels apart)
+    gqa_decode_fp8 / gqa_paged_decode_fp8 (+ _partials, gqa_decode_combine_fp8, gqa_decode_plan_fp8)
+    gqa_decode_mq / gqa_paged_decode_mq (M query tokens per sequence)
     gqa_status_string(code)
 bf16 tensors may be torch.bfloat16 or int16/uint16 views of the bit patterns.
 """
@@ -29,8 +32,8 @@ STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_
 EXPORTED = ("gqa_decode_plan", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_paged_decode",
             "gqa_decode_partials", "gqa_paged_decode_partials", "gqa_decode_combine",
             "gqa_decode_fp8", "gqa_paged_decode_fp8", "gqa_decode_fp8_partials",
-            "gqa_paged_decode_fp8_partials", "gqa_decode_mq", "gqa_paged_decode_mq",
-            "gqa_status_string")
+            "gqa_paged_decode_fp8_partials", "gqa_decode_plan_fp8", "gqa_decode_combine_fp8",
+            "gqa_decode_mq", "gqa_paged_decode_mq", "gqa_status_string")
 
 
 class GqaError(RuntimeError):
@@ -66,6 +69,8 @@ def load(path: str = LIB_PATH):
     vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.gqa_decode_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(Plan)]
     lib.gqa_decode_plan.restype = ci
+    lib.gqa_decode_plan_fp8.argtypes = lib.gqa_decode_plan.argtypes
+    lib.gqa_decode_plan_fp8.restype = ci
     lib.gqa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci, ci]
     lib.gqa_decode_workspace_bytes.restype = sz
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp, vp, sz, ci, vp]
@@ -79,6 +84,8 @@ def load(path: str = LIB_PATH):
     lib.gqa_paged_decode_partials.restype = ci
     lib.gqa_decode_combine.argtypes = [vp, sz, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp]
     lib.gqa_decode_combine.restype = ci
+    lib.gqa_decode_combine_fp8.argtypes = lib.gqa_decode_combine.argtypes
+    lib.gqa_decode_combine_fp8.restype = ci
     lib.gqa_decode_fp8.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, cf, cf, vp, vp, sz, ci, vp]
     lib.gqa_decode_fp8.restype = ci
     lib.gqa_paged_decode_fp8.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, cf, cf,
@@ -107,13 +114,20 @@ def gqa_status_string(code: int) -> str:
         return STATUS_NAMES.get(code, str(code))
 
 
-def gqa_decode_plan(B, Hq, Hkv, head_dim, max_seq_len, page_size=0, num_splits=0, cu_count=256):
+def gqa_decode_plan(B, Hq, Hkv, head_dim, max_seq_len, page_size=0, num_splits=0, cu_count=256,
+                    _entry="gqa_decode_plan"):
     p = Plan()
-    rc = load().gqa_decode_plan(B, Hq, Hkv, head_dim, max_seq_len, page_size, num_splits,
-                                cu_count, ctypes.byref(p))
+    rc = getattr(load(), _entry)(B, Hq, Hkv, head_dim, max_seq_len, page_size, num_splits,
+                                 cu_count, ctypes.byref(p))
     if rc != GQA_OK:
-        raise GqaError(rc, "gqa_decode_plan")
+        raise GqaError(rc, _entry)
     return p
+
+
+def gqa_decode_plan_fp8(B, Hq, Hkv, head_dim, max_seq_len, page_size=0, num_splits=0, cu_count=256):
+    """The plan of a call over an E4M3 cache (paged head_dim 128 takes 32-key tiles)."""
+    return gqa_decode_plan(B, Hq, Hkv, head_dim, max_seq_len, page_size, num_splits, cu_count,
+                           _entry="gqa_decode_plan_fp8")
 
 
 def gqa_decode_workspace_bytes(B, Hq, Hkv, head_dim, max_seq_len, page_size=0, num_splits=0):
@@ -351,15 +365,22 @@ def gqa_paged_decode_partials(q, k_pool, v_pool, seq_lens, page_table, scale, ou
 
 
 def gqa_decode_combine(workspace, seq_lens, out, B, Hq, Hkv, head_dim, max_seq_len, page_size=0,
-                       num_splits=0, stream=None):
+                       num_splits=0, stream=None, _entry="gqa_decode_combine"):
     """Fold the partials a *_partials call left in `workspace` into `out`."""
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = load().gqa_decode_combine(ws_ptr, ws_bytes,
-                                   _dev_ptr(seq_lens, "seq_lens", (_torch().int32,)), B, Hq, Hkv,
-                                   head_dim, max_seq_len, page_size, num_splits,
-                                   _dev_ptr(out, "out", (_torch().float32,)),
-                                   _stream_ptr(stream, out.device))
+    rc = getattr(load(), _entry)(ws_ptr, ws_bytes,
+                                 _dev_ptr(seq_lens, "seq_lens", (_torch().int32,)), B, Hq, Hkv,
+                                 head_dim, max_seq_len, page_size, num_splits,
+                                 _dev_ptr(out, "out", (_torch().float32,)),
+                                 _stream_ptr(stream, out.device))
     if rc != GQA_OK:
-        raise GqaError(rc, "gqa_decode_combine")
+        raise GqaError(rc, _entry)
     return out
+
+
+def gqa_decode_combine_fp8(workspace, seq_lens, out, B, Hq, Hkv, head_dim, max_seq_len, page_size=0,
+                           num_splits=0, stream=None):
+    """Fold the partials a gqa_*_fp8_partials call left in `workspace` into `out`."""
+    return gqa_decode_combine(workspace, seq_lens, out, B, Hq, Hkv, head_dim, max_seq_len,
+                              page_size, num_splits, stream, _entry="gqa_decode_combine_fp8")

@@ -1480,8 +1480,12 @@ int env_int(const char *name, int fallback) {
 // Keys per wave tile: 16 KB of K+V per wave (64 keys at D=64, 32 at D=128,
 // 16 at D=256).  GQA_DECODE_TILE (16, 32 or 64) overrides it for A/B runs
 // when the result stays within 16 KB.
-int tile_tokens_for(int D, bool double_buffer) {
-    const int dflt = double_buffer ? (D == 64 ? 64 : (D == 128 ? 32 : 16)) : (D == 64 ? 32 : 16);
+int tile_tokens_for(int D, bool double_buffer, bool paged, int elem_bytes) {
+    int dflt = double_buffer ? (D == 64 ? 64 : (D == 128 ? 32 : 16)) : (D == 64 ? 32 : 16);
+    // A paged E4M3 cache at head_dim 128: 32 keys, so that a wave still reads
+    // 4 KB of K (and of V) in one piece of a page, as a bf16 tile of 16 does
+    // (measured: the ragged 8k paged workload 80.2 -> 62.4 us per call).
+    if (!double_buffer && paged && elem_bytes == 1 && D == 128) dflt = 32;
     const int t = env_int("GQA_DECODE_TILE", dflt);
     if ((t == 16 || t == 32 || t == 64) && t * D <= 4096) return t;
     return dflt;
@@ -1702,15 +1706,19 @@ gqa_status_t check_common(const void *q, const void *k, const void *v, const int
     return GQA_OK;
 }
 
+gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_size, int num_splits,
+                       int cu_count, int elem_bytes, gqa_plan_t *plan);
+
+// elem_bytes: 2 for a bf16 cache, 1 for E4M3.
 gqa_status_t plan_for_call(int B, int Hq, int Hkv, int D, int cap, int page_size, int num_splits,
-                           gqa_plan_t *plan) {
+                           gqa_plan_t *plan, int elem_bytes = 2) {
     if (num_splits == 0) num_splits = env_splits();
     int cu = 256;
     if (num_splits == 0) {
         gqa_status_t s = device_cu_count(&cu);
         if (s != GQA_OK) return s;
     }
-    return gqa_decode_plan(B, Hq, Hkv, D, cap, page_size, num_splits, cu, plan);
+    return plan_impl(B, Hq, Hkv, D, cap, page_size, num_splits, cu, elem_bytes, plan);
 }
 
 }  // namespace
@@ -1719,6 +1727,20 @@ extern "C" {
 
 gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int page_size,
                              int num_splits, int cu_count, gqa_plan_t *plan) {
+    return plan_impl(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, cu_count, 2, plan);
+}
+
+gqa_status_t gqa_decode_plan_fp8(int B, int Hq, int Hkv, int D, int max_seq_len, int page_size,
+                                 int num_splits, int cu_count, gqa_plan_t *plan) {
+    return plan_impl(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, cu_count, 1, plan);
+}
+
+}  // extern "C"
+
+namespace {
+
+gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_size, int num_splits,
+                       int cu_count, int elem_bytes, gqa_plan_t *plan) {
     if (plan == nullptr) return GQA_ERR_NULL;
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_seq_len < 0 || page_size < 0 ||
         num_splits < 0 || cu_count <= 0)
@@ -1727,7 +1749,7 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
     if (page_size > 0 && page_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
 
     const int dbuf = env_dbuf();
-    int tt = tile_tokens_for(D, dbuf != 0);
+    int tt = tile_tokens_for(D, dbuf != 0, page_size > 0, elem_bytes);
     if (page_size > 0) {
         while (page_size % tt != 0) tt /= 2;  // a tile never straddles a page (tt >= 16)
     }
@@ -1804,6 +1826,12 @@ gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int
     return GQA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+// The bf16 plan: an upper bound for an E4M3 cache too (its longer paged tiles
+// give no more shares or splits).
 size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_seq_len, int page_size,
                                   int num_splits) {
     gqa_plan_t plan;
@@ -1838,7 +1866,7 @@ gqa_status_t decode_contig(const void *q, const void *k_cache, const void *v_cac
     if (((int64_t)S_max + 64) * D * eb > INT32_MAX) return GQA_ERR_SHAPE;  // 32-bit buffer offsets
     if (workspace != nullptr && misaligned(workspace, 16)) return GQA_ERR_ALIGN;
     gqa_plan_t plan;
-    s = plan_for_call(B, M * Hq, Hkv, D, S_max, 0, num_splits, &plan);
+    s = plan_for_call(B, M * Hq, Hkv, D, S_max, 0, num_splits, &plan, kv.type == kKvFp8 ? 1 : 2);
     if (s != GQA_OK) return s;
     if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
         return workspace == nullptr ? GQA_ERR_NULL : GQA_ERR_WORKSPACE;
@@ -1876,7 +1904,7 @@ gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
         return GQA_ERR_SHAPE;
     if (workspace != nullptr && misaligned(workspace, 16)) return GQA_ERR_ALIGN;
     gqa_plan_t plan;
-    s = plan_for_call(B, M * Hq, Hkv, D, max_pages * page_size, page_size, num_splits, &plan);
+    s = plan_for_call(B, M * Hq, Hkv, D, max_pages * page_size, page_size, num_splits, &plan, kv.type == kKvFp8 ? 1 : 2);
     if (s != GQA_OK) return s;
     if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
         return workspace == nullptr ? GQA_ERR_NULL : GQA_ERR_WORKSPACE;
@@ -1998,9 +2026,13 @@ gqa_status_t gqa_paged_decode_mq(const void *q, const void *k_pool, const void *
                         stream, kPhaseSplit | kPhaseCombine);
 }
 
-gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, const int32_t *seq_lens,
-                                int B, int Hq, int Hkv, int D, int max_seq_len, int page_size,
-                                int num_splits, float *out, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+gqa_status_t combine_impl(const void *workspace, size_t workspace_bytes, const int32_t *seq_lens, int B, int Hq,
+                          int Hkv, int D, int max_seq_len, int page_size, int num_splits, float *out,
+                          hipStream_t stream, int elem_bytes) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_seq_len < 0 || page_size < 0 ||
         num_splits < 0)
         return GQA_ERR_SHAPE;
@@ -2012,7 +2044,7 @@ gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, c
         (workspace != nullptr && misaligned(workspace, 16)))
         return GQA_ERR_ALIGN;
     gqa_plan_t plan;
-    gqa_status_t s = plan_for_call(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, &plan);
+    gqa_status_t s = plan_for_call(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, &plan, elem_bytes);
     if (s != GQA_OK) return s;
     if (plan.direct) return GQA_OK;  // the split kernel already wrote `out`
     if (workspace == nullptr) return GQA_ERR_NULL;
@@ -2028,6 +2060,24 @@ gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, c
         a.S_max = max_seq_len;
     }
     return run(plan, a, D, page_size > 0, kKvBf16, const_cast<void *>(workspace), stream, kPhaseCombine);
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status_t gqa_decode_combine(const void *workspace, size_t workspace_bytes, const int32_t *seq_lens,
+                                int B, int Hq, int Hkv, int D, int max_seq_len, int page_size,
+                                int num_splits, float *out, hipStream_t stream) {
+    return combine_impl(workspace, workspace_bytes, seq_lens, B, Hq, Hkv, D, max_seq_len, page_size, num_splits,
+                        out, stream, 2);
+}
+
+gqa_status_t gqa_decode_combine_fp8(const void *workspace, size_t workspace_bytes, const int32_t *seq_lens,
+                                    int B, int Hq, int Hkv, int D, int max_seq_len, int page_size,
+                                    int num_splits, float *out, hipStream_t stream) {
+    return combine_impl(workspace, workspace_bytes, seq_lens, B, Hq, Hkv, D, max_seq_len, page_size, num_splits,
+                        out, stream, 1);
 }
 
 const char *gqa_status_string(gqa_status_t status) {

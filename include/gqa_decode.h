@@ -198,7 +198,7 @@ gqa_status_t gqa_paged_decode_fp8(const void *q, const void *k_pool, const void 
                                   hipStream_t stream);
 
 /* The split kernel of gqa_decode_fp8 / gqa_paged_decode_fp8 alone (see the
- * *_partials entry points above); gqa_decode_combine folds their partials. */
+ * *_partials entry points above); gqa_decode_combine_fp8 folds their partials. */
 gqa_status_t gqa_decode_fp8_partials(const void *q, const void *k_cache, const void *v_cache,
                                      const int32_t *seq_lens, int B, int Hq, int Hkv, int head_dim,
                                      int S_max, float scale, float k_scale, float v_scale, float *out,
@@ -212,6 +212,25 @@ gqa_status_t gqa_paged_decode_fp8_partials(const void *q, const void *k_pool, co
                                            float k_scale, float v_scale, float *out,
                                            void *workspace, size_t workspace_bytes,
                                            int num_splits, hipStream_t stream);
+
+/*
+ * The plan of a call over an E4M3 cache (gqa_decode_plan's arguments and
+ * rules), and the combine of gqa_decode_fp8_partials /
+ * gqa_paged_decode_fp8_partials (gqa_decode_combine's arguments and rules).
+ * A paged E4M3 cache at head_dim 128 takes 32-key tiles where bf16 takes 16,
+ * so that a wave still reads 4 KB of K and of V in one piece of a page; the
+ * plan therefore depends on the element type, and the combine must recompute
+ * the plan of the partials call.  The workspace a bf16 call of the same
+ * shapes needs (gqa_decode_workspace_bytes) is always enough: longer tiles
+ * never give more shares or splits.
+ */
+gqa_status_t gqa_decode_plan_fp8(int B, int Hq, int Hkv, int head_dim, int max_seq_len, int page_size,
+                                 int num_splits, int cu_count, gqa_plan_t *plan);
+
+gqa_status_t gqa_decode_combine_fp8(const void *workspace, size_t workspace_bytes,
+                                    const int32_t *seq_lens, int B, int Hq, int Hkv, int head_dim,
+                                    int max_seq_len, int page_size, int num_splits, float *out,
+                                    hipStream_t stream);
 
 /*
  * Multi-query decode (verification of M drafted tokens in speculative

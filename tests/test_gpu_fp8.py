@@ -105,8 +105,11 @@ def test_fp8_paged(ps, D):
         compare(dc.run_host(splits), ref, f"fp8 paged ps={ps} D={D} splits={splits}")
 
 
-def test_fp8_paged_equals_contiguous_bitwise():
-    """The same bytes through the paged and the contiguous layout give identical bits."""
+def test_fp8_paged_equals_contiguous_bitwise(monkeypatch):
+    """The same bytes through the paged and the contiguous layout give identical bits under the
+    same plan.  By default a paged E4M3 cache at head_dim 128 takes 32-key tiles where the
+    contiguous one takes 16, so the tile is pinned to 16 for the bitwise comparison; the
+    default plans are checked against the oracle."""
     p = W.fp8_paged_case(3, 8, 2, 128, 32, 100, seq_lens=[700, 65, 1024], max_len=1024, seed=93)
     S_max = p.max_pages * p.page_size
     k = np.zeros((p.B, p.Hkv, S_max, p.D), np.uint8)
@@ -119,6 +122,11 @@ def test_fp8_paged_equals_contiguous_bitwise():
             v[b, :, i * p.page_size:(i + 1) * p.page_size] = p.v[page]
     c = W.Case("fp8_gathered", p.B, p.Hq, p.Hkv, p.D, p.scale, p.q, k, v, p.seq_lens, kv="fp8",
                k_scale=p.k_scale, v_scale=p.v_scale)
+    ref = oracle_out(p)
+    for splits in (0, 5):
+        compare(DeviceCase(p).run_host(splits), ref, f"fp8 paged, default plan, splits={splits}")
+        compare(DeviceCase(c).run_host(splits), ref, f"fp8 contiguous, default plan, splits={splits}")
+    monkeypatch.setenv("GQA_DECODE_TILE", "16")
     for splits in (0, 5):
         a = DeviceCase(p).run_host(splits)
         b = DeviceCase(c).run_host(splits)
@@ -154,7 +162,7 @@ def test_fp8_even_shares(monkeypatch):
 
 @pytest.mark.parametrize("paged", [False, True])
 def test_fp8_partials_then_combine_equals_one_call(paged):
-    """gqa_*_fp8_partials + gqa_decode_combine on one stream give the one-call result bit for bit."""
+    """gqa_*_fp8_partials + gqa_decode_combine_fp8 on one stream give the one-call result bit for bit."""
     if paged:
         case = W.fp8_paged_case(4, 32, 8, 128, 32, 200, seq_lens=[1000, 1, 555, 1024], max_len=1024,
                                 seed=96)
@@ -173,7 +181,7 @@ def test_fp8_partials_then_combine_equals_one_call(paged):
         else:
             gd.gqa_decode_fp8_partials(dc.q, dc.k, dc.v, dc.seq_lens, case.scale, case.k_scale,
                                        case.v_scale, out=out, workspace=ws, num_splits=splits)
-        gd.gqa_decode_combine(ws, dc.seq_lens, out, case.B, case.Hq, case.Hkv, case.D, cap, ps,
-                              splits)
+        gd.gqa_decode_combine_fp8(ws, dc.seq_lens, out, case.B, case.Hq, case.Hkv, case.D, cap, ps,
+                                  splits)
         torch.cuda.synchronize()
         assert np.array_equal(_bits(out.cpu().numpy()), _bits(dc.run_host(splits)))

@@ -272,3 +272,25 @@ def test_mq_workspace_is_the_plan_of_m_times_hq_rows():
     need = gd.gqa_decode_plan(1, 4 * 8, 2, 128, 64, 0, 2, 256).workspace_bytes
     assert need > 0
     assert call_decode_mq(None or gd.load(), ws_bytes=need - 1) == 5
+
+
+@pytest.mark.parametrize("shape", [
+    (32, 32, 8, 128, 8192, 32), (4, 8, 2, 128, 1024, 32), (1, 8, 1, 128, 131072, 64),
+    (3, 16, 4, 128, 640, 64), (2, 16, 2, 128, 4096, 16), (5, 24, 4, 256, 2048, 32),
+    (6, 16, 4, 64, 512, 32), (16, 32, 4, 128, 16384, 0)])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_fp8_plan_tiles_and_workspace_bound(shape, splits):
+    """The E4M3 plan takes 32-key tiles for a paged head_dim-128 cache (when the page holds
+    them) and 16 otherwise as bf16 does; its workspace never exceeds the bf16 plan's, which is
+    what gqa_decode_workspace_bytes reports for both."""
+    B, Hq, Hkv, D, cap, ps = shape
+    p16 = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, splits, 256)
+    p8 = gd.gqa_decode_plan_fp8(B, Hq, Hkv, D, cap, ps, splits, 256)
+    if ps > 0 and D == 128 and ps % 32 == 0:
+        assert p8.tile_tokens == 32
+    else:
+        assert p8.tile_tokens == p16.tile_tokens
+        assert p8.as_dict() == p16.as_dict()
+    assert p8.workspace_bytes <= p16.workspace_bytes
+    if ps > 0:
+        assert ps % p8.tile_tokens == 0
