@@ -734,7 +734,8 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
         // One tile of registers, refilled as soon as each part is dead: the next
         // tile's K loads go out once QK^T has consumed K, its V loads once this
         // tile's V is in LDS, so they fly during the rest of the tile's math.
-        // Half the registers of the double buffer, so more waves fit per SIMD.
+        // (Measured faster than two buffers or a ring of two tiles: the stream
+        // is bandwidth-bound, and more loads in flight only add contention.)
         Tile<D, NB, KV> buf;
         if constexpr (SPEC) {
             buf = pre->tile;

@@ -73,7 +73,7 @@ typedef struct gqa_plan {
     int max_pieces;         /* most partials one (sequence, kv head) can have */
     int64_t slots;          /* partial blocks in the workspace: B*Hkv*S, or shares + B*Hkv */
     int pv_mode;            /* PV contraction: 1 = bf16 MFMA with P split hi+lo, 0 = fp32 MFMA */
-    int double_buffer;      /* 1: two tile buffers per wave; 0: one (more waves per SIMD) */
+    int double_buffer;      /* 1: two tile buffers per wave; 0: one, refilled part by part */
     int streaming;          /* 1: K/V loads carry the non-temporal hint (large caches) */
     size_t workspace_bytes; /* scratch the call needs (0 when direct) */
 } gqa_plan_t;
