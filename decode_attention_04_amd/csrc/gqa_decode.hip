@@ -88,6 +88,7 @@ struct SplitArgs {
     int num_pages;              // paged
     int num_splits, split_tokens;
     int piece_cost;             // even partition: tiles a piece's start and fold are worth
+    int halve_long;             // even partition, contiguous cache: one share per CU for long segments
     float qk_scale_log2;        // scale * log2(e) (times k_scale for an E4M3 cache)
     float v_scale;              // E4M3 cache: V's per-tensor scale
 };
@@ -102,6 +103,7 @@ struct CombineArgs {
     int shares;               // even partition: workgroups of the split kernel
     int M, Gh;                // query tokens per sequence, query heads per kv head (G = M * Gh)
     int piece_cost;           // even partition: as in SplitArgs
+    int halve_long;           // as in SplitArgs
 };
 
 __device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
@@ -582,19 +584,46 @@ __device__ __forceinline__ SegmentLocation locate_tile(const int32_t *seq_lens, 
     return loc;
 }
 
-// Axis positions of all segments before sequence b's first one, and of all segments.
+// Axis positions of all segments before sequence b's first one, and of all
+// segments; and the number of non-empty segments.
 __device__ __forceinline__ void prefix_tiles(const int32_t *seq_lens, int B, int Hkv, int cap, int TT, int K, int b,
-                                             int lane, long long &before, long long &total) {
-    long long run = 0, pre = 0;
+                                             int lane, long long &before, long long &total, long long &segs) {
+    long long run = 0, pre = 0, ne = 0;
     for (int c0 = 0; c0 < B; c0 += 64) {
         const int bb = c0 + lane;
         const int n = bb < B ? seg_span((clamp_len(seq_lens, bb, cap) + TT - 1) / TT, K) : 0;
         const int cnt = wave_sum(bb < b ? n : 0);
         pre += cnt;
         run += wave_sum(n);
+        ne += wave_sum(n > 0 ? 1 : 0);
     }
     before = uniform64(pre * Hkv);
     total = uniform64(run * Hkv);
+    segs = uniform64(ne * Hkv);
+}
+
+// Segments of a contiguous cache averaging at least this many tiles stream
+// best with one share per CU: half the launched shares (the plan launches two
+// per CU) then take the axis, and the other half exit at once.  Shorter
+// segments, and every paged cache, keep two per CU, whose second workgroup
+// covers the first one's piece starts (measured: uniform 16k-key batch 84.4 ->
+// 81.8 us per call; ragged batches of up to 2k keys 48.8 -> 52.8 with one per CU).
+constexpr int kLongSegmentTiles = 128;
+
+// The number of shares the axis is cut into: the launched P, or half of it
+// (halve_long, for long segments); N = axis positions, segs = non-empty segments.
+__device__ __forceinline__ long long shares_for(long long P, long long N, long long segs, int K, int halve_long) {
+    return (halve_long && segs > 0 && N >= (long long)(kLongSegmentTiles + K) * segs) ? (P + 1) / 2 : P;
+}
+
+// Non-empty (sequence, kv head) segments.
+__device__ __forceinline__ long long nonempty_segments(const int32_t *seq_lens, int B, int Hkv, int cap, int lane) {
+    long long cnt = 0;
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        const int bb = c0 + lane;
+        cnt += wave_sum(bb < B && clamp_len(seq_lens, bb, cap) > 0 ? 1 : 0);
+    }
+    return uniform64(cnt * Hkv);
 }
 
 // The share of workgroup w: [share_begin(w), share_begin(w + 1)).
@@ -1039,7 +1068,6 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
         // This workgroup's equal share of the tile axis (each segment's tiles
         // plus K positions for its start and fold), walked piece by piece.
         const int lane = threadIdx.x & 63;
-        const long long P = gridDim.x;
         const int K = a.piece_cost;
         SegmentLocation loc;
         long long cur, end;
@@ -1049,6 +1077,9 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
             const int n = seg_span((ln + TT - 1) / TT, K);
             const int incl = wave_scan(n, lane);
             const long long N = uniform64((long long)__shfl(incl, 63, 64) * a.Hkv);
+            const long long segs = uniform64((long long)wave_sum(ln > 0 ? 1 : 0) * a.Hkv);
+            const long long P = shares_for(gridDim.x, N, segs, K, a.halve_long);
+            if ((long long)blockIdx.x >= P) return;
             cur = share_begin(blockIdx.x, N, P);
             end = share_begin(blockIdx.x + 1, N, P);
             if (cur >= end) return;
@@ -1061,6 +1092,9 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
             loc.before = uniform64((long long)__shfl(incl - n, l, 64) * a.Hkv);
         } else {
             loc = locate_tile(a.seq_lens, a.B, a.Hkv, cap, TT, K, -1, lane);  // the total only
+            const long long segs = a.halve_long ? nonempty_segments(a.seq_lens, a.B, a.Hkv, cap, lane) : 0;
+            const long long P = shares_for(gridDim.x, loc.total, segs, K, a.halve_long);
+            if ((long long)blockIdx.x >= P) return;
             cur = share_begin(blockIdx.x, loc.total, P);
             end = share_begin(blockIdx.x + 1, loc.total, P);
             if (cur >= end) return;
@@ -1231,10 +1265,11 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
     } else {
         long long before, total;
         const int lane = threadIdx.x & 63;
-        prefix_tiles(a.seq_lens, a.B, a.Hkv, a.cap, a.tile, a.piece_cost, (int)b, lane, before, total);
+        long long segs;
+        prefix_tiles(a.seq_lens, a.B, a.Hkv, a.cap, a.tile, a.piece_cost, (int)b, lane, before, total, segs);
         const int n = (clamp_len(a.seq_lens, (int)b, a.cap) + a.tile - 1) / a.tile;
         N = total;
-        P = a.shares;
+        P = shares_for(a.shares, N, segs, a.piece_cost, a.halve_long);
         maybe_empty = N < P;
         if (n == 0) {
             S = 0;
@@ -1398,10 +1433,11 @@ __global__ __launch_bounds__(kNarrowThreads) void gqa_combine_narrow_kernel(cons
         lo = bk * S;
     } else {
         long long before, total;
-        prefix_tiles(a.seq_lens, a.B, a.Hkv, a.cap, a.tile, a.piece_cost, b, lane, before, total);
+        long long segs;
+        prefix_tiles(a.seq_lens, a.B, a.Hkv, a.cap, a.tile, a.piece_cost, b, lane, before, total, segs);
         const int n = (clamp_len(a.seq_lens, b, a.cap) + a.tile - 1) / a.tile;
         N = total;
-        P = a.shares;
+        P = shares_for(a.shares, N, segs, a.piece_cost, a.halve_long);
         maybe_empty = N < P;
         if (n == 0) {
             S = 0;
@@ -1545,6 +1581,16 @@ int piece_cost() {
     return kDefaultPieceCost;
 }
 
+// Even shares over a contiguous cache: whether the kernels may take one share
+// per CU when the segments are long (decided on the device from seq_lens, the
+// same way in the split and combine kernels).  Off for paged caches, and when
+// GQA_DECODE_SHARES fixes the share count or GQA_DECODE_HALVE_LONG=0.
+int halve_long_shares(bool paged) {
+    if (paged || getenv("GQA_DECODE_SHARES") != nullptr) return 0;
+    const char *s = getenv("GQA_DECODE_HALVE_LONG");
+    return (s != nullptr && strcmp(s, "0") == 0) ? 0 : 1;
+}
+
 // Tile buffering: one register tile per wave refilled early (the default;
 // it leaves room for twice the waves), or GQA_DECODE_DBUF=1 for two.
 int env_dbuf() {
@@ -1570,11 +1616,12 @@ bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t
 
 hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const float *part_ml,
                           float *out, const int32_t *seq_lens, int B, int M, int Hq, int Hkv, int D,
-                          int cap, hipStream_t stream) {
+                          int cap, bool paged, hipStream_t stream) {
     // rows: M query tokens x Hq heads per sequence, M * G per (sequence, kv head)
     const int rows = M * Hq;
     CombineArgs ca{part_acc, part_ml, out, seq_lens, D, rows / Hkv, rows, plan.num_splits,
-                   B, Hkv, cap, plan.tile_tokens, plan.grid, M, Hq / Hkv, piece_cost()};
+                   B, Hkv, cap, plan.tile_tokens, plan.grid, M, Hq / Hkv, piece_cost(),
+                   halve_long_shares(paged)};
     // The widest dim chunk (NCOL = 16, 8, 4 or 2 columns of 4 dims) that
     // still gives at least 128 workgroups: narrower chunks put more threads on
     // the pieces of a column (measured best for few heads with many pieces).
@@ -1672,6 +1719,7 @@ constexpr KvSpec kBf16Cache{kKvBf16, 1.f, 1.f};
 gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, int kv, void *workspace,
                  hipStream_t stream, int phases) {
     a.piece_cost = piece_cost();
+    a.halve_long = halve_long_shares(paged);
     if (!plan.direct) {
         WorkspaceLayout w = workspace_layout(a.M * a.Hq, a.Hkv, D, plan.slots);
         char *base = static_cast<char *>(workspace);
@@ -1690,7 +1738,8 @@ gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, int kv
     }
     if (plan.direct || !(phases & kPhaseCombine)) return GQA_OK;
     const int cap = paged ? a.max_pages * a.page_size : a.S_max;
-    e = launch_combine(plan, a.part_acc, a.part_ml, a.out, a.seq_lens, a.B, a.M, a.Hq, a.Hkv, D, cap, stream);
+    e = launch_combine(plan, a.part_acc, a.part_ml, a.out, a.seq_lens, a.B, a.M, a.Hq, a.Hkv, D, cap, paged,
+                       stream);
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 

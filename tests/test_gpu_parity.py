@@ -340,6 +340,29 @@ def test_fixed_and_even_agree_with_oracle(monkeypatch):
     compare(fixed, ref, "fixed")
 
 
+@pytest.mark.parametrize("halve", ["default", "0"])
+def test_even_shares_long_segments(monkeypatch, halve):
+    """Contiguous batches whose segments average >= 128 tiles take one share per CU (half the
+    launched shares; the rest exit); shorter ones keep two.  Both sides of the rule, with the
+    rule switched off, and the many-sequence walk (B > 64), against the oracle and bit-exact
+    across runs."""
+    say(f"[parity] long segments, halve={halve}")
+    if halve == "0":
+        monkeypatch.setenv("GQA_DECODE_HALVE_LONG", "0")
+    rng = np.random.default_rng(70)
+    cases = [
+        W.contig_case(8, 32, 4, 128, 4096, seq_lens=[4096, 4000, 2048, 3000, 4096, 1, 0, 4095], seed=71),
+        W.contig_case(8, 32, 4, 128, 4096, seq_lens=[100, 4, 0, 300, 17, 1000, 2, 64], seed=72),
+        W.contig_case(70, 16, 2, 128, 2304, seq_lens=rng.integers(2048, 2305, 70), seed=73),
+        W.mq_case(8, 2, 16, 4, 128, 4096, seq_lens=[4096, 2048, 3000, 4096, 2500, 4096, 2200, 3333], seed=74),
+    ]
+    for case in cases:
+        dc = DeviceCase(case)
+        runs = [dc.run_host() for _ in range(2)]
+        compare(runs[0], oracle_out(case), f"{case.name} halve={halve}")
+        assert np.array_equal(runs[0].view(np.uint32), runs[1].view(np.uint32))
+
+
 @pytest.mark.parametrize("nt", ["0", "1"])
 def test_cache_policy_variants(monkeypatch, nt):
     """Both K/V load cache policies give the same bits (only the hint differs)."""
