@@ -45,6 +45,30 @@ def test_workload_full_size(name):
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), "not bit-exact across runs"
 
 
+def test_million_key_context():
+    """One sequence of 2^20 keys (256 MB of K and of V at head_dim 128), a length just short of
+    the capacity: 32-bit buffer offsets up to 256 MB, 512 fixed splits of 2048 keys, against
+    the oracle and bit-exact across runs."""
+    S = 1 << 20
+    say("[parity] 1M-key context: generating")
+    rng = np.random.default_rng(75)
+
+    def bf16_bits(shape):  # random sign, exponent 2^-4 .. 2^0, random mantissa: fast to draw
+        return ((rng.integers(0, 2, shape, dtype=np.uint16) << 15)
+                | (rng.integers(123, 128, shape, dtype=np.uint16) << 7)
+                | rng.integers(0, 128, shape, dtype=np.uint16))
+
+    case = W.Case("ctx_1m", 1, 8, 1, 128, W.default_scale(128), bf16_bits((1, 8, 128)),
+                  bf16_bits((1, 1, S, 128)), bf16_bits((1, 1, S, 128)), np.array([S - 5], np.int32))
+    dc = DeviceCase(case)
+    plan = gd.gqa_decode_plan(1, 8, 1, 128, S)
+    say(f"[parity] 1M-key context: plan {plan.as_dict()}")
+    outs = [dc.run_host() for _ in range(2)]
+    stats = compare(outs[0], oracle_out(case), "1M keys")
+    say(f"[parity] 1M-key context: {stats}")
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
 # ------------------------------------------------------------------ shape matrix
 MATRIX = []
 for D in (64, 128, 256):
