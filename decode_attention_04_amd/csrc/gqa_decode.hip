@@ -173,7 +173,7 @@ __device__ __forceinline__ constexpr int kslot_block(int kb) {
 }
 
 // One wave's tile as loaded: NB blocks of 16 keys.
-//   k[blk][w]: key 16*blk + r; bf16: k-block w, dims kslot_dim(w, grp) ..;
+//   k[blk][w]: key 16*blk + r; bf16: k-block w, dims kslot_lane(grp) + kslot_block(w) ..;
 //              E4M3: 16 bytes for k-blocks 2w and 2w + 1.
 //   v[blk][j][c]: key 16*blk + 4*grp + j, dims 16*DPL*c + DPL*r .. (DPL values).
 template <int D, int NB, int KV>
@@ -311,6 +311,8 @@ __device__ __forceinline__ void stage_v(const Tile<D, NB, KV> &t, int r, int grp
                 if constexpr (S::VW == 4) {
                     *reinterpret_cast<u32x4_t *>(dst) = u32x4_t{v_word(t, blk, j, c, 0), v_word(t, blk, j, c, 1),
                                                                 v_word(t, blk, j, c, 2), v_word(t, blk, j, c, 3)};
+                } else if constexpr (S::VW == 1) {  // head_dim 32
+                    *reinterpret_cast<unsigned int *>(dst) = v_word(t, blk, j, c, 0);
                 } else {
                     *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{v_word(t, blk, j, c, 0), v_word(t, blk, j, c, 1)};
                 }
@@ -1200,8 +1202,10 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
         const int len = min(max(__builtin_amdgcn_readfirstlane(len_v), 0), cap);
         const int t_end = min(len, t_begin + a.split_tokens);
         const size_t slot = (size_t)bk * nsplit + split;
-        if (!DBUF && PV == kPvBf16 && a.split_tokens <= kWaves * TT) {
-            process_single<D, NB, PAGED, CPOL, KV, kSpec>(a, lds, b, kvh, len, t_begin, t_end, slot, direct, pre);
+        // (the one-tile path splits the head dims in quarters of 16-dim blocks: D >= 64)
+        if (D >= 64 && !DBUF && PV == kPvBf16 && a.split_tokens <= kWaves * TT) {
+            if constexpr (D >= 64)
+                process_single<D, NB, PAGED, CPOL, KV, kSpec>(a, lds, b, kvh, len, t_begin, t_end, slot, direct, pre);
         } else {
             process_range<D, NB, PAGED, PV, DBUF, CPOL, KV, kSpec>(a, lds, b, kvh, len, t_begin, t_end, slot, direct,
                                                                    &pre);
@@ -1518,7 +1522,7 @@ int env_int(const char *name, int fallback) {
 // 16 at D=256).  GQA_DECODE_TILE (16, 32 or 64) overrides it for A/B runs
 // when the result stays within 16 KB.
 int tile_tokens_for(int D, bool double_buffer, bool paged, int elem_bytes) {
-    int dflt = double_buffer ? (D == 64 ? 64 : (D == 128 ? 32 : 16)) : (D == 64 ? 32 : 16);
+    int dflt = double_buffer ? (D <= 64 ? 64 : (D == 128 ? 32 : 16)) : (D == 32 ? 64 : (D == 64 ? 32 : 16));
     // A paged E4M3 cache at head_dim 128: 32 keys, so that a wave still reads
     // 4 KB of K (and of V) in one piece of a page, as a bf16 tile of 16 does
     // (measured: the ragged 8k paged workload 80.2 -> 62.4 us per call).
@@ -1528,7 +1532,7 @@ int tile_tokens_for(int D, bool double_buffer, bool paged, int elem_bytes) {
     return dflt;
 }
 
-bool supported_dim(int D) { return D == 64 || D == 128 || D == 256; }
+bool supported_dim(int D) { return D == 32 || D == 64 || D == 128 || D == 256; }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -1646,6 +1650,7 @@ hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const f
         ncol = 16;
         while (ncol > 2 && heads * (D / (4 * ncol)) < 128) ncol /= 2;
     }
+    while (4 * ncol > D) ncol /= 2;  // a chunk never exceeds the head (head_dim 32: 8 columns)
     const unsigned grid = (unsigned)(heads * (D / (4 * ncol)));
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, dim3(grid), dim3(kCombineThreads), 0, stream, ca.part_acc, ca.part_ml,
@@ -1673,14 +1678,21 @@ hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, int kv, h
                                cap, a.split_tokens, qpack, a);
         };
         if (kv == kKvFp8) {
-            // The E4M3 cache always runs the default pipeline (bf16 PV, one register tile).
-            if (nt) even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, kNonTemporal, kKvFp8>)
-                         : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, kNonTemporal, kKvFp8>);
-            else even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, 0, kKvFp8>)
-                      : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, 0, kKvFp8>);
-        } else if (plan.pv_mode == kPvF32) {
-            even ? go(gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionEven, 0, kKvBf16>)
-                 : go(gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionFixed, 0, kKvBf16>);
+            // The E4M3 cache always runs the default pipeline (bf16 PV, one register tile);
+            // its 16-byte K loads feed two 32-dim k-blocks, so it needs D >= 64.
+            if constexpr (D < 64) {
+                return hipErrorInvalidValue;
+            } else {
+                if (nt) even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, kNonTemporal, kKvFp8>)
+                             : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, kNonTemporal, kKvFp8>);
+                else even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, 0, kKvFp8>)
+                          : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, 0, kKvFp8>);
+            }
+        } else if (D >= 64 && plan.pv_mode == kPvF32) {  // (its fold reads 4 dims per lane: D >= 64)
+            if constexpr (D >= 64) {
+                even ? go(gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionEven, 0, kKvBf16>)
+                     : go(gqa_split_kernel<D, NB, PAGED, kPvF32, true, kPartitionFixed, 0, kKvBf16>);
+            }
         } else if (plan.double_buffer) {
             even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionEven, 0, kKvBf16>)
                  : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionFixed, 0, kKvBf16>);
@@ -1729,6 +1741,7 @@ gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, int kv
     hipError_t e = hipSuccess;
     if (phases & kPhaseSplit) {
         switch (D) {
+            case 32: e = paged ? launch_split<32, true>(plan, a, kv, stream) : launch_split<32, false>(plan, a, kv, stream); break;
             case 64: e = paged ? launch_split<64, true>(plan, a, kv, stream) : launch_split<64, false>(plan, a, kv, stream); break;
             case 128: e = paged ? launch_split<128, true>(plan, a, kv, stream) : launch_split<128, false>(plan, a, kv, stream); break;
             case 256: e = paged ? launch_split<256, true>(plan, a, kv, stream) : launch_split<256, false>(plan, a, kv, stream); break;
@@ -1909,6 +1922,7 @@ gqa_status_t decode_contig(const void *q, const void *k_cache, const void *v_cac
                            size_t workspace_bytes, int num_splits, hipStream_t stream, int phases) {
     gqa_status_t s = check_common(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, scale);
     if (s != GQA_OK) return s;
+    if (kv.type == kKvFp8 && D < 64) return GQA_ERR_UNSUPPORTED;  // E4M3: head_dim 64, 128 or 256
     if ((s = check_queries(B, M, Hq, Hkv, D)) != GQA_OK) return s;
     if (S_max < 0 || num_splits < 0 || !isfinite(kv.k_scale) || !isfinite(kv.v_scale)) return GQA_ERR_SHAPE;
     if (B == 0) return GQA_OK;
@@ -1943,6 +1957,7 @@ gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
                           size_t workspace_bytes, int num_splits, hipStream_t stream, int phases) {
     gqa_status_t s = check_common(q, k_pool, v_pool, seq_lens, out, B, Hq, Hkv, D, scale);
     if (s != GQA_OK) return s;
+    if (kv.type == kKvFp8 && D < 64) return GQA_ERR_UNSUPPORTED;  // E4M3: head_dim 64, 128 or 256
     if ((s = check_queries(B, M, Hq, Hkv, D)) != GQA_OK) return s;
     if (!isfinite(kv.k_scale) || !isfinite(kv.v_scale)) return GQA_ERR_SHAPE;
     if (B == 0) return (page_size > 0 && page_size % 16 == 0) ? GQA_OK : GQA_ERR_UNSUPPORTED;

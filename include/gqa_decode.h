@@ -55,7 +55,7 @@ typedef enum gqa_status {
     GQA_OK = 0,
     GQA_ERR_NULL = 1,        /* a required pointer is NULL */
     GQA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
-    GQA_ERR_UNSUPPORTED = 3, /* head_dim not in {64,128,256}, G > 16, page_size % 16 != 0 */
+    GQA_ERR_UNSUPPORTED = 3, /* head_dim not in {32,64,128,256} (E4M3: {64,128,256}), G > 16, page_size % 16 != 0 */
     GQA_ERR_ALIGN = 4,       /* a pointer violates the alignment above */
     GQA_ERR_WORKSPACE = 5,   /* workspace smaller than the plan needs */
     GQA_ERR_HIP = 6          /* a HIP runtime call or launch failed */

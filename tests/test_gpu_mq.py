@@ -36,7 +36,7 @@ def _bits(a: np.ndarray) -> np.ndarray:
 VERIFY = [(7, 16, 8), (7, 4, 2), (4, 16, 4), (2, 24, 4), (16, 8, 8), (3, 8, 2)]   # (M, Hq, Hkv)
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 @pytest.mark.parametrize("M,Hq,Hkv", VERIFY)
 def test_mq_matrix(D, M, Hq, Hkv):
     """Ragged lengths (including len < M, len = M and len = 0) and a NaN tail, several splits."""

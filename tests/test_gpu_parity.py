@@ -71,14 +71,14 @@ def test_million_key_context():
 
 # ------------------------------------------------------------------ shape matrix
 MATRIX = []
-for D in (64, 128, 256):
+for D in (32, 64, 128, 256):
     for (Hq, Hkv) in ((8, 8), (8, 2), (12, 2), (16, 2), (16, 1)):
         MATRIX.append((D, Hq, Hkv))
 
 
 @pytest.mark.parametrize("D,Hq,Hkv", MATRIX)
 def test_matrix_ragged_with_nan_tail(D, Hq, Hkv):
-    tt = {64: 64, 128: 32, 256: 16}[D]
+    tt = {32: 64, 64: 64, 128: 32, 256: 16}[D]
     lens = [1, tt - 1, tt + 1, 3 * tt + 5, 517]
     S_max = 600
     say(f"[parity] matrix D={D} Hq={Hq} Hkv={Hkv} lens={lens}")
@@ -146,7 +146,7 @@ def test_side_stream_and_reused_workspace():
 
 # ------------------------------------------------------------------ paged
 @pytest.mark.parametrize("ps", [16, 32, 64, 48])
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 def test_paged_matrix(ps, D):
     say(f"[parity] paged ps={ps} D={D}")
     lens = [1, ps - 1, ps, ps + 1, 5 * ps + 3, 700]
@@ -341,7 +341,7 @@ def test_even_shares_contiguous(monkeypatch, lens, shares):
 
 
 @pytest.mark.parametrize("shares", ["5", "0"])
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 def test_even_shares_paged(monkeypatch, shares, D):
     say(f"[parity] even shares paged D={D} shares={shares}")
     if shares != "0":

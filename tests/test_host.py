@@ -164,7 +164,7 @@ def call_paged(lib, q=A, k=A, v=A, lens=A, table=A, B=1, Hq=8, Hkv=2, D=128, ps=
     (dict(out=None), 1), (dict(ws=None), 1),
     (dict(Hq=9), 2), (dict(Hkv=0), 2), (dict(B=-1), 2), (dict(S=-1), 2), (dict(splits=-1), 2),
     (dict(scale=float("nan")), 2), (dict(scale=float("inf")), 2), (dict(S=1 << 30), 2),
-    (dict(D=32), 3), (dict(D=80), 3), (dict(Hq=64, Hkv=2), 3),
+    (dict(D=16), 3), (dict(D=80), 3), (dict(Hq=64, Hkv=2), 3),
     (dict(q=A + 8), 4), (dict(k=A + 2), 4), (dict(v=A + 4), 4), (dict(out=A + 4), 4),
     (dict(lens=A + 2), 4), (dict(ws=A + 8), 4),
     (dict(ws_bytes=16), 5),
@@ -236,7 +236,7 @@ def call_paged_fp8(lib, q=A, k=A, v=A, lens=A, table=A, B=1, Hq=8, Hkv=2, D=128,
     (dict(k=None), 1), (dict(v=None), 1), (dict(lens=None), 1), (dict(out=None), 1),
     (dict(ks=float("nan")), 2), (dict(vs=float("inf")), 2), (dict(ks=float("-inf")), 2),
     (dict(scale=float("nan")), 2), (dict(S=1 << 30), 2), (dict(Hq=9), 2),
-    (dict(D=96), 3), (dict(k=A + 8), 4), (dict(v=A + 1), 4), (dict(ws_bytes=16), 5),
+    (dict(D=96), 3), (dict(D=32), 3), (dict(k=A + 8), 4), (dict(v=A + 1), 4), (dict(ws_bytes=16), 5),
     (dict(B=0, q=None, k=None, v=None, lens=None, out=None, ws=None), 0),
 ])
 def test_decode_fp8_rejects(lib, kw, code):
@@ -245,7 +245,7 @@ def test_decode_fp8_rejects(lib, kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(table=None), 1), (dict(vs=float("nan")), 2), (dict(ps=0), 2), (dict(ps=24), 3),
-    (dict(table=A + 2), 4), (dict(ws_bytes=0), 5),
+    (dict(table=A + 2), 4), (dict(ws_bytes=0), 5), (dict(D=32), 3),
 ])
 def test_paged_decode_fp8_rejects(lib, kw, code):
     assert call_paged_fp8(lib, **kw) == code
