@@ -1585,12 +1585,15 @@ int piece_cost() {
     return kDefaultPieceCost;
 }
 
-// Even shares over a contiguous cache: whether the kernels may take one share
-// per CU when the segments are long (decided on the device from seq_lens, the
-// same way in the split and combine kernels).  Off for paged caches, and when
-// GQA_DECODE_SHARES fixes the share count or GQA_DECODE_HALVE_LONG=0.
-int halve_long_shares(bool paged) {
-    if (paged || getenv("GQA_DECODE_SHARES") != nullptr) return 0;
+// Even shares over a contiguous bf16 cache: whether the kernels may take one
+// share per CU when the segments are long (decided on the device from
+// seq_lens, the same way in the split and combine kernels).  Off for paged
+// caches, for E4M3 caches (half the bytes per tile for the same math: their
+// second workgroup per CU hides it; measured 50.2 -> 62.0 us per call at the
+// batched E4M3 workload with one per CU), and when GQA_DECODE_SHARES fixes the
+// share count or GQA_DECODE_HALVE_LONG=0.
+int halve_long_shares(bool paged, int kv) {
+    if (paged || kv != kKvBf16 || getenv("GQA_DECODE_SHARES") != nullptr) return 0;
     const char *s = getenv("GQA_DECODE_HALVE_LONG");
     return (s != nullptr && strcmp(s, "0") == 0) ? 0 : 1;
 }
@@ -1620,12 +1623,11 @@ bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t
 
 hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const float *part_ml,
                           float *out, const int32_t *seq_lens, int B, int M, int Hq, int Hkv, int D,
-                          int cap, bool paged, hipStream_t stream) {
+                          int cap, int halve_long, hipStream_t stream) {
     // rows: M query tokens x Hq heads per sequence, M * G per (sequence, kv head)
     const int rows = M * Hq;
     CombineArgs ca{part_acc, part_ml, out, seq_lens, D, rows / Hkv, rows, plan.num_splits,
-                   B, Hkv, cap, plan.tile_tokens, plan.grid, M, Hq / Hkv, piece_cost(),
-                   halve_long_shares(paged)};
+                   B, Hkv, cap, plan.tile_tokens, plan.grid, M, Hq / Hkv, piece_cost(), halve_long};
     // The widest dim chunk (NCOL = 16, 8, 4 or 2 columns of 4 dims) that
     // still gives at least 128 workgroups: narrower chunks put more threads on
     // the pieces of a column (measured best for few heads with many pieces).
@@ -1731,7 +1733,7 @@ constexpr KvSpec kBf16Cache{kKvBf16, 1.f, 1.f};
 gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, int kv, void *workspace,
                  hipStream_t stream, int phases) {
     a.piece_cost = piece_cost();
-    a.halve_long = halve_long_shares(paged);
+    a.halve_long = halve_long_shares(paged, kv);
     if (!plan.direct) {
         WorkspaceLayout w = workspace_layout(a.M * a.Hq, a.Hkv, D, plan.slots);
         char *base = static_cast<char *>(workspace);
@@ -1751,7 +1753,7 @@ gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, int kv
     }
     if (plan.direct || !(phases & kPhaseCombine)) return GQA_OK;
     const int cap = paged ? a.max_pages * a.page_size : a.S_max;
-    e = launch_combine(plan, a.part_acc, a.part_ml, a.out, a.seq_lens, a.B, a.M, a.Hq, a.Hkv, D, cap, paged,
+    e = launch_combine(plan, a.part_acc, a.part_ml, a.out, a.seq_lens, a.B, a.M, a.Hq, a.Hkv, D, cap, a.halve_long,
                        stream);
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
@@ -2124,7 +2126,9 @@ gqa_status_t combine_impl(const void *workspace, size_t workspace_bytes, const i
     } else {
         a.S_max = max_seq_len;
     }
-    return run(plan, a, D, page_size > 0, kKvBf16, const_cast<void *>(workspace), stream, kPhaseCombine);
+    // the cache type only matters for the share rule the split call used
+    return run(plan, a, D, page_size > 0, elem_bytes == 1 ? kKvFp8 : kKvBf16, const_cast<void *>(workspace), stream,
+               kPhaseCombine);
 }
 
 }  // namespace

@@ -160,12 +160,15 @@ def test_fp8_even_shares(monkeypatch):
         compare(dc.run_host(), ref, f"fp8 even shares={shares}")
 
 
-@pytest.mark.parametrize("paged", [False, True])
-def test_fp8_partials_then_combine_equals_one_call(paged):
-    """gqa_*_fp8_partials + gqa_decode_combine_fp8 on one stream give the one-call result bit for bit."""
+@pytest.mark.parametrize("paged,long_segments", [(False, False), (True, False), (False, True)])
+def test_fp8_partials_then_combine_equals_one_call(paged, long_segments):
+    """gqa_*_fp8_partials + gqa_decode_combine_fp8 on one stream give the one-call result bit for bit
+    (the combine recomputes the E4M3 plan: paged tiles, the share rule of long segments)."""
     if paged:
         case = W.fp8_paged_case(4, 32, 8, 128, 32, 200, seq_lens=[1000, 1, 555, 1024], max_len=1024,
                                 seed=96)
+    elif long_segments:
+        case = W.fp8_contig_case(4, 16, 2, 128, 4096, seq_lens=[4096, 4000, 3000, 4096], seed=98)
     else:
         case = W.fp8_contig_case(3, 24, 4, 256, 1500, seq_lens=[1500, 700, 3], seed=97, scale=1 / 16)
     dc = DeviceCase(case)

@@ -280,12 +280,16 @@ def test_pv_modes(monkeypatch, pv, D):
 
 
 @pytest.mark.parametrize("paged", [False, True])
-def test_partials_then_combine_equals_one_call(paged):
-    """gqa_*_partials + gqa_decode_combine on one stream give the one-call result bit for bit."""
-    say(f"[parity] partials + combine, paged={paged}")
+@pytest.mark.parametrize("long_segments", [False, True])
+def test_partials_then_combine_equals_one_call(paged, long_segments):
+    """gqa_*_partials + gqa_decode_combine on one stream give the one-call result bit for bit
+    (long contiguous segments: with one share per CU in both kernels)."""
+    say(f"[parity] partials + combine, paged={paged} long={long_segments}")
     if paged:
         case = W.paged_case(4, 32, 8, 128, 32, 200, seq_lens=[1000, 1, 555, 1024], max_len=1024,
                             seed=50)
+    elif long_segments:
+        case = W.contig_case(4, 16, 2, 128, 4096, seq_lens=[4096, 4000, 3000, 4096], seed=52)
     else:
         case = W.contig_case(3, 24, 4, 256, 1500, seq_lens=[1500, 700, 3], seed=51, scale=1 / 16)
     dc = DeviceCase(case)
