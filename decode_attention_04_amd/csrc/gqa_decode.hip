@@ -85,6 +85,7 @@ struct SplitArgs {
     int qdiv;                   // ceil(256 / G): row r belongs to query token (r * qdiv) >> 8
     int S_max;                  // contiguous capacity
     int page_size, max_pages;   // paged
+    int page_shift;             // paged: log2(page_size) when a power of two, else -1
     int num_pages;              // paged
     int num_splits, split_tokens;
     int piece_cost;             // even partition: tiles a piece's start and fold are worth
@@ -731,7 +732,7 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
         const int t0 = t_begin + (wave + kWaves * it) * TT;
         if constexpr (PAGED) {
             if (it > 0 && (it & 63) == 0) load_pages(it >> 6);
-            const int pidx = t0 / a.page_size;
+            const int pidx = a.page_shift >= 0 ? t0 >> a.page_shift : t0 / a.page_size;
             const int row0 = t0 - pidx * a.page_size;
             const int page = min(max(__builtin_amdgcn_readlane(page_vec, it & 63), 0), a.num_pages - 1);
             const int rows = min(a.page_size, len - pidx * a.page_size);
@@ -1985,6 +1986,7 @@ gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
     a.out = out;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.M = M; a.R = M * (Hq / Hkv); a.qdiv = (256 + a.G - 1) / a.G;
     a.page_size = page_size;
+    a.page_shift = (page_size & (page_size - 1)) == 0 ? __builtin_ctz((unsigned)page_size) : -1;
     a.max_pages = max_pages;
     a.num_pages = num_pages;
     a.num_splits = plan.num_splits;
