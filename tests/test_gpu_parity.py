@@ -5,6 +5,8 @@ output against the fp64 oracle on unit-normal bf16 inputs.
 """
 from __future__ import annotations
 
+import dataclasses
+
 import sys
 
 import numpy as np
@@ -127,6 +129,34 @@ def test_batch_zero():
     q0 = dc.q[:0]
     gd.gqa_decode(q0, dc.k[:0], dc.v[:0], dc.seq_lens[:0], case.scale, out=out)
     torch.cuda.synchronize()
+
+
+def test_out_of_range_lengths_and_pages_are_clamped():
+    """Device-resident values the host cannot check are clamped on the device, so no access
+    leaves the caller's buffers: a negative length reads nothing (a zero row), a length past
+    the capacity reads the capacity, and page ids outside [0, num_pages) read the nearest
+    valid page.  The header leaves the output for such inputs unspecified; this checks the
+    clamped result against the oracle on the clamped inputs, with an in-range sequence in
+    the same batch, contiguous and paged, even shares and fixed splits."""
+    say("[parity] clamped lengths and page ids")
+    S = 512
+    c = W.contig_case(3, 16, 4, 128, S, seq_lens=[100, 300, 200], seed=76)
+    bad = c.seq_lens.copy()
+    bad[0], bad[1] = -7, 10 ** 9
+    c_bad = dataclasses.replace(c, seq_lens=bad)
+    c_ref = dataclasses.replace(c, seq_lens=np.clip(bad, 0, S).astype(np.int32))
+    ref = oracle_out(c_ref)
+    for splits in (0, 3):
+        compare(DeviceCase(c_bad).run_host(splits), ref, f"clamped lengths, splits={splits}")
+
+    p = W.paged_case(3, 16, 4, 128, 32, 64, seq_lens=[512, 300, 200], max_len=S, seed=77)
+    table = p.page_table.copy()
+    table[0, 1], table[0, 5], table[1, 2] = -1, p.num_pages + 5, 1 << 30
+    p_bad = dataclasses.replace(p, page_table=table)
+    p_ref = dataclasses.replace(p, page_table=np.clip(table, 0, p.num_pages - 1).astype(np.int32))
+    ref = oracle_out(p_ref)
+    for splits in (0, 3):
+        compare(DeviceCase(p_bad).run_host(splits), ref, f"clamped page ids, splits={splits}")
 
 
 def test_side_stream_and_reused_workspace():
