@@ -894,7 +894,8 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
 // four accumulators afterwards: each wave writes its quarter of the range's
 // partial (or of the output) straight from the MFMA registers.
 //   m = max_w m_w,  c_w = 2^(m_w - m),  l = sum_w c_w l_w,
-//   acc[:, quarter] = sum_w (c_w P_w) V_w[:, quarter]   (ascending w).
+//   acc[:, quarter] = sum_w (c_w P_w) V_w[:, quarter]   (blocks of 16 keys in
+//   ascending pairs, one 32-deep MFMA per pair).
 // Tile loads as in process_range; `pf` holds Q and the tile when SPEC.
 template <int D, int NB, bool PAGED, int CPOL, int KV, bool SPEC>
 __device__ __forceinline__ void process_single(const SplitArgs &a, FoldLds<D, NB> &lds, int b, int kvh, int len,
@@ -952,8 +953,11 @@ __device__ __forceinline__ void process_single(const SplitArgs &a, FoldLds<D, NB
     if (has) {
         qk_softmax(tile, pf.qb, st, t0, row_end, grp, a.qk_scale_log2, sc);
         if (SPEC && t0 + TT > len) zero_v_past(tile, t0, len, grp);  // read against the capacity
-        stage_v(tile, r, grp, stage);
+    } else {
+        // no keys: a zero V block meets this tile's zero probabilities below
+        zero_v_past(tile, t0, t0, grp);
     }
+    stage_v(tile, r, grp, stage);
     const float lsum = sum_rows(st.l);
     if (grp == 0) {
         lds.m[wave][r] = st.m;
@@ -982,32 +986,41 @@ __device__ __forceinline__ void process_single(const SplitArgs &a, FoldLds<D, NB
         L += cw[w] * lw[w];
     }
 
-    // PV over the four tiles for this wave's quarter of the dims.
+    // PV over the range's 4 * NB blocks of 16 keys for this wave's quarter of
+    // the dims, two blocks per 32-deep MFMA: contraction slots 8*grp .. + 3 hold
+    // the first block's keys 4*grp .. + 3 and slots 8*grp + 4 .. + 7 the second
+    // block's, in both operands (the lane's own probabilities and two
+    // transposing reads), so no lane exchange is needed.  Every block takes part
+    // (a tile without keys is all zeros), which lets all LDS reads go out at once.
+    constexpr int NBLK = kWaves * NB;
     f32x4_t acc[NQ];
 #pragma unroll
     for (int j = 0; j < NQ; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        if (t_begin + w * TT >= t_end) continue;  // uniform: that wave staged nothing
-        const unsigned short *wst = lds.stage(w);
+    for (int e = 0; e < NBLK; e += 2) {
+        bf16x8_t hi, lo;
+        bf16x4_t av[2][NQ];
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
+        for (int h = 0; h < 2; ++h) {
+            const int w = (e + h) / NB;
+            const int blk = (e + h) % NB;
             const f32x4_t pw = lds.p[w][blk][lane] * cw[w];
-            bf16x4_t hi, lo;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                hi[i] = (__bf16)pw[i];
-                lo[i] = (__bf16)(pw[i] - (float)hi[i]);
+                hi[4 * h + i] = (__bf16)pw[i];
+                lo[4 * h + i] = (__bf16)(pw[i] - (float)hi[4 * h + i]);
             }
-            const unsigned short *src = wst + (16 * blk + 4 * grp + (r >> 2)) * RS + 4 * (r & 3);
+            const unsigned short *src = lds.stage(w) + (16 * blk + 4 * grp + (r >> 2)) * RS + 4 * (r & 3);
 #pragma unroll
-            for (int j = 0; j < NQ; ++j) {
-                const int nb = wave * NQ + j;
-                const bf16x4_t av = __builtin_bit_cast(
-                    bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(src + 16 * nb)));
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, hi, acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, lo, acc[j], 0, 0, 0);
-            }
+            for (int j = 0; j < NQ; ++j)
+                av[h][j] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                            (lds_i16x4_t *)(src + 16 * (wave * NQ + j))));
+        }
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const bf16x8_t v2 = __builtin_shufflevector(av[0][j], av[1][j], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v2, hi, acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v2, lo, acc[j], 0, 0, 0);
         }
     }
     if constexpr (KV == kKvFp8) {
