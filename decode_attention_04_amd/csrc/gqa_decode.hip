@@ -464,7 +464,7 @@ struct FoldLds {
     float m[kWaves][kMaxHeadsPerKv];
     float l[kWaves][kMaxHeadsPerKv];
     alignas(16) unsigned char region[kWaves][kRegion];
-    f32x4_t p[kWaves][NB][64];  // one-tile ranges: each wave's probabilities, in its lane layout
+    u32x4_t p[kWaves][NB][64];  // one-tile ranges: each wave's probabilities (bf16 hi, lo), in its lane layout
     __device__ float *acc(int w) { return reinterpret_cast<float *>(region[w]); }
     __device__ unsigned short *stage(int w) { return reinterpret_cast<unsigned short *>(region[w]); }
 };
@@ -888,14 +888,16 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
 // --------------------------------------------------- one tile per wave
 //
 // A key range of at most four tiles (the short splits that fill the CUs for a
-// single sequence): the four waves take one tile each, exchange their
-// probabilities and maxima through LDS, and then each wave computes PV over
-// all four tiles for its own quarter of the head dims.  There is no fold of
-// four accumulators afterwards: each wave writes its quarter of the range's
-// partial (or of the output) straight from the MFMA registers.
-//   m = max_w m_w,  c_w = 2^(m_w - m),  l = sum_w c_w l_w,
-//   acc[:, quarter] = sum_w (c_w P_w) V_w[:, quarter]   (blocks of 16 keys in
-//   ascending pairs, one 32-deep MFMA per pair).
+// single sequence): the four waves take one tile each and exchange, through
+// LDS, first their score maxima, then their probabilities against the range's
+// maximum (as bf16 hi + lo parts, each wave splitting only its own) and sums;
+// each wave then computes PV over all four tiles for its own quarter of the
+// head dims.  There is no fold of four accumulators afterwards: each wave
+// writes its quarter of the range's partial (or of the output) straight from
+// the MFMA registers.
+//   m = max_w m_w,  P_w = 2^(S_w - m),  l = sum_w rowsum(P_w)  (ascending w),
+//   acc[:, quarter] = sum_w P_w V_w[:, quarter]   (blocks of 16 keys in
+//   ascending pairs, one 32-deep MFMA per pair and part).
 // Tile loads as in process_range; `pf` holds Q and the tile when SPEC.
 template <int D, int NB, bool PAGED, int CPOL, int KV, bool SPEC>
 __device__ __forceinline__ void process_single(const SplitArgs &a, FoldLds<D, NB> &lds, int b, int kvh, int len,
@@ -940,51 +942,67 @@ __device__ __forceinline__ void process_single(const SplitArgs &a, FoldLds<D, NB
         }
     }
 
-    // This wave's tile: probabilities against its own maximum, V staged.
-    WaveState<D> st;  // fresh state: acc unused here
-#pragma unroll
-    for (int i = 0; i < S::NACC; ++i) st.acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    st.m = -INFINITY;
-    st.l = 0.f;
+    // This wave's scores (keys past the range or past a row's limit: -inf) and
+    // their maximum per head row; the range's maximum is known after one exchange.
     f32x4_t sc[NB];
-#pragma unroll
-    for (int blk = 0; blk < NB; ++blk) sc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    unsigned short *stage = lds.stage(wave);
+    float mx = -INFINITY;
     if (has) {
-        qk_softmax(tile, pf.qb, st, t0, row_end, grp, a.qk_scale_log2, sc);
-        if (SPEC && t0 + TT > len) zero_v_past(tile, t0, len, grp);  // read against the capacity
-    } else {
-        // no keys: a zero V block meets this tile's zero probabilities below
-        zero_v_past(tile, t0, t0, grp);
-    }
-    stage_v(tile, r, grp, stage);
-    const float lsum = sum_rows(st.l);
-    if (grp == 0) {
-        lds.m[wave][r] = st.m;
-        lds.l[wave][r] = lsum;
-    }
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) lds.p[wave][blk][lane] = sc[blk];
+        for (int blk = 0; blk < NB; ++blk) {
+            f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < S::KB; ++kb)
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(tile, blk, kb), pf.qb[kb], c, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tok = t0 + 16 * blk + 4 * grp + i;
+                sc[blk][i] = tok < row_end ? c[i] * a.qk_scale_log2 : -INFINITY;
+                mx = fmaxf(mx, sc[blk][i]);
+            }
+        }
+        mx = max_rows(mx);
+    } else {
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) sc[blk] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+    if (grp == 0) lds.m[wave][r] = mx;
     __syncthreads();
 
-    // The range's maximum and sum for head r, and each tile's weight.
-    float mw[kWaves], lw[kWaves];
+    // Probabilities against the range's maximum M (0 for a row with no key in
+    // the range), published as bf16 hi + lo parts with this wave's sum; V staged.
+    float M = lds.m[0][r];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        mw[w] = lds.m[w][r];
-        lw[w] = lds.l[w][r];
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, lds.m[w][r]);
+    const float m_ref = M == -INFINITY ? 0.f : M;
+    float psum = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+        bf16x4_t hi, lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(sc[blk][i] - m_ref);
+            psum += p;
+            hi[i] = (__bf16)p;
+            lo[i] = (__bf16)(p - (float)hi[i]);
+        }
+        const u32x2_t h = __builtin_bit_cast(u32x2_t, hi);
+        const u32x2_t l = __builtin_bit_cast(u32x2_t, lo);
+        lds.p[wave][blk][lane] = u32x4_t{h[0], h[1], l[0], l[1]};
     }
-    float M = mw[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mw[w]);
+    const float lsum = sum_rows(psum);
+    if (grp == 0) lds.l[wave][r] = lsum;
+    unsigned short *stage = lds.stage(wave);
+    if (has) {
+        if (SPEC && t0 + TT > len) zero_v_past(tile, t0, len, grp);  // read against the capacity
+    } else {
+        zero_v_past(tile, t0, t0, grp);  // no keys: a zero V block meets zero probabilities
+    }
+    stage_v(tile, r, grp, stage);
+    __syncthreads();
+
     float L = 0.f;
-    float cw[kWaves];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        // a tile without keys has m = -inf, l = 0 and is skipped below
-        cw[w] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
-        L += cw[w] * lw[w];
-    }
+    for (int w = 0; w < kWaves; ++w) L += lds.l[w][r];
 
     // PV over the range's 4 * NB blocks of 16 keys for this wave's quarter of
     // the dims, two blocks per 32-deep MFMA: contraction slots 8*grp .. + 3 hold
@@ -998,24 +1016,21 @@ __device__ __forceinline__ void process_single(const SplitArgs &a, FoldLds<D, NB
     for (int j = 0; j < NQ; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < NBLK; e += 2) {
-        bf16x8_t hi, lo;
+        u32x4_t pp[2];
         bf16x4_t av[2][NQ];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int w = (e + h) / NB;
             const int blk = (e + h) % NB;
-            const f32x4_t pw = lds.p[w][blk][lane] * cw[w];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                hi[4 * h + i] = (__bf16)pw[i];
-                lo[4 * h + i] = (__bf16)(pw[i] - (float)hi[4 * h + i]);
-            }
+            pp[h] = lds.p[w][blk][lane];
             const unsigned short *src = lds.stage(w) + (16 * blk + 4 * grp + (r >> 2)) * RS + 4 * (r & 3);
 #pragma unroll
             for (int j = 0; j < NQ; ++j)
                 av[h][j] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                                             (lds_i16x4_t *)(src + 16 * (wave * NQ + j))));
         }
+        const bf16x8_t hi = __builtin_bit_cast(bf16x8_t, u32x4_t{pp[0][0], pp[0][1], pp[1][0], pp[1][1]});
+        const bf16x8_t lo = __builtin_bit_cast(bf16x8_t, u32x4_t{pp[0][2], pp[0][3], pp[1][2], pp[1][3]});
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             const bf16x8_t v2 = __builtin_shufflevector(av[0][j], av[1][j], 0, 1, 2, 3, 4, 5, 6, 7);
