@@ -1014,28 +1014,63 @@ __device__ __forceinline__ void process_single(const SplitArgs &a, FoldLds<D, NB
     f32x4_t acc[NQ];
 #pragma unroll
     for (int j = 0; j < NQ; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (a.R <= 8) {
+        // At most 8 head rows: MFMA columns 8..15 carry the lo parts of rows
+        // 0..7 (lane r >= 8 reads the lo half of lane r - 8's entry), so one
+        // MFMA per pair takes both parts; each row's two column sums are added
+        // once at the end (a row-of-16 rotation by 8).
+        const int src = r < 8 ? lane : lane - 8;
+        const int part = r < 8 ? 0 : 1;
 #pragma unroll
-    for (int e = 0; e < NBLK; e += 2) {
-        u32x4_t pp[2];
-        bf16x4_t av[2][NQ];
+        for (int e = 0; e < NBLK; e += 2) {
+            u32x2_t pp[2];
+            bf16x4_t av[2][NQ];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int w = (e + h) / NB;
-            const int blk = (e + h) % NB;
-            pp[h] = lds.p[w][blk][lane];
-            const unsigned short *src = lds.stage(w) + (16 * blk + 4 * grp + (r >> 2)) * RS + 4 * (r & 3);
+            for (int h = 0; h < 2; ++h) {
+                const int w = (e + h) / NB;
+                const int blk = (e + h) % NB;
+                pp[h] = reinterpret_cast<const u32x2_t *>(&lds.p[w][blk][src])[part];
+                const unsigned short *vsrc = lds.stage(w) + (16 * blk + 4 * grp + (r >> 2)) * RS + 4 * (r & 3);
 #pragma unroll
-            for (int j = 0; j < NQ; ++j)
-                av[h][j] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                            (lds_i16x4_t *)(src + 16 * (wave * NQ + j))));
+                for (int j = 0; j < NQ; ++j)
+                    av[h][j] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                                (lds_i16x4_t *)(vsrc + 16 * (wave * NQ + j))));
+            }
+            const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u32x4_t{pp[0][0], pp[0][1], pp[1][0], pp[1][1]});
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                const bf16x8_t v2 = __builtin_shufflevector(av[0][j], av[1][j], 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v2, pb, acc[j], 0, 0, 0);
+            }
         }
-        const bf16x8_t hi = __builtin_bit_cast(bf16x8_t, u32x4_t{pp[0][0], pp[0][1], pp[1][0], pp[1][1]});
-        const bf16x8_t lo = __builtin_bit_cast(bf16x8_t, u32x4_t{pp[0][2], pp[0][3], pp[1][2], pp[1][3]});
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-            const bf16x8_t v2 = __builtin_shufflevector(av[0][j], av[1][j], 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v2, hi, acc[j], 0, 0, 0);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v2, lo, acc[j], 0, 0, 0);
+        for (int j = 0; j < NQ; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[j][i] += row_ror(acc[j][i], 8);
+    } else {
+#pragma unroll
+        for (int e = 0; e < NBLK; e += 2) {
+            u32x4_t pp[2];
+            bf16x4_t av[2][NQ];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int w = (e + h) / NB;
+                const int blk = (e + h) % NB;
+                pp[h] = lds.p[w][blk][lane];
+                const unsigned short *src = lds.stage(w) + (16 * blk + 4 * grp + (r >> 2)) * RS + 4 * (r & 3);
+#pragma unroll
+                for (int j = 0; j < NQ; ++j)
+                    av[h][j] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                                (lds_i16x4_t *)(src + 16 * (wave * NQ + j))));
+            }
+            const bf16x8_t hi = __builtin_bit_cast(bf16x8_t, u32x4_t{pp[0][0], pp[0][1], pp[1][0], pp[1][1]});
+            const bf16x8_t lo = __builtin_bit_cast(bf16x8_t, u32x4_t{pp[0][2], pp[0][3], pp[1][2], pp[1][3]});
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                const bf16x8_t v2 = __builtin_shufflevector(av[0][j], av[1][j], 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v2, hi, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v2, lo, acc[j], 0, 0, 0);
+            }
         }
     }
     if constexpr (KV == kKvFp8) {
