@@ -272,9 +272,11 @@ __device__ __forceinline__ void load_tile(Tile<D, NB, KV> &t, __amdgpu_buffer_rs
 //   kPvF32  v_mfma_f32_16x16x4_f32 on V widened to fp32 straight from the
 //           load registers (exact products, 2048 MFMA cycles per 16 keys at
 //           head_dim 256);
-//   kPvBf16 v_mfma_f32_16x16x16_bf16 with P split into bf16 hi + lo parts
-//           (P = hi + lo to about 2^-17 relative) and V transposed through a
-//           per-wave LDS buffer (8x fewer MFMA cycles than kPvF32).
+//   kPvBf16 bf16 MFMAs with P split into bf16 hi + lo parts (P = hi + lo to
+//           about 2^-17 relative) and V transposed through a per-wave LDS
+//           buffer (8x fewer MFMA cycles than kPvF32): v_mfma_f32_16x16x16_bf16
+//           per 16 keys in key ranges; in one-tile ranges 32-deep MFMAs over
+//           pairs of 16-key blocks (process_single).
 constexpr int kPvF32 = 0;
 constexpr int kPvBf16 = 1;
 
