@@ -1284,12 +1284,13 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
 // pieces s with s % NSG == sg (NSG = 256 / NCOL).  It loads U of its pieces
 // at a time and folds each round into its running (m, l, o) against the
 // round's maximum (independent exponentials, not a chain of merges).  The
-// NSG folds of a column are then combined max first: the column's maximum M
-// over the workgroup (a max tree inside each wave over the lanes that share c,
-// row rotations then the row-pair and half-wave swaps, and the four waves
-// through LDS), each fold rescaled once by 2^(m - M), and the rescaled (l, o)
-// summed by the same tree and then the four waves in order.  Every step has a
-// fixed order, so the result is bit-reproducible.
+// NSG folds of a column are then combined max first inside each wave: the
+// wave's maximum for the column (a max tree over the lanes that share c: row
+// rotations, then the row-pair and half-wave swaps), each fold rescaled once to
+// it, and the rescaled (l, o) summed by the same tree; the four waves' results
+// then meet in LDS (one barrier) and the column's thread merges them in wave
+// order against their common maximum.  Every step has a fixed order, so the
+// result is bit-reproducible.
 constexpr int kCombineThreads = 256;
 
 struct Fold {
@@ -1391,8 +1392,8 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
         }
     }
 
-    // The column's maximum: lanes of one column inside a wave are c, c + NCOL,
-    // ... (64 / NCOL of them), then the four waves through LDS.
+    // The wave's maximum for column c: lanes of one column inside a wave are c,
+    // c + NCOL, ... (64 / NCOL of them).
     __shared__ float wm[kWaves][NCOL], wl[kWaves][NCOL];
     __shared__ f32x4_t wo[kWaves][NCOL];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1405,15 +1406,11 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
         q = halves32(fmaxf(q.lo, q.hi));
         mx = fmaxf(q.lo, q.hi);
     }
-    if (lane < NCOL) wm[wave][lane] = mx;
-    __syncthreads();
-    float M = wm[0][c];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w][c]);
 
-    // Each fold rescaled to M once (an empty fold, m = -inf, weighs 0), then
-    // the sums: the same tree inside the wave, the waves in order.
-    const float wt = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(run.m - M);
+    // Each fold rescaled to the wave's maximum once (an empty fold, m = -inf,
+    // weighs 0), then the sums by the same tree; the four waves' (max, sums)
+    // meet in LDS and are merged in wave order by the column's thread.
+    const float wt = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(run.m - mx);
     float sl = run.l * wt;
     f32x4_t so = run.o * wt;
     auto add_ror = [&](int n) {
@@ -1436,17 +1433,22 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
     add_swap([](float v) { return rows16(v); });
     add_swap([](float v) { return halves32(v); });
     if (lane < NCOL) {
+        wm[wave][lane] = mx;
         wl[wave][lane] = sl;
         wo[wave][lane] = so;
     }
     __syncthreads();
     if (threadIdx.x < NCOL) {
+        float M = wm[0][c];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w][c]);
         float L = 0.f;
         f32x4_t O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            L += wl[w][c];
-            O += wo[w][c];
+            const float ww = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(wm[w][c] - M);
+            L += ww * wl[w][c];
+            O += ww * wo[w][c];
         }
         // row h = kvh * G + i * Gh + gh of sequence b is out[b][i][kvh * Gh + gh]
         size_t orow = bh;
