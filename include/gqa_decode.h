@@ -10,7 +10,7 @@
  * head h reads kv head h / G) and len = seq_lens[b].  The KV range of every
  * (sequence, kv head) is cut into splits; each split emits unnormalised
  * partials (m, l, acc) that a combine step folds with the log-sum-exp rescale
- * in ascending split order (sparkinfer PR #877 "split the flash-decode KV range
+ * in a fixed order (sparkinfer PR #877 "split the flash-decode KV range
  * across warp-groups", section Mechanism; AstrAI csrc commit log, the split-KV
  * decode bullets: partials over gridDim.z blocks reduced by a combine kernel,
  * split count chosen to fill the device).  All G query heads of a kv head are
