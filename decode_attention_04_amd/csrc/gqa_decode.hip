@@ -2219,7 +2219,12 @@ gqa_status_t gqa_decode_combine_fp8(const void *workspace, size_t workspace_byte
 }
 
 const char *gqa_status_string(gqa_status_t status) {
-    switch (status) {
+    // A C caller may pass any int: read it as one (an enum object holding a
+    // value outside the enumerators must not be loaded as the enum in C++).
+    static_assert(sizeof(gqa_status_t) == sizeof(int), "the C ABI passes the status as an int");
+    int code;
+    memcpy(&code, &status, sizeof code);
+    switch (code) {
         case GQA_OK: return "ok";
         case GQA_ERR_NULL: return "a required pointer is NULL";
         case GQA_ERR_SHAPE: return "a size is out of range or inconsistent";
