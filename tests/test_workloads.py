@@ -79,3 +79,20 @@ def test_fp8_cases():
     assert c.algorithmic_bytes() == 57 * 2 * 64 * 2 + 2 * 8 * 64 * 6
     p = W.fp8_paged_case(4, 8, 2, 64, 16, 64, max_len=100, seed=4)
     assert p.paged and p.k.dtype == np.uint8 and p.page_table.shape == (4, 7)
+
+
+def test_random_parity_draws_are_valid():
+    """The random-shape parity generator: every draw respects the library's limits, and the cases
+    it builds have the drawn shapes and lengths (the GPU test compares them with the oracle)."""
+    from tests import test_gpu_random as R
+    for i in range(R.N_CASES):
+        c = R.draw(i)
+        assert c == R.draw(i)
+        assert c["M"] * c["G"] <= 16 and c["page_size"] % 16 == 0
+        assert len(c["lens"]) == c["B"] and all(0 <= n <= c["S_max"] for n in c["lens"])
+        if i % 5:
+            continue  # building every case takes half a minute; every fifth covers each kind
+        case = R.build(c)
+        assert case.B == c["B"] and case.Hq == c["G"] * c["Hkv"] and case.D == c["D"]
+        assert case.M == c["M"] and list(case.seq_lens) == c["lens"]
+        assert case.paged == ("paged" in c["kind"]) and case.kv == ("fp8" if c["kind"].startswith("fp8") else "bf16")
