@@ -192,7 +192,7 @@ def main():
                    args.splits, torch.cuda.get_device_properties(0).multi_processor_count)
     need = gd.gqa_decode_workspace_bytes(case.B, case.M * case.Hq, case.Hkv, case.D, cap, case.page_size,
                                          args.splits)
-    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    ws = gd.new_workspace(max(need, gd.COUNTER_BYTES))
     oshape = (case.B, case.Hq, case.D) if case.M == 1 else (case.B, case.M, case.Hq, case.D)
     outs = [torch.empty(oshape, dtype=torch.float32, device="cuda")
             for _ in range(R)]

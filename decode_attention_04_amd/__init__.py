@@ -13,6 +13,7 @@ Entry points mirror include/gqa_decode.h:
     gqa_decode_partials / gqa_paged_decode_partials + gqa_decode_combine (the two kernels apart)
     gqa_decode_fp8 / gqa_paged_decode_fp8 (+ _partials, gqa_decode_combine_fp8, gqa_decode_plan_fp8)
     gqa_decode_mq / gqa_paged_decode_mq (M query tokens per sequence)
+    gqa_decode_get_tuning / gqa_decode_set_tuning, and `tuning(**fields)` (a context manager)
     gqa_status_string(code)
 bf16 tensors may be torch.bfloat16 or int16/uint16 views of the bit patterns.
 """
@@ -25,6 +26,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgqa_decode.so")
 
 GQA_OK = 0
+# bytes at the start of every workspace that hold the in-kernel fold's arrival counters: they must
+# be zero before a workspace is first used (every call leaves them zero)
+COUNTER_BYTES = 16384
 STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_UNSUPPORTED",
                 4: "GQA_ERR_ALIGN", 5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_HIP"}
 
@@ -33,7 +37,8 @@ EXPORTED = ("gqa_decode_plan", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_
             "gqa_decode_partials", "gqa_paged_decode_partials", "gqa_decode_combine",
             "gqa_decode_fp8", "gqa_paged_decode_fp8", "gqa_decode_fp8_partials",
             "gqa_paged_decode_fp8_partials", "gqa_decode_plan_fp8", "gqa_decode_combine_fp8",
-            "gqa_decode_mq", "gqa_paged_decode_mq", "gqa_status_string")
+            "gqa_decode_mq", "gqa_paged_decode_mq", "gqa_decode_get_tuning", "gqa_decode_set_tuning",
+            "gqa_status_string")
 
 
 class GqaError(RuntimeError):
@@ -49,7 +54,18 @@ class Plan(ctypes.Structure):
                 ("max_pieces", ctypes.c_int), ("slots", ctypes.c_int64),
                 ("pv_mode", ctypes.c_int),
                 ("double_buffer", ctypes.c_int), ("streaming", ctypes.c_int),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("fused", ctypes.c_int),
+                ("fold_fanin", ctypes.c_int), ("counters", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class Tuning(ctypes.Structure):
+    """gqa_tuning_t: the plan and kernel-variant choices (see include/gqa_decode.h)."""
+    _fields_ = [(name, ctypes.c_int) for name in (
+        "tile_tokens", "double_buffer", "pv_mode", "streaming", "partition", "shares", "split_keys",
+        "piece_cost", "halve_long", "combine", "combine_cols", "num_splits", "fold")]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -100,6 +116,10 @@ def load(path: str = LIB_PATH):
     lib.gqa_paged_decode_mq.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, cf, vp,
                                         vp, sz, ci, vp]
     lib.gqa_paged_decode_mq.restype = ci
+    lib.gqa_decode_get_tuning.argtypes = [ctypes.POINTER(Tuning)]
+    lib.gqa_decode_get_tuning.restype = None
+    lib.gqa_decode_set_tuning.argtypes = [ctypes.POINTER(Tuning)]
+    lib.gqa_decode_set_tuning.restype = ci
     lib.gqa_status_string.argtypes = [ci]
     lib.gqa_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -128,6 +148,40 @@ def gqa_decode_plan_fp8(B, Hq, Hkv, head_dim, max_seq_len, page_size=0, num_spli
     """The plan of a call over an E4M3 cache (paged head_dim 128 takes 32-key tiles)."""
     return gqa_decode_plan(B, Hq, Hkv, head_dim, max_seq_len, page_size, num_splits, cu_count,
                            _entry="gqa_decode_plan_fp8")
+
+
+def gqa_decode_get_tuning() -> Tuning:
+    t = Tuning()
+    load().gqa_decode_get_tuning(ctypes.byref(t))
+    return t
+
+
+def gqa_decode_set_tuning(t: Tuning) -> None:
+    rc = load().gqa_decode_set_tuning(ctypes.byref(t))
+    if rc != GQA_OK:
+        raise GqaError(rc, "gqa_decode_set_tuning")
+
+
+class tuning:
+    """Context manager: run the body under the current tuning with some fields replaced, e.g.
+    `with tuning(fold=2, shares=7): ...`; the previous tuning is restored on exit."""
+
+    def __init__(self, **fields):
+        self.fields = fields
+
+    def __enter__(self):
+        self.saved = gqa_decode_get_tuning()
+        t = gqa_decode_get_tuning()
+        for k, v in self.fields.items():
+            if k not in t.as_dict():
+                raise KeyError(f"no tuning field {k!r}")
+            setattr(t, k, int(v))
+        gqa_decode_set_tuning(t)
+        return t
+
+    def __exit__(self, *exc):
+        gqa_decode_set_tuning(self.saved)
+        return False
 
 
 def gqa_decode_workspace_bytes(B, Hq, Hkv, head_dim, max_seq_len, page_size=0, num_splits=0):
@@ -166,12 +220,29 @@ def _stream_ptr(stream, device):
     return s.cuda_stream
 
 
-def _workspace(workspace, need, device):
+def _alloc(shape, dtype, device, stream, zero=False):
+    """A buffer the binding allocates for one call.  It is allocated on the stream the kernels
+    run on: the caching allocator then never hands its memory to other work until that stream
+    has passed the kernels, even after the tensor is dropped."""
     torch = _torch()
+    make = torch.zeros if zero else torch.empty
+    if stream is None:
+        return make(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return make(shape, dtype=dtype, device=device)
+
+
+def new_workspace(nbytes, device="cuda", stream=None):
+    """A workspace for gqa_* calls: zero-filled (its arrival counters must start at zero; every
+    call leaves them zero again), reusable by any later call of any shape on the same stream."""
+    return _alloc(max(int(nbytes), 0), _torch().uint8, device, stream, zero=True)
+
+
+def _workspace(workspace, need, device, stream):
     if need == 0:
         return None, 0
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        workspace = new_workspace(need, device, stream)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -179,15 +250,16 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None, n
                stream=None, _entry="gqa_decode"):
     """Contiguous cache: q [B,Hq,D], k/v [B,Hkv,S_max,D] bf16, seq_lens int32 [B].
 
-    Returns out (fp32 [B,Hq,D]).  `workspace` (a uint8 device tensor) is
-    allocated when not given; pass one to keep the call allocation-free."""
+    Returns out (fp32 [B,Hq,D]).  `workspace` (a uint8 device tensor from new_workspace, or any
+    buffer whose first 16384 bytes are zero) is allocated when not given; pass one to keep the
+    call allocation-free."""
     torch = _torch()
     B, Hq, D = q.shape
     _, Hkv, S_max, _ = k_cache.shape
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        out = _alloc((B, Hq, D), torch.float32, q.device, stream)
     need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, S_max, 0, num_splits)
-    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    workspace, ws_bytes = _workspace(workspace, need, q.device, stream)
     bf = _bf16_types()
     rc = getattr(load(), _entry)(
         _dev_ptr(q, "q", bf), _dev_ptr(k_cache, "k_cache", bf), _dev_ptr(v_cache, "v_cache", bf),
@@ -208,9 +280,9 @@ def gqa_paged_decode(q, k_pool, v_pool, seq_lens, page_table, scale, out=None, w
     P, Hkv, page_size, _ = k_pool.shape
     max_pages = page_table.shape[1]
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        out = _alloc((B, Hq, D), torch.float32, q.device, stream)
     need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, max_pages * page_size, page_size, num_splits)
-    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    workspace, ws_bytes = _workspace(workspace, need, q.device, stream)
     bf = _bf16_types()
     rc = getattr(load(), _entry)(
         _dev_ptr(q, "q", bf), _dev_ptr(k_pool, "k_pool", bf), _dev_ptr(v_pool, "v_pool", bf),
@@ -237,9 +309,9 @@ def gqa_decode_fp8(q, k_cache, v_cache, seq_lens, scale, k_scale, v_scale, out=N
     B, Hq, D = q.shape
     _, Hkv, S_max, _ = k_cache.shape
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        out = _alloc((B, Hq, D), torch.float32, q.device, stream)
     need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, S_max, 0, num_splits)
-    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    workspace, ws_bytes = _workspace(workspace, need, q.device, stream)
     f8 = _fp8_types()
     rc = getattr(load(), _entry)(
         _dev_ptr(q, "q", _bf16_types()), _dev_ptr(k_cache, "k_cache", f8),
@@ -262,9 +334,9 @@ def gqa_paged_decode_fp8(q, k_pool, v_pool, seq_lens, page_table, scale, k_scale
     P, Hkv, page_size, _ = k_pool.shape
     max_pages = page_table.shape[1]
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        out = _alloc((B, Hq, D), torch.float32, q.device, stream)
     need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, max_pages * page_size, page_size, num_splits)
-    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    workspace, ws_bytes = _workspace(workspace, need, q.device, stream)
     f8 = _fp8_types()
     rc = getattr(load(), _entry)(
         _dev_ptr(q, "q", _bf16_types()), _dev_ptr(k_pool, "k_pool", f8),
@@ -306,9 +378,9 @@ def gqa_decode_mq(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None
     B, M, Hq, D = q.shape
     _, Hkv, S_max, _ = k_cache.shape
     if out is None:
-        out = torch.empty((B, M, Hq, D), dtype=torch.float32, device=q.device)
+        out = _alloc((B, M, Hq, D), torch.float32, q.device, stream)
     need = gqa_decode_workspace_bytes(B, M * Hq, Hkv, D, S_max, 0, num_splits)
-    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    workspace, ws_bytes = _workspace(workspace, need, q.device, stream)
     bf = _bf16_types()
     rc = load().gqa_decode_mq(
         _dev_ptr(q, "q", bf), _dev_ptr(k_cache, "k_cache", bf), _dev_ptr(v_cache, "v_cache", bf),
@@ -329,10 +401,10 @@ def gqa_paged_decode_mq(q, k_pool, v_pool, seq_lens, page_table, scale, out=None
     P, Hkv, page_size, _ = k_pool.shape
     max_pages = page_table.shape[1]
     if out is None:
-        out = torch.empty((B, M, Hq, D), dtype=torch.float32, device=q.device)
+        out = _alloc((B, M, Hq, D), torch.float32, q.device, stream)
     need = gqa_decode_workspace_bytes(B, M * Hq, Hkv, D, max_pages * page_size, page_size,
                                       num_splits)
-    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    workspace, ws_bytes = _workspace(workspace, need, q.device, stream)
     bf = _bf16_types()
     rc = load().gqa_paged_decode_mq(
         _dev_ptr(q, "q", bf), _dev_ptr(k_pool, "k_pool", bf), _dev_ptr(v_pool, "v_pool", bf),

@@ -50,6 +50,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "gqa_decode.h"
 
@@ -92,6 +93,9 @@ struct SplitArgs {
     int halve_long;             // even partition, contiguous cache: one share per CU for long segments
     float qk_scale_log2;        // scale * log2(e) (times k_scale for an E4M3 cache)
     float v_scale;              // E4M3 cache: V's per-tensor scale
+    unsigned *counters;         // in-kernel fold: the arrival counters (workspace header)
+    int fused;                  // 1: this kernel folds the partials itself
+    int fanin;                  // fused fixed splits: partials per node of the fold tree
 };
 
 struct CombineArgs {
@@ -467,6 +471,7 @@ struct FoldLds {
     float l[kWaves][kMaxHeadsPerKv];
     alignas(16) unsigned char region[kWaves][kRegion];
     u32x4_t p[kWaves][NB][64];  // one-tile ranges: each wave's probabilities (bf16 hi, lo), in its lane layout
+    unsigned ticket[2];         // in-kernel fold: arrival tickets
     __device__ float *acc(int w) { return reinterpret_cast<float *>(region[w]); }
     __device__ unsigned short *stage(int w) { return reinterpret_cast<unsigned short *>(region[w]); }
 };
@@ -1108,6 +1113,165 @@ __device__ __forceinline__ void process_single(const SplitArgs &a, FoldLds<D, NB
     }
 }
 
+// ------------------------------------------------------------ the fold
+//
+// The partials of one (sequence b, kv head) segment are folded with the
+// log-sum-exp rescale (AstrAI csrc commit log, split-KV bullets; sparkinfer
+// PR #877, section Mechanism), either by a combine kernel after the split
+// kernel, or -- the in-kernel fold -- by the split workgroup that finishes a
+// group of partials last, which it learns from an arrival ticket.
+
+struct Fold {
+    float m, l;
+    f32x4_t o;
+};
+
+constexpr int kNarrowPieces = 16;  // partials loaded per round of a column fold
+
+// One output column (4 dims of one row) over partials s = 0 .. n-1, where
+// load(s) gives partial s's (m, l, 4 accumulator values), skipping the slots
+// `skip(s)` names (a share that holds no tile writes nothing): rounds of
+// kNarrowPieces partials in ascending order, each folded against the round's
+// maximum.  The thread-per-column combine kernel and the in-kernel fold both
+// call this, so the two give the same bits.
+template <typename Load, typename Skip>
+__device__ __forceinline__ Fold fold_column(int n, Load load, Skip skip) {
+    float M = -INFINITY, L = 0.f;
+    f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < n; s0 += kNarrowPieces) {
+        float mv[kNarrowPieces], lv[kNarrowPieces];
+        f32x4_t av[kNarrowPieces];
+        // Every load goes out before any is used (no branch around them):
+        // slots past the last are read as the last one, and their values and
+        // those of skipped slots are replaced by an empty partial.  The slot
+        // flags are settled before the loads are issued: computed after them,
+        // with a different segment per lane, the generated code (hipcc, ROCm
+        // 7.2) flagged every slot after the first as skipped.
+        bool used[kNarrowPieces];
+#pragma unroll
+        for (int u = 0; u < kNarrowPieces; ++u) used[u] = s0 + u < n && !skip(s0 + u);
+        Fold x[kNarrowPieces];
+#pragma unroll
+        for (int u = 0; u < kNarrowPieces; ++u) x[u] = load(min(s0 + u, n - 1));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kNarrowPieces; ++u) {
+            mv[u] = used[u] ? x[u].m : -INFINITY;
+            lv[u] = used[u] ? x[u].l : 0.f;
+            av[u] = used[u] ? x[u].o : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        float mr = M;
+#pragma unroll
+        for (int u = 0; u < kNarrowPieces; ++u) mr = fmaxf(mr, mv[u]);
+        if (mr != -INFINITY) {
+            const float wr = __builtin_amdgcn_exp2f(M - mr);
+            L *= wr;
+            O *= wr;
+#pragma unroll
+            for (int u = 0; u < kNarrowPieces; ++u) {
+                const float w = __builtin_amdgcn_exp2f(mv[u] - mr);
+                L += w * lv[u];
+                O += w * av[u];
+            }
+            M = mr;
+        }
+    }
+    return Fold{M, L, O};
+}
+
+// Arrival counters of the in-kernel fold: the first kCounterBytes of the
+// workspace, one 32-bit word per group of partials, zero between calls.
+constexpr int kCounterBytes = 16384;
+constexpr int kMaxCounters = kCounterBytes / 4;
+
+// The ticket of a workgroup that has written its partial of a group of n:
+// true for the last to arrive.  Every thread first waits until its own
+// device-scope partial stores are complete, so when the last ticket is handed
+// out every partial of the group is visible at device scope; the counter
+// wraps back to zero on that last ticket (atomic increment modulo n), ready
+// for the next call.  A vector (global) atomic; the result reaches the other
+// threads through LDS.
+__device__ __forceinline__ bool arrive_last(unsigned *ctr, int n, unsigned *lds_ticket) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are done
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *lds_ticket = __builtin_amdgcn_atomic_inc32(ctr, (unsigned)(n - 1), __ATOMIC_RELAXED, "agent");
+    __syncthreads();
+    const bool last = *lds_ticket == (unsigned)(n - 1);
+    __syncthreads();  // the ticket word is free again
+    return last;
+}
+
+// Nodes above the leaves of the fold tree over S partials with fan-in F
+// (levels of ceil(n / F) nodes until one, the root, is left).
+__host__ __device__ __forceinline__ int fold_tree_nodes(int S, int F) {
+    int nodes = 0;
+    for (int n = S; n > 1;) {
+        n = (n + F - 1) / F;
+        nodes += n;
+    }
+    return nodes;
+}
+
+// Even partition: slot s of a segment whose first piece is share w0 was
+// written only if share w0 + s holds a tile (shares can be empty only when
+// there are fewer positions than shares).
+struct EmptyShareSkip {
+    long long w0, N, P;
+    bool maybe_empty;
+    __device__ bool operator()(int s) const {
+        return maybe_empty && share_begin(w0 + s, N, P) >= share_begin(w0 + s + 1, N, P);
+    }
+};
+
+// In-kernel fold of one segment's partials (slots lo .. lo + n - 1, R rows
+// each; with maybe_empty, slots of empty shares from w0 on are skipped as in
+// EmptyShareSkip) by all threads of the workgroup: into the segment's output
+// rows (final; row g = query token g / G, head kvh * G + g % G) or, as one
+// more partial, into slot dst.  The partials were written by other
+// workgroups of this launch: device-scope loads and stores.  Each split
+// kernel calls it from one site (keeps the build small).
+template <int D>
+__device__ __forceinline__ void fold_segment(float *part_acc, float *part_ml, float *out, int R, int G, int M, int Hq,
+                                          size_t lo, int n, long long w0, long long N, long long P, int maybe_empty,
+                                          int b, int kvh, int final, size_t dst) {
+    const EmptyShareSkip skip{w0, N, P, maybe_empty != 0};
+    // Every column belongs to this segment: buffer resources on its first
+    // slot (uniform), each lane's column as the offset.
+    const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(part_ml + lo * R * 2), (short)0, n * R * 2 * 4, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(part_acc + lo * R * D), (short)0, n * R * D * 4, kRsrcWord3);
+    for (int col = threadIdx.x; col < R * (D / 4); col += 64 * kWaves) {
+        const int g = col / (D / 4);
+        const int d = 4 * (col - g * (D / 4));
+        auto load = [&](int s) {
+            const u32x2_t x = __builtin_bit_cast(
+                u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rm, (s * R + g) * 8, 0, kDeviceScope));
+            const f32x4_t v = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, ((s * R + g) * D + d) * 4, 0, kDeviceScope));
+            return Fold{__uint_as_float(x[0]), __uint_as_float(x[1]), v};
+        };
+        const Fold f = fold_column(n, load, skip);
+        if (final) {
+            const int i = g / G;
+            float *orow = out + (((size_t)b * M + i) * Hq + (size_t)kvh * G + (g - i * G)) * D;
+            *reinterpret_cast<f32x4_t *>(orow + d) = f.l > 0.f ? f.o / f.l : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        } else {
+            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(part_acc + dst * R * D), (short)0, R * D * 4, kRsrcWord3);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, f.o), ra, (g * D + d) * 4, 0,
+                                                   kDeviceScope);
+            if (d == 0) {
+                const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(part_ml + dst * R * 2), (short)0, R * 2 * 4, kRsrcWord3);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(f.m), __float_as_uint(f.l)}, rm,
+                                                      g * 8, 0, kDeviceScope);
+            }
+        }
+    }
+}
+
 template <int D, int NB, bool PAGED, int PV, bool DBUF, int PART, int CPOL, int KV>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEu<D, NB, DBUF>)))
 void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const unsigned char *v, const uint16_t *q,
@@ -1137,8 +1301,18 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
         // plus K positions for its start and fold), walked piece by piece.
         const int lane = threadIdx.x & 63;
         const int K = a.piece_cost;
+        // In-kernel fold: no piece covers a sequence of length 0, so the
+        // workgroups zero its output rows (sequences blockIdx.x, + grid, ...).
+        auto zero_empty = [&]() {
+            if (!args.fused) return;
+            for (int bb = blockIdx.x; bb < a.B; bb += gridDim.x) {
+                if (__builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens, bb, cap)) != 0) continue;
+                f32x4_t *o = reinterpret_cast<f32x4_t *>(a.out + (size_t)bb * a.M * a.Hq * D);
+                for (int i = threadIdx.x; i < a.M * a.Hq * (D / 4); i += 64 * kWaves) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        };
         SegmentLocation loc;
-        long long cur, end;
+        long long cur, end, P;
         if (a.B <= 64) {
             // one load of the lengths: the total, then this share's start
             const int ln = lane < a.B ? clamp_len(a.seq_lens, lane, cap) : 0;
@@ -1146,11 +1320,11 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
             const int incl = wave_scan(n, lane);
             const long long N = uniform64((long long)__shfl(incl, 63, 64) * a.Hkv);
             const long long segs = uniform64((long long)wave_sum(ln > 0 ? 1 : 0) * a.Hkv);
-            const long long P = shares_for(gridDim.x, N, segs, K, a.halve_long);
-            if ((long long)blockIdx.x >= P) return;
+            P = shares_for(gridDim.x, N, segs, K, a.halve_long);
+            if ((long long)blockIdx.x >= P) return zero_empty();
             cur = share_begin(blockIdx.x, N, P);
             end = share_begin(blockIdx.x + 1, N, P);
-            if (cur >= end) return;
+            if (cur >= end) return zero_empty();
             const unsigned long long hit =
                 __ballot(lane < a.B && (long long)(incl - n) * a.Hkv <= cur && cur < (long long)incl * a.Hkv);
             const int l = __builtin_ctzll(hit);
@@ -1161,11 +1335,11 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
         } else {
             loc = locate_tile(a.seq_lens, a.B, a.Hkv, cap, TT, K, -1, lane);  // the total only
             const long long segs = a.halve_long ? nonempty_segments(a.seq_lens, a.B, a.Hkv, cap, lane) : 0;
-            const long long P = shares_for(gridDim.x, loc.total, segs, K, a.halve_long);
-            if ((long long)blockIdx.x >= P) return;
+            P = shares_for(gridDim.x, loc.total, segs, K, a.halve_long);
+            if ((long long)blockIdx.x >= P) return zero_empty();
             cur = share_begin(blockIdx.x, loc.total, P);
             end = share_begin(blockIdx.x + 1, loc.total, P);
-            if (cur >= end) return;
+            if (cur >= end) return zero_empty();
             loc = locate_tile(a.seq_lens, a.B, a.Hkv, cap, TT, K, cur, lane);
         }
         int b = loc.b;
@@ -1181,6 +1355,42 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
         // batches of short paged sequences; no gain, and a loss, contiguous).
         bool have_pages = false;
         int pages = 0;
+        // In-kernel fold: a segment this share covers whole is written to
+        // `out` directly; the (at most two) segments it shares with other
+        // workgroups take their arrival tickets once the share is done, so the
+        // stream never stalls on them, and the last piece to arrive folds.
+        const long long N = loc.total;
+        struct Pending {
+            int b, kvh, n, arrivals;
+            long long w0;
+        };
+        Pending pend0{}, pend1{};
+        int npend = 0;
+        // Only the segments holding the share's first and last positions can
+        // extend beyond it (a segment inside the share is held by it alone),
+        // so a share has at most two such pieces pending.
+        auto settle = [&]() {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are done
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                lds.ticket[0] = __builtin_amdgcn_atomic_inc32(args.counters + (size_t)pend0.b * a.Hkv + pend0.kvh,
+                                                              (unsigned)(pend0.arrivals - 1), __ATOMIC_RELAXED, "agent");
+                if (npend > 1)
+                    lds.ticket[1] = __builtin_amdgcn_atomic_inc32(args.counters + (size_t)pend1.b * a.Hkv + pend1.kvh,
+                                                                  (unsigned)(pend1.arrivals - 1), __ATOMIC_RELAXED,
+                                                                  "agent");
+            }
+            __syncthreads();
+            const unsigned t0 = lds.ticket[0], t1 = lds.ticket[1];
+            __syncthreads();  // the ticket words are free again
+#pragma unroll 1
+            for (int i = 0; i < npend; ++i) {  // one call site of the fold
+                const Pending p = i == 0 ? pend0 : pend1;
+                if ((i == 0 ? t0 : t1) != (unsigned)(p.arrivals - 1)) continue;
+                fold_segment<D>(a.part_acc, a.part_ml, a.out, a.R, a.G, a.M, a.Hq,
+                                (size_t)p.w0 + (size_t)p.b * a.Hkv + p.kvh, p.n, p.w0, N, P, N < P, p.b, p.kvh, 1, 0);
+            }
+        };
         while (cur < end) {
             // off < nb_tiles + K here
             const bool same_b = kvh + 1 < a.Hkv;
@@ -1191,6 +1401,25 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
             if (off < nb_tiles) {
                 const int take = (int)min((long long)(nb_tiles - off), end - cur);
                 const size_t slot = (size_t)blockIdx.x + (size_t)b * a.Hkv + kvh;
+                bool whole = false;  // in-kernel fold: this piece is the whole segment
+                if (args.fused) {
+                    // the segment's tiles are axis positions [z, z + nb_tiles), held by shares w0 .. w1
+                    const long long z = cur - off;
+                    const long long w0 = share_of(z, N, P);
+                    const int npieces = (int)(share_of(z + nb_tiles - 1, N, P) - w0 + 1);
+                    if (npieces == 1) {
+                        whole = true;
+                    } else {
+                        int arrivals = npieces;  // shares holding a tile (only those write a piece)
+                        if (N < P)
+                            for (int i = 0; i < npieces; ++i)
+                                arrivals -= share_begin(w0 + i, N, P) >= share_begin(w0 + i + 1, N, P) ? 1 : 0;
+                        const Pending pe{b, kvh, npieces, arrivals, w0};
+                        if (npend == 0) pend0 = pe;
+                        else pend1 = pe;
+                        ++npend;
+                    }
+                }
                 const bool has_next = off + take == nb_tiles && cur + take + K < end;
                 if (PAGED && has_next) {
                     next_len = same_b ? len : load_len_or_zero(a.seq_lens, nb, a.B);
@@ -1200,7 +1429,7 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
                     fetched = true;
                 }
                 process_range<D, NB, PAGED, PV, DBUF, CPOL, KV>(a, lds, b, kvh, len, off * TT,
-                                                                min(len, (off + take) * TT), slot, false, nullptr,
+                                                                min(len, (off + take) * TT), slot, whole, nullptr,
                                                                 have_pages, pages);
                 cur += take;
                 off += take;
@@ -1229,7 +1458,8 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
                 nb_tiles = (len + TT - 1) / TT;
             }
         }
-        return;
+        if (npend > 0) settle();
+        return zero_empty();
     } else {
         const int b = blockIdx.x / (num_splits * Hkv);  // one division before the length load
         const int len_v = load_len_vmem(seq_lens, b);
@@ -1276,6 +1506,35 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
             process_range<D, NB, PAGED, PV, DBUF, CPOL, KV, kSpec>(a, lds, b, kvh, len, t_begin, t_end, slot, direct,
                                                                    &pre);
         }
+        if (args.fused && !direct) {
+            // In-kernel fold: a tree over the segment's splits, fan-in F.  The
+            // last of a node's children to arrive folds them (in ascending
+            // order) into the node's partial, then arrives at the parent; the
+            // root's folder writes the output.  Node j of a level has the
+            // children F*j .. F*j + F - 1 of the level below; level slots and
+            // counters follow the splits' partials, level after level.
+            const int F = args.fanin;
+            const int nodes = fold_tree_nodes(nsplit, F);
+            unsigned *ctr = args.counters + bk * nodes;
+            const size_t tree = (size_t)a.B * a.Hkv * nsplit + bk * (size_t)(nodes - 1);
+            size_t child0 = bk * (size_t)nsplit;  // slot of node 0 of the current level
+            int level_n = nsplit, j = split, off = 0;
+            while (true) {
+                const int parent = j / F;
+                const int first = parent * F;
+                const int cnt = min(F, level_n - first);
+                const int next_n = (level_n + F - 1) / F;
+                if (!arrive_last(ctr + off + parent, cnt, &lds.ticket[0])) break;
+                const bool root = next_n == 1;
+                fold_segment<D>(a.part_acc, a.part_ml, a.out, a.R, a.G, a.M, a.Hq, child0 + first, cnt, 0, 0, 1, 0, b,
+                                kvh, root, tree + off + parent);
+                if (root) break;
+                child0 = tree + off;
+                off += next_n;
+                level_n = next_n;
+                j = parent;
+            }
+        }
     }
 }
 
@@ -1292,11 +1551,6 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
 // order against their common maximum.  Every step has a fixed order, so the
 // result is bit-reproducible.
 constexpr int kCombineThreads = 256;
-
-struct Fold {
-    float m, l;
-    f32x4_t o;
-};
 
 template <int NCOL, int PART>
 __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const float *part_acc, const float *part_ml,
@@ -1467,7 +1721,6 @@ __global__ __launch_bounds__(kCombineThreads) void gqa_combine_kernel(const floa
 // column kNarrowPieces at a time (one round when the segment has no more) and
 // folds each round in ascending order against the round's maximum.  No tree,
 // no LDS, no barrier.
-constexpr int kNarrowPieces = 16;
 constexpr int kNarrowThreads = 64;  // one wave per workgroup: the waves spread over every CU
 
 template <int PART>
@@ -1526,43 +1779,13 @@ __global__ __launch_bounds__(kNarrowThreads) void gqa_combine_narrow_kernel(cons
     const float *ml = a.part_ml + (lo * G + g) * 2;
     const float *acc = a.part_acc + (lo * G + g) * D + d;
     const size_t ml_stride = (size_t)G * 2, acc_stride = (size_t)G * D;
-
-    float M = -INFINITY, L = 0.f;
-    f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < S; s0 += kNarrowPieces) {
-        float mv[kNarrowPieces], lv[kNarrowPieces];
-        f32x4_t av[kNarrowPieces];
-#pragma unroll
-        for (int u = 0; u < kNarrowPieces; ++u) {
-            const int s = s0 + u;
-            mv[u] = -INFINITY;
-            lv[u] = 0.f;
-            av[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            // even partition: a share that holds no tile wrote nothing
-            const bool used = !maybe_empty || share_begin(w0 + s, N, P) < share_begin(w0 + s + 1, N, P);
-            if (s < S && used) {
-                const u32x2_t x = *reinterpret_cast<const u32x2_t *>(ml + s * ml_stride);
-                mv[u] = __uint_as_float(x[0]);
-                lv[u] = __uint_as_float(x[1]);
-                av[u] = *reinterpret_cast<const f32x4_t *>(acc + s * acc_stride);
-            }
-        }
-        float mr = M;
-#pragma unroll
-        for (int u = 0; u < kNarrowPieces; ++u) mr = fmaxf(mr, mv[u]);
-        if (mr != -INFINITY) {
-            const float wr = __builtin_amdgcn_exp2f(M - mr);
-            L *= wr;
-            O *= wr;
-#pragma unroll
-            for (int u = 0; u < kNarrowPieces; ++u) {
-                const float w = __builtin_amdgcn_exp2f(mv[u] - mr);
-                L += w * lv[u];
-                O += w * av[u];
-            }
-            M = mr;
-        }
-    }
+    auto load = [&](int s) {
+        const u32x2_t x = *reinterpret_cast<const u32x2_t *>(ml + s * ml_stride);
+        return Fold{__uint_as_float(x[0]), __uint_as_float(x[1]), *reinterpret_cast<const f32x4_t *>(acc + s * acc_stride)};
+    };
+    const Fold f = fold_column(S, load, EmptyShareSkip{w0, N, P, maybe_empty});
+    const float L = f.l;
+    const f32x4_t O = f.o;
     if (!active) return;
     // row h = kvh * G + i * Gh + gh of sequence b is out[b][i][kvh * Gh + gh]
     size_t orow = (size_t)b * a.Hq + h;
@@ -1577,26 +1800,91 @@ __global__ __launch_bounds__(kNarrowThreads) void gqa_combine_narrow_kernel(cons
 
 constexpr int kMaxDevices = 64;
 constexpr int kDefaultPieceCost = 4;
+constexpr int kDefaultSplitKeys = 2048;
 std::atomic<int> g_cu_count[kMaxDevices];
 
-int env_int(const char *name, int fallback) {
-    const char *s = getenv(name);
-    if (s == nullptr || *s == '\0') return fallback;
-    const int v = atoi(s);
-    return v > 0 ? v : fallback;
+// ------------------------------------------------------------------ tuning
+//
+// The plan and kernel-variant choices every call makes, process-wide.  The
+// defaults are the measured best on MI355X; GQA_DECODE_* environment variables
+// override them for same-binary A/B runs, read once when the library is
+// loaded; gqa_decode_set_tuning replaces the whole set at run time.  Every
+// call copies the tuning once at entry, so the kernels of one call, and the
+// plan they derive, always agree.
+gqa_tuning_t default_tuning() {
+    gqa_tuning_t t{};
+    t.pv_mode = 1;  // kPvBf16
+    t.streaming = 1;
+    t.piece_cost = kDefaultPieceCost;
+    t.halve_long = 1;
+    return t;
+}
+
+bool tuning_valid(const gqa_tuning_t &t) {
+    auto in = [](int v, int lo, int hi) { return v >= lo && v <= hi; };
+    return (t.tile_tokens == 0 || t.tile_tokens == 16 || t.tile_tokens == 32 || t.tile_tokens == 64) &&
+           in(t.double_buffer, 0, 1) && in(t.pv_mode, 0, 1) && in(t.streaming, 0, 1) && in(t.partition, 0, 2) &&
+           in(t.shares, 0, INT32_MAX / 2) && in(t.split_keys, 0, INT32_MAX) && in(t.piece_cost, 0, 1024) &&
+           in(t.halve_long, 0, 1) && in(t.combine, 0, 1) &&
+           (t.combine_cols == 0 || t.combine_cols == 2 || t.combine_cols == 4 || t.combine_cols == 8 ||
+            t.combine_cols == 16) &&
+           in(t.num_splits, 0, INT32_MAX) && in(t.fold, 0, 2);
+}
+
+// Each variable that is set to a valid value replaces its field; anything
+// else leaves the default.
+gqa_tuning_t tuning_from_env() {
+    gqa_tuning_t t = default_tuning();
+    auto num = [](const char *name, int &field, int lo, int hi) {
+        const char *s = getenv(name);
+        if (s == nullptr || *s == '\0') return;
+        char *end = nullptr;
+        const long v = strtol(s, &end, 10);
+        if (*end == '\0' && v >= lo && v <= hi) field = (int)v;
+    };
+    auto is = [](const char *name, const char *value) {
+        const char *s = getenv(name);
+        return s != nullptr && strcmp(s, value) == 0;
+    };
+    int tile = 0, cols = 0;
+    num("GQA_DECODE_TILE", tile, 16, 64);
+    if (tile == 16 || tile == 32 || tile == 64) t.tile_tokens = tile;
+    if (is("GQA_DECODE_DBUF", "1")) t.double_buffer = 1;
+    if (is("GQA_DECODE_PV", "f32")) t.pv_mode = 0;
+    if (is("GQA_DECODE_NT", "0")) t.streaming = 0;
+    if (is("GQA_DECODE_PARTITION", "fixed")) t.partition = 1;
+    if (is("GQA_DECODE_PARTITION", "even")) t.partition = 2;
+    num("GQA_DECODE_SHARES", t.shares, 1, INT32_MAX / 2);
+    num("GQA_DECODE_SPLIT_KEYS", t.split_keys, 1, INT32_MAX);
+    num("GQA_DECODE_PIECE_COST", t.piece_cost, 0, 1024);
+    if (is("GQA_DECODE_HALVE_LONG", "0")) t.halve_long = 0;
+    if (is("GQA_DECODE_COMBINE", "tree")) t.combine = 1;
+    num("GQA_DECODE_COMBINE_COLS", cols, 2, 16);
+    if (cols == 2 || cols == 4 || cols == 8 || cols == 16) t.combine_cols = cols;
+    num("GQA_DECODE_SPLITS", t.num_splits, 1, INT32_MAX);
+    if (is("GQA_DECODE_FOLD", "kernel")) t.fold = 1;
+    if (is("GQA_DECODE_FOLD", "fused")) t.fold = 2;
+    return t;
+}
+
+std::mutex g_tuning_mu;
+gqa_tuning_t g_tuning = tuning_from_env();  // dynamic initialisation: once, at load
+
+gqa_tuning_t current_tuning() {
+    std::lock_guard<std::mutex> lock(g_tuning_mu);
+    return g_tuning;
 }
 
 // Keys per wave tile: 16 KB of K+V per wave (64 keys at D=64, 32 at D=128,
-// 16 at D=256).  GQA_DECODE_TILE (16, 32 or 64) overrides it for A/B runs
-// when the result stays within 16 KB.
-int tile_tokens_for(int D, bool double_buffer, bool paged, int elem_bytes) {
+// 16 at D=256).  A tuned tile (16, 32 or 64) replaces it when the result
+// stays within 16 KB.
+int tile_tokens_for(int D, bool double_buffer, bool paged, int elem_bytes, int tuned) {
     int dflt = double_buffer ? (D <= 64 ? 64 : (D == 128 ? 32 : 16)) : (D == 32 ? 64 : (D == 64 ? 32 : 16));
     // A paged E4M3 cache at head_dim 128: 32 keys, so that a wave still reads
     // 4 KB of K (and of V) in one piece of a page, as a bf16 tile of 16 does
     // (measured: the ragged 8k paged workload 80.2 -> 62.4 us per call).
     if (!double_buffer && paged && elem_bytes == 1 && D == 128) dflt = 32;
-    const int t = env_int("GQA_DECODE_TILE", dflt);
-    if ((t == 16 || t == 32 || t == 64) && t * D <= 4096) return t;
+    if (tuned != 0 && tuned * D <= 4096) return tuned;
     return dflt;
 }
 
@@ -1623,15 +1911,20 @@ gqa_status_t device_cu_count(int *out) {
 }
 
 struct WorkspaceLayout {
-    size_t part_acc, part_ml, total;
+    size_t counters, part_acc, part_ml, total;
 };
 
-// `slots` partial blocks of G heads: B*Hkv*S for fixed splits, P + B*Hkv for
+// The arrival counters of the in-kernel fold first (kCounterBytes, in every
+// plan's workspace, so that calls of any shape can share one workspace without
+// a partial ever landing on a counter), then `slots` partial blocks of G
+// heads: B*Hkv*S (+ the fold tree's nodes) for fixed splits, P + B*Hkv for P
 // even shares.
 WorkspaceLayout workspace_layout(int Hq, int Hkv, int D, int64_t slots) {
     WorkspaceLayout w{};
     const size_t G = (size_t)(Hq / Hkv);
     size_t off = 0;
+    w.counters = off;
+    off += kCounterBytes;
     w.part_acc = off;
     off += align_up((size_t)slots * G * D * sizeof(float), 256);
     w.part_ml = off;
@@ -1640,17 +1933,25 @@ WorkspaceLayout workspace_layout(int Hq, int Hkv, int D, int64_t slots) {
     return w;
 }
 
-// Even shares: axis positions a piece's start and fold are worth, added to
-// every segment's tiles (a piece's first-tile latency plus its fold take about
-// as long as K tiles of streaming).  GQA_DECODE_PIECE_COST overrides it for
-// A/B runs; the split and combine kernels of one call read the same value.
-int piece_cost() {
-    const char *s = getenv("GQA_DECODE_PIECE_COST");
-    if (s != nullptr && *s != '\0') {
-        const int v = atoi(s);
-        if (v >= 0 && v <= 1024) return v;
-    }
-    return kDefaultPieceCost;
+// Which plans fold in the split kernel by default (tuning fold = 0).  On
+// MI355X a level of the in-kernel fold costs more than the second launch it
+// saves: the device-scope store acknowledgement and the ticket take ~1.3 us,
+// and one workgroup folding a group is held to a single CU's memory pipe, where
+// the combine kernel spreads the same reads over the whole device.  Measured,
+// us per call (two launches vs one): GQA-6 hd256 4k 8.6 vs 15.1, 128k keys on
+// one kv head 16.2 vs 20.4, ragged paged 8k 107.6 vs 111.3, uniform 16k batch
+// 83.0 vs 82.6.  So both partitions fold in a combine kernel by default.
+constexpr bool kFuseEvenByDefault = false;
+constexpr bool kFuseFixedByDefault = false;
+
+// Fan-in of the fold tree over S fixed splits: one node for up to
+// kNarrowPieces splits, else the smallest power of two F with F * F >= S
+// (at most kNarrowPieces): two levels up to 256 splits.
+int fold_fanin(int S) {
+    if (S <= kNarrowPieces) return S;
+    int F = 2;
+    while (F * F < S && F < kNarrowPieces) F *= 2;
+    return F;
 }
 
 // Even shares over a contiguous bf16 cache: whether the kernels may take one
@@ -1658,55 +1959,30 @@ int piece_cost() {
 // seq_lens, the same way in the split and combine kernels).  Off for paged
 // caches, for E4M3 caches (half the bytes per tile for the same math: their
 // second workgroup per CU hides it; measured 50.2 -> 62.0 us per call at the
-// batched E4M3 workload with one per CU), and when GQA_DECODE_SHARES fixes the
-// share count or GQA_DECODE_HALVE_LONG=0.
-int halve_long_shares(bool paged, int kv) {
-    if (paged || kv != kKvBf16 || getenv("GQA_DECODE_SHARES") != nullptr) return 0;
-    const char *s = getenv("GQA_DECODE_HALVE_LONG");
-    return (s != nullptr && strcmp(s, "0") == 0) ? 0 : 1;
-}
-
-// Tile buffering: one register tile per wave refilled early (the default;
-// it leaves room for twice the waves), or GQA_DECODE_DBUF=1 for two.
-int env_dbuf() {
-    const char *s = getenv("GQA_DECODE_DBUF");
-    return (s != nullptr && strcmp(s, "1") == 0) ? 1 : 0;
-}
-
-// PV contraction: GQA_DECODE_PV=f32 selects the fp32-MFMA variant for A/B.
-int env_pv_mode() {
-    const char *s = getenv("GQA_DECODE_PV");
-    if (s != nullptr && strcmp(s, "f32") == 0) return kPvF32;
-    return kPvBf16;
-}
-
-int env_splits() {
-    const char *s = getenv("GQA_DECODE_SPLITS");
-    if (s == nullptr || *s == '\0') return 0;
-    const int v = atoi(s);
-    return v > 0 ? v : 0;
+// batched E4M3 workload with one per CU), and when the tuning fixes the share
+// count or turns the rule off.
+int halve_long_shares(const gqa_tuning_t &t, bool paged, int kv) {
+    return (!paged && kv == kKvBf16 && t.shares == 0 && t.halve_long) ? 1 : 0;
 }
 
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
-hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const float *part_ml,
-                          float *out, const int32_t *seq_lens, int B, int M, int Hq, int Hkv, int D,
-                          int cap, int halve_long, hipStream_t stream) {
+hipError_t launch_combine(const gqa_plan_t &plan, const gqa_tuning_t &t, const float *part_acc,
+                          const float *part_ml, float *out, const int32_t *seq_lens, int B, int M, int Hq, int Hkv,
+                          int D, int cap, int halve_long, hipStream_t stream) {
     // rows: M query tokens x Hq heads per sequence, M * G per (sequence, kv head)
     const int rows = M * Hq;
     CombineArgs ca{part_acc, part_ml, out, seq_lens, D, rows / Hkv, rows, plan.num_splits,
-                   B, Hkv, cap, plan.tile_tokens, plan.grid, M, Hq / Hkv, piece_cost(), halve_long};
+                   B, Hkv, cap, plan.tile_tokens, plan.grid, M, Hq / Hkv, t.piece_cost, halve_long};
     // The widest dim chunk (NCOL = 16, 8, 4 or 2 columns of 4 dims) that
     // still gives at least 128 workgroups: narrower chunks put more threads on
     // the pieces of a column (measured best for few heads with many pieces).
-    // GQA_DECODE_COMBINE_COLS = 2, 4, 8 or 16 overrides it.
+    // The tuning's combine_cols (2, 4, 8 or 16) overrides it.
     const int64_t heads = (int64_t)B * rows;
     const bool even = plan.partition == kPartitionEven;
     // Few pieces per segment (at full length): one thread per column folds
-    // them (no tree).  GQA_DECODE_COMBINE=tree keeps the tree for A/B runs.
-    const char *cmb = getenv("GQA_DECODE_COMBINE");
-    const bool tree_only = cmb != nullptr && strcmp(cmb, "tree") == 0;
-    if (!tree_only && plan.max_pieces <= kNarrowPieces) {
+    // them (no tree).  The tuning's combine = 1 keeps the tree for A/B runs.
+    if (t.combine == 0 && plan.max_pieces <= kNarrowPieces) {
         const int64_t waves = (int64_t)B * ((rows * (D / 4) + 63) / 64);
         auto go = [&](auto kernel) {
             hipLaunchKernelGGL(kernel, dim3((unsigned)waves), dim3(kNarrowThreads), 0, stream, ca.part_acc,
@@ -1715,7 +1991,7 @@ hipError_t launch_combine(const gqa_plan_t &plan, const float *part_acc, const f
         even ? go(gqa_combine_narrow_kernel<kPartitionEven>) : go(gqa_combine_narrow_kernel<kPartitionFixed>);
         return hipGetLastError();
     }
-    int ncol = env_int("GQA_DECODE_COMBINE_COLS", 0);
+    int ncol = t.combine_cols;
     if (ncol != 2 && ncol != 4 && ncol != 8 && ncol != 16) {
         ncol = 16;
         while (ncol > 2 && heads * (D / (4 * ncol)) < 128) ncol /= 2;
@@ -1798,16 +2074,21 @@ struct KvSpec {
 };
 constexpr KvSpec kBf16Cache{kKvBf16, 1.f, 1.f};
 
-gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, int kv, void *workspace,
-                 hipStream_t stream, int phases) {
-    a.piece_cost = piece_cost();
-    a.halve_long = halve_long_shares(paged, kv);
+gqa_status_t run(const gqa_plan_t &plan, const gqa_tuning_t &t, SplitArgs &a, int D, bool paged, int kv,
+                 void *workspace, hipStream_t stream, int phases) {
+    a.piece_cost = t.piece_cost;
+    a.halve_long = halve_long_shares(t, paged, kv);
     if (!plan.direct) {
         WorkspaceLayout w = workspace_layout(a.M * a.Hq, a.Hkv, D, plan.slots);
         char *base = static_cast<char *>(workspace);
+        a.counters = reinterpret_cast<unsigned *>(base + w.counters);
         a.part_acc = reinterpret_cast<float *>(base + w.part_acc);
         a.part_ml = reinterpret_cast<float *>(base + w.part_ml);
     }
+    // Only a whole call folds in the split kernel: a *_partials call leaves
+    // every partial for gqa_decode_combine.
+    a.fused = plan.fused && phases == (kPhaseSplit | kPhaseCombine) ? 1 : 0;
+    a.fanin = plan.fold_fanin;
     hipError_t e = hipSuccess;
     if (phases & kPhaseSplit) {
         switch (D) {
@@ -1819,10 +2100,10 @@ gqa_status_t run(const gqa_plan_t &plan, SplitArgs &a, int D, bool paged, int kv
         }
         if (e != hipSuccess) return GQA_ERR_HIP;
     }
-    if (plan.direct || !(phases & kPhaseCombine)) return GQA_OK;
+    if (plan.direct || !(phases & kPhaseCombine) || a.fused) return GQA_OK;
     const int cap = paged ? a.max_pages * a.page_size : a.S_max;
-    e = launch_combine(plan, a.part_acc, a.part_ml, a.out, a.seq_lens, a.B, a.M, a.Hq, a.Hkv, D, cap, a.halve_long,
-                       stream);
+    e = launch_combine(plan, t, a.part_acc, a.part_ml, a.out, a.seq_lens, a.B, a.M, a.Hq, a.Hkv, D, cap,
+                       a.halve_long, stream);
     return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
@@ -1840,32 +2121,50 @@ gqa_status_t check_common(const void *q, const void *k, const void *v, const int
 }
 
 gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_size, int num_splits,
-                       int cu_count, int elem_bytes, gqa_plan_t *plan);
+                       int cu_count, int elem_bytes, const gqa_tuning_t &t, gqa_plan_t *plan);
 
 // elem_bytes: 2 for a bf16 cache, 1 for E4M3.
 gqa_status_t plan_for_call(int B, int Hq, int Hkv, int D, int cap, int page_size, int num_splits,
-                           gqa_plan_t *plan, int elem_bytes = 2) {
-    if (num_splits == 0) num_splits = env_splits();
+                           const gqa_tuning_t &t, gqa_plan_t *plan, int elem_bytes = 2) {
+    if (num_splits == 0) num_splits = t.num_splits;
     int cu = 256;
     if (num_splits == 0) {
         gqa_status_t s = device_cu_count(&cu);
         if (s != GQA_OK) return s;
     }
-    return plan_impl(B, Hq, Hkv, D, cap, page_size, num_splits, cu, elem_bytes, plan);
+    return plan_impl(B, Hq, Hkv, D, cap, page_size, num_splits, cu, elem_bytes, t, plan);
 }
 
 }  // namespace
 
 extern "C" {
 
+// The plan a call with these arguments makes (the tuning's num_splits applies
+// when num_splits is 0, as in a call).
 gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int D, int max_seq_len, int page_size,
                              int num_splits, int cu_count, gqa_plan_t *plan) {
-    return plan_impl(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, cu_count, 2, plan);
+    const gqa_tuning_t t = current_tuning();
+    return plan_impl(B, Hq, Hkv, D, max_seq_len, page_size, num_splits == 0 ? t.num_splits : num_splits, cu_count,
+                     2, t, plan);
 }
 
 gqa_status_t gqa_decode_plan_fp8(int B, int Hq, int Hkv, int D, int max_seq_len, int page_size,
                                  int num_splits, int cu_count, gqa_plan_t *plan) {
-    return plan_impl(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, cu_count, 1, plan);
+    const gqa_tuning_t t = current_tuning();
+    return plan_impl(B, Hq, Hkv, D, max_seq_len, page_size, num_splits == 0 ? t.num_splits : num_splits, cu_count,
+                     1, t, plan);
+}
+
+void gqa_decode_get_tuning(gqa_tuning_t *tuning) {
+    if (tuning != nullptr) *tuning = current_tuning();
+}
+
+gqa_status_t gqa_decode_set_tuning(const gqa_tuning_t *tuning) {
+    if (tuning == nullptr) return GQA_ERR_NULL;
+    if (!tuning_valid(*tuning)) return GQA_ERR_SHAPE;
+    std::lock_guard<std::mutex> lock(g_tuning_mu);
+    g_tuning = *tuning;
+    return GQA_OK;
 }
 
 }  // extern "C"
@@ -1873,7 +2172,7 @@ gqa_status_t gqa_decode_plan_fp8(int B, int Hq, int Hkv, int D, int max_seq_len,
 namespace {
 
 gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_size, int num_splits,
-                       int cu_count, int elem_bytes, gqa_plan_t *plan) {
+                       int cu_count, int elem_bytes, const gqa_tuning_t &t, gqa_plan_t *plan) {
     if (plan == nullptr) return GQA_ERR_NULL;
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_seq_len < 0 || page_size < 0 ||
         num_splits < 0 || cu_count <= 0)
@@ -1881,27 +2180,25 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
     if (!supported_dim(D) || Hq / Hkv > kMaxHeadsPerKv) return GQA_ERR_UNSUPPORTED;
     if (page_size > 0 && page_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
 
-    const int dbuf = env_dbuf();
-    int tt = tile_tokens_for(D, dbuf != 0, page_size > 0, elem_bytes);
+    *plan = gqa_plan_t{};
+    const int dbuf = t.double_buffer;
+    int tt = tile_tokens_for(D, dbuf != 0, page_size > 0, elem_bytes, t.tile_tokens);
     if (page_size > 0) {
         while (page_size % tt != 0) tt /= 2;  // a tile never straddles a page (tt >= 16)
     }
     const int tiles_total = max_seq_len > 0 ? (max_seq_len + tt - 1) / tt : 1;
     const int base = B > 0 ? B * Hkv : 1;
-    const char *part_env = getenv("GQA_DECODE_PARTITION");
-    const bool want_fixed = part_env != nullptr && strcmp(part_env, "fixed") == 0;
-    const bool want_even = part_env != nullptr && strcmp(part_env, "even") == 0;
+    const bool want_fixed = t.partition == 1;
+    const bool want_even = t.partition == 2;
     plan->tile_tokens = tt;
     plan->waves = kWaves;
-    plan->pv_mode = env_pv_mode();
+    plan->pv_mode = t.pv_mode;
     plan->double_buffer = dbuf;
     // Non-temporal K/V loads: every KV byte is read once per call, and in a
     // decode step the caches of all layers together far exceed the 256 MB
     // Infinity Cache, so they stream from HBM (measured faster at every
     // workload size when the inputs are not cache-resident).
-    // GQA_DECODE_NT=0 selects the default policy for A/B runs.
-    const char *nt_env = getenv("GQA_DECODE_NT");
-    plan->streaming = (nt_env != nullptr && strcmp(nt_env, "0") == 0) ? 0 : 1;
+    plan->streaming = t.streaming;
 
     // Even shares (the default for batches): about two workgroups per CU, each at least
     // one tile per wave at full length; a segment short enough for one
@@ -1910,7 +2207,7 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
     // split without the device-side length scan.
     if (num_splits == 0 && !want_fixed && tiles_total > 4 * kWaves && (B > 1 || want_even)) {
         const int64_t tiles_max = (int64_t)base * tiles_total;
-        int64_t P = env_int("GQA_DECODE_SHARES", B > 1 ? 2 * cu_count : cu_count);
+        int64_t P = t.shares > 0 ? t.shares : (B > 1 ? 2 * cu_count : cu_count);
         if (P > (tiles_max + kWaves - 1) / kWaves) P = (tiles_max + kWaves - 1) / kWaves;
         if (P < 1) P = 1;
         if (P > INT32_MAX / 2) return GQA_ERR_SHAPE;
@@ -1921,16 +2218,24 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
         plan->direct = 0;
         plan->slots = (int64_t)P + base;
         plan->max_pieces = (int)std::min<int64_t>(P, (int64_t)tiles_total * P / tiles_max + 1);
+        // In-kernel fold: one counter per (sequence, kv head); every segment's
+        // few pieces are folded by the share that finishes last among them.
+        // Not for segments of many pieces (one workgroup would read them all).
+        const bool fuse = t.fold == 2 || (t.fold == 0 && kFuseEvenByDefault && plan->max_pieces <= kNarrowPieces);
+        if (fuse && base <= kMaxCounters) {
+            plan->fused = 1;
+            plan->counters = base;
+        }
         plan->workspace_bytes = workspace_layout(Hq, Hkv, D, plan->slots).total;
         return GQA_OK;
     }
 
     // Fixed splits: enough workgroups to give every CU one of them (measured
     // best for one long sequence: fewer partials to fold, no loss in the
-    // stream), and no split longer than kMaxSplitTokens keys, but at least
-    // one tile per wave; a short segment (<= 4 tiles per wave) gets a single
-    // split.
-    const int kMaxSplitTokens = env_int("GQA_DECODE_SPLIT_KEYS", 2048);
+    // stream), and no split longer than the tuning's split_keys (2048 keys),
+    // but at least one tile per wave; a short segment (<= 4 tiles per wave)
+    // gets a single split.
+    const int kMaxSplitTokens = t.split_keys > 0 ? t.split_keys : kDefaultSplitKeys;
     int S = num_splits;
     if (S == 0) {
         const int fill = (cu_count + base - 1) / base;
@@ -1955,7 +2260,20 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
     plan->slots = (int64_t)base * S;
     plan->max_pieces = S;
     plan->workspace_bytes = 0;
-    if (!plan->direct) plan->workspace_bytes = workspace_layout(Hq, Hkv, D, plan->slots).total;
+    if (!plan->direct) {
+        // In-kernel fold: a tree over each segment's splits (fan-in F), one
+        // counter per node; the inner nodes' partials follow the splits'.
+        const bool fuse = t.fold == 2 || (t.fold == 0 && kFuseFixedByDefault);
+        const int F = fold_fanin(S);
+        const int64_t nodes = fold_tree_nodes(S, F);
+        if (fuse && (int64_t)base * nodes <= kMaxCounters) {
+            plan->fused = 1;
+            plan->fold_fanin = F;
+            plan->counters = (int64_t)base * nodes;
+            plan->slots += (int64_t)base * (nodes - 1);
+        }
+        plan->workspace_bytes = workspace_layout(Hq, Hkv, D, plan->slots).total;
+    }
     return GQA_OK;
 }
 
@@ -1968,7 +2286,8 @@ extern "C" {
 size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int max_seq_len, int page_size,
                                   int num_splits) {
     gqa_plan_t plan;
-    if (plan_for_call(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, &plan) != GQA_OK) return SIZE_MAX;
+    if (plan_for_call(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, current_tuning(), &plan) != GQA_OK)
+        return SIZE_MAX;
     return plan.workspace_bytes;
 }
 
@@ -1999,8 +2318,9 @@ gqa_status_t decode_contig(const void *q, const void *k_cache, const void *v_cac
     const int eb = kv.type == kKvFp8 ? 1 : 2;
     if (((int64_t)S_max + 64) * D * eb > INT32_MAX) return GQA_ERR_SHAPE;  // 32-bit buffer offsets
     if (workspace != nullptr && misaligned(workspace, 16)) return GQA_ERR_ALIGN;
+    const gqa_tuning_t t = current_tuning();
     gqa_plan_t plan;
-    s = plan_for_call(B, M * Hq, Hkv, D, S_max, 0, num_splits, &plan, kv.type == kKvFp8 ? 1 : 2);
+    s = plan_for_call(B, M * Hq, Hkv, D, S_max, 0, num_splits, t, &plan, kv.type == kKvFp8 ? 1 : 2);
     if (s != GQA_OK) return s;
     if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
         return workspace == nullptr ? GQA_ERR_NULL : GQA_ERR_WORKSPACE;
@@ -2017,7 +2337,7 @@ gqa_status_t decode_contig(const void *q, const void *k_cache, const void *v_cac
     a.split_tokens = plan.split_tokens;
     a.qk_scale_log2 = scale * kv.k_scale * 1.4426950408889634f;
     a.v_scale = kv.v_scale;
-    return run(plan, a, D, false, kv.type, workspace, stream, phases);
+    return run(plan, t, a, D, false, kv.type, workspace, stream, phases);
 }
 
 gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
@@ -2038,8 +2358,10 @@ gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
     if ((int64_t)max_pages * page_size > INT32_MAX || (int64_t)page_size * D * 2 > INT32_MAX)  // 32-bit offsets
         return GQA_ERR_SHAPE;
     if (workspace != nullptr && misaligned(workspace, 16)) return GQA_ERR_ALIGN;
+    const gqa_tuning_t t = current_tuning();
     gqa_plan_t plan;
-    s = plan_for_call(B, M * Hq, Hkv, D, max_pages * page_size, page_size, num_splits, &plan, kv.type == kKvFp8 ? 1 : 2);
+    s = plan_for_call(B, M * Hq, Hkv, D, max_pages * page_size, page_size, num_splits, t, &plan,
+                      kv.type == kKvFp8 ? 1 : 2);
     if (s != GQA_OK) return s;
     if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
         return workspace == nullptr ? GQA_ERR_NULL : GQA_ERR_WORKSPACE;
@@ -2060,7 +2382,7 @@ gqa_status_t decode_paged(const void *q, const void *k_pool, const void *v_pool,
     a.split_tokens = plan.split_tokens;
     a.qk_scale_log2 = scale * kv.k_scale * 1.4426950408889634f;
     a.v_scale = kv.v_scale;
-    return run(plan, a, D, true, kv.type, workspace, stream, phases);
+    return run(plan, t, a, D, true, kv.type, workspace, stream, phases);
 }
 
 }  // namespace
@@ -2179,8 +2501,9 @@ gqa_status_t combine_impl(const void *workspace, size_t workspace_bytes, const i
     if (misaligned(out, 16) || misaligned(seq_lens, 4) ||
         (workspace != nullptr && misaligned(workspace, 16)))
         return GQA_ERR_ALIGN;
+    const gqa_tuning_t t = current_tuning();
     gqa_plan_t plan;
-    gqa_status_t s = plan_for_call(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, &plan, elem_bytes);
+    gqa_status_t s = plan_for_call(B, Hq, Hkv, D, max_seq_len, page_size, num_splits, t, &plan, elem_bytes);
     if (s != GQA_OK) return s;
     if (plan.direct) return GQA_OK;  // the split kernel already wrote `out`
     if (workspace == nullptr) return GQA_ERR_NULL;
@@ -2196,8 +2519,8 @@ gqa_status_t combine_impl(const void *workspace, size_t workspace_bytes, const i
         a.S_max = max_seq_len;
     }
     // the cache type only matters for the share rule the split call used
-    return run(plan, a, D, page_size > 0, elem_bytes == 1 ? kKvFp8 : kKvBf16, const_cast<void *>(workspace), stream,
-               kPhaseCombine);
+    return run(plan, t, a, D, page_size > 0, elem_bytes == 1 ? kKvFp8 : kKvBf16, const_cast<void *>(workspace),
+               stream, kPhaseCombine);
 }
 
 }  // namespace

@@ -76,7 +76,57 @@ typedef struct gqa_plan {
     int double_buffer;      /* 1: two tile buffers per wave; 0: one, refilled part by part */
     int streaming;          /* 1: K/V loads carry the non-temporal hint (large caches) */
     size_t workspace_bytes; /* scratch the call needs (0 when direct) */
+    int fused;              /* 1: the split kernel folds its own partials (one launch, see gqa_tuning_t.fold);
+                               0: a combine kernel folds them (two launches) */
+    int fold_fanin;         /* fused fixed splits: partials per node of the fold tree; otherwise 0 */
+    int64_t counters;       /* arrival counters a fused call uses in the workspace header (0 otherwise) */
 } gqa_plan_t;
+
+/*
+ * Tuning: the plan and kernel-variant choices every call makes, process-wide.
+ * The defaults (gqa_decode_get_tuning right after loading, when no GQA_DECODE_*
+ * variable is set) are the measured best on MI355X.  The environment
+ * variables named below override single fields for same-binary A/B runs; they
+ * are read ONCE, when the library is loaded, never per call.
+ * gqa_decode_set_tuning replaces the whole set at run time (thread-safe).
+ * Every call copies the tuning once at entry, so the launches of one call and
+ * the plan they follow always agree.  A *_partials call and the
+ * gqa_decode_combine that folds its partials must run under the same tuning.
+ */
+typedef struct gqa_tuning {
+    int tile_tokens;   /* GQA_DECODE_TILE: keys per wave tile, 0 = by head_dim and cache type; 16, 32 or 64
+                          (ignored where a tile would exceed 16 KB of K+V per wave) */
+    int double_buffer; /* GQA_DECODE_DBUF=1: two register tiles per wave (A/B variant); 0 (default): one */
+    int pv_mode;       /* GQA_DECODE_PV=f32 -> 0: fp32-MFMA PV (A/B variant); 1 (default): bf16 MFMA, P hi+lo */
+    int streaming;     /* GQA_DECODE_NT=0 -> 0: default cache policy; 1 (default): non-temporal K/V loads */
+    int partition;     /* GQA_DECODE_PARTITION=fixed|even -> 1|2; 0 (default): by shape */
+    int shares;        /* GQA_DECODE_SHARES: even-share workgroups; 0 (default): two per CU for batches
+                          (one per CU for long contiguous segments), one per CU for one sequence */
+    int split_keys;    /* GQA_DECODE_SPLIT_KEYS: most keys per fixed split; 0 (default): 2048 */
+    int piece_cost;    /* GQA_DECODE_PIECE_COST: tiles a piece's start and fold are worth in the even
+                          partition, 0..1024; default 4 */
+    int halve_long;    /* GQA_DECODE_HALVE_LONG=0 -> 0: keep two shares per CU for long contiguous bf16
+                          segments; 1 (default): one per CU */
+    int combine;       /* GQA_DECODE_COMBINE=tree -> 1: always the tree combine; 0 (default): by plan */
+    int combine_cols;  /* GQA_DECODE_COMBINE_COLS: tree-combine columns per workgroup, 2, 4, 8 or 16;
+                          0 (default): by grid size */
+    int num_splits;    /* GQA_DECODE_SPLITS: splits used when a call passes num_splits = 0;
+                          0 (default): the heuristic */
+    int fold;          /* GQA_DECODE_FOLD=kernel|fused -> 1|2: fold the partials in a combine kernel (two
+                          launches), or in the split kernel itself (one launch: the workgroup that writes
+                          the last partial of a group, as counted by an arrival ticket in the workspace
+                          header, folds the group -- every piece of a segment in the even partition, a
+                          node of a fold tree over fixed splits -- in a fixed order, so results stay
+                          bit-exact from run to run); 0 (default): the combine kernel, measured faster on
+                          MI355X at every workload shape tried */
+} gqa_tuning_t;
+
+/* The tuning calls use from now on (a copy). */
+void gqa_decode_get_tuning(gqa_tuning_t *tuning);
+
+/* Replace the tuning; GQA_ERR_NULL for NULL, GQA_ERR_SHAPE (nothing changed)
+ * when a field is outside the range documented above. */
+gqa_status_t gqa_decode_set_tuning(const gqa_tuning_t *tuning);
 
 /*
  * The split plan for a call (the split-count rule of the AstrAI csrc commit
@@ -113,10 +163,14 @@ size_t gqa_decode_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int max_
  *   known) but never contribute to the result, whatever they hold (NaN too).
  *   workspace: at least gqa_decode_workspace_bytes(B, Hq, Hkv, head_dim,
  *              S_max, 0, num_splits) bytes; may be NULL when that is 0.
- *              It needs no initialisation: it carries one call's partials
- *              from the split kernel to the combine kernel, so calls that
- *              share a workspace must not run concurrently (one stream
- *              orders them).
+ *              Its first 16384 bytes hold the arrival counters of the
+ *              in-kernel fold (gqa_tuning_t.fold): they must be ZERO before
+ *              the workspace is first used (zero the whole buffer once after
+ *              allocating it, e.g. hipMemset, outside any graph capture), and
+ *              every call leaves them zero again.  The rest needs no
+ *              initialisation: it carries one call's partials from the split
+ *              workgroups to the fold.  Calls that share a workspace must not
+ *              run concurrently (one stream orders them).
  *   num_splits: 0 = heuristic, > 0 = forced.
  */
 gqa_status_t gqa_decode(const void *q, const void *k_cache, const void *v_cache,

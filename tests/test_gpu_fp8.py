@@ -105,7 +105,7 @@ def test_fp8_paged(ps, D):
         compare(dc.run_host(splits), ref, f"fp8 paged ps={ps} D={D} splits={splits}")
 
 
-def test_fp8_paged_equals_contiguous_bitwise(monkeypatch):
+def test_fp8_paged_equals_contiguous_bitwise(tune):
     """The same bytes through the paged and the contiguous layout give identical bits under the
     same plan.  By default a paged E4M3 cache at head_dim 128 takes 32-key tiles where the
     contiguous one takes 16, so the tile is pinned to 16 for the bitwise comparison; the
@@ -126,7 +126,7 @@ def test_fp8_paged_equals_contiguous_bitwise(monkeypatch):
     for splits in (0, 5):
         compare(DeviceCase(p).run_host(splits), ref, f"fp8 paged, default plan, splits={splits}")
         compare(DeviceCase(c).run_host(splits), ref, f"fp8 contiguous, default plan, splits={splits}")
-    monkeypatch.setenv("GQA_DECODE_TILE", "16")
+    tune(tile_tokens=16)
     for splits in (0, 5):
         a = DeviceCase(p).run_host(splits)
         b = DeviceCase(c).run_host(splits)
@@ -150,14 +150,15 @@ def test_fp8_matches_bf16_path_on_dequantised_cache():
     compare(got, oracle_out(c), "fp8 vs oracle")
 
 
-def test_fp8_even_shares(monkeypatch):
+def test_fp8_even_shares(tune):
     """Ragged E4M3 batches under several share counts (the even partition)."""
     case = W.fp8_contig_case(6, 16, 2, 128, 3000, seq_lens=[3000, 1, 0, 1500, 77, 2999], seed=95)
     dc = DeviceCase(case)
     ref = oracle_out(case)
     for shares in ("1", "7", "64", "1000"):
-        monkeypatch.setenv("GQA_DECODE_SHARES", shares)
-        compare(dc.run_host(), ref, f"fp8 even shares={shares}")
+        for fold in (1, 2):
+            tune(shares=int(shares), fold=fold)
+            compare(dc.run_host(), ref, f"fp8 even shares={shares} fold={fold}")
 
 
 @pytest.mark.parametrize("paged,long_segments", [(False, False), (True, False), (False, True)])
@@ -175,7 +176,7 @@ def test_fp8_partials_then_combine_equals_one_call(paged, long_segments):
     cap, ps = case.capacity, case.page_size
     for splits in (0, 5):
         need = gd.gqa_decode_workspace_bytes(case.B, case.Hq, case.Hkv, case.D, cap, ps, splits)
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        ws = gd.new_workspace(max(need, gd.COUNTER_BYTES))
         out = torch.empty((case.B, case.Hq, case.D), dtype=torch.float32, device="cuda")
         if paged:
             gd.gqa_paged_decode_fp8_partials(dc.q, dc.k, dc.v, dc.seq_lens, dc.page_table, case.scale,

@@ -96,13 +96,14 @@ def test_mq_paged(ps):
         compare(dc.run_host(splits), ref, f"mq paged ps={ps} splits={splits}")
 
 
-def test_mq_even_shares(monkeypatch):
+def test_mq_even_shares(tune):
     case = W.mq_case(5, 4, 16, 4, 128, 2000, seq_lens=[2000, 4, 0, 999, 1500], seed=105)
     dc = DeviceCase(case)
     ref = oracle_out(case)
     for shares in ("1", "7", "64", "1000"):
-        monkeypatch.setenv("GQA_DECODE_SHARES", shares)
-        compare(dc.run_host(), ref, f"mq even shares={shares}")
+        for fold in (1, 2):
+            tune(shares=int(shares), fold=fold)
+            compare(dc.run_host(), ref, f"mq even shares={shares} fold={fold}")
 
 
 def test_mq_rejects_too_many_rows():

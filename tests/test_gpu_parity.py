@@ -230,14 +230,18 @@ def test_paged_page_permutation_bitwise():
 
 
 # ------------------------------------------------------------------ workspace reuse and call variants
-def test_shared_workspace_across_plans():
-    """One workspace, never initialised (all bytes 0xFF: NaN floats), serves calls with
-    different shapes and plans (even shares, fixed splits) back to back."""
-    say("[parity] shared workspace")
+@pytest.mark.parametrize("fold", [0, 2], ids=["default", "fused"])
+def test_shared_workspace_across_plans(tune, fold):
+    """One workspace whose partial region was never initialised (all bytes 0xFF: NaN floats;
+    only the arrival counters are zero) serves calls with different shapes and plans (even
+    shares, fixed splits, folded in a combine kernel or in the split kernel) back to back."""
+    say(f"[parity] shared workspace fold={fold}")
+    tune(fold=fold)
     a = W.contig_case(1, 8, 1, 128, 20000, seed=30)          # one long sequence, fixed splits
     b = W.contig_case(3, 16, 4, 64, 700, seq_lens=[700, 5, 300], seed=31)
     c = W.paged_case(4, 32, 8, 128, 32, 300, seq_lens=[1000, 0, 555, 1024], max_len=1024, seed=32)
     ws = torch.full((1 << 24,), 255, dtype=torch.uint8, device="cuda")
+    ws[:gd.COUNTER_BYTES] = 0  # only the arrival counters must start at zero
     da, db, dc = DeviceCase(a), DeviceCase(b), DeviceCase(c)
     ra, rb, rc = oracle_out(a), oracle_out(b), oracle_out(c)
     for _ in range(3):
@@ -253,15 +257,15 @@ def test_shared_workspace_across_plans():
 
 
 @pytest.mark.parametrize("mode", ["default", "tree"])
-def test_combine_thread_per_column(monkeypatch, mode):
+def test_combine_thread_per_column(tune, mode):
     """Plans with few pieces per segment at full length use one thread per output column
-    (default); GQA_DECODE_COMBINE=tree forces the tree.  Both match the oracle and are
+    (default); the tuning's combine = 1 forces the tree.  Both match the oracle and are
     bit-exact across runs: even shares whose short sequences make the long ones span more
     than 16 shares (several rounds of loads per thread), paged shares, a few fixed splits,
     and multi-query rows."""
     say(f"[parity] combine {mode}")
     if mode == "tree":
-        monkeypatch.setenv("GQA_DECODE_COMBINE", "tree")
+        tune(combine=1)
     lens = [4096, 3, 0, 17, 1, 2000] + [1] * 10
     cases = [
         (W.contig_case(16, 16, 4, 128, 4096, seq_lens=lens, seed=62), 0),
@@ -277,12 +281,12 @@ def test_combine_thread_per_column(monkeypatch, mode):
 
 
 @pytest.mark.parametrize("cols", ["2", "4", "8", "16"])
-def test_combine_column_widths(monkeypatch, cols):
+def test_combine_column_widths(tune, cols):
     """Every combine width (lanes of a column merged by row rotations, row-pair and
     half-wave swaps, then the waves) matches the oracle and is bit-exact across runs,
     for fixed splits (several rounds of loads per thread) and ragged even shares."""
     say(f"[parity] combine columns={cols}")
-    monkeypatch.setenv("GQA_DECODE_COMBINE_COLS", cols)
+    tune(combine_cols=int(cols), fold=1)  # the tree combine runs in its own kernel
     fixed = W.contig_case(2, 24, 4, 256, 3000, seq_lens=[3000, 1111], seed=60, scale=1 / 16)
     even = W.paged_case(5, 16, 4, 128, 32, 400, seq_lens=[2048, 1, 0, 777, 1500], max_len=2048, seed=61)
     for case, splits in ((fixed, 0), (fixed, 150), (even, 0)):
@@ -294,11 +298,11 @@ def test_combine_column_widths(monkeypatch, cols):
 
 @pytest.mark.parametrize("pv", ["f32", "bf16"])
 @pytest.mark.parametrize("D", [64, 128, 256])
-def test_pv_modes(monkeypatch, pv, D):
+def test_pv_modes(tune, pv, D):
     """Both PV contractions (fp32 MFMA; bf16 MFMA with P split hi+lo) match the oracle,
     with a NaN-poisoned tail and ragged lengths."""
     say(f"[parity] pv={pv} D={D}")
-    monkeypatch.setenv("GQA_DECODE_PV", pv)
+    tune(pv_mode=0 if pv == "f32" else 1)
     assert gd.gqa_decode_plan(2, 16, 2, D, 300).pv_mode == (0 if pv == "f32" else 1)
     case = W.contig_case(3, 16, 2, D, 300, seq_lens=[300, 17, 129], seed=40 + D, tail="nan")
     dc = DeviceCase(case)
@@ -355,16 +359,18 @@ EVEN_LENS = {
 
 @pytest.mark.parametrize("lens", list(EVEN_LENS))
 @pytest.mark.parametrize("shares", ["1", "3", "7", "64", "1000"])
-def test_even_shares_contiguous(monkeypatch, lens, shares):
-    """Equal shares of the concatenated tiles, any share count, ragged and empty sequences."""
-    say(f"[parity] even shares={shares} lens={lens}")
-    monkeypatch.setenv("GQA_DECODE_SHARES", shares)
+@pytest.mark.parametrize("fold", [1, 2], ids=["kernel", "fused"])
+def test_even_shares_contiguous(tune, lens, shares, fold):
+    """Equal shares of the concatenated tiles, any share count, ragged and empty sequences
+    (a capacity of at least 1024 keys keeps every case on even shares, short ones included),
+    folded by the combine kernel and in the split kernel."""
+    say(f"[parity] even shares={shares} lens={lens} fold={fold}")
+    tune(shares=int(shares), fold=fold)
     L = EVEN_LENS[lens]
-    S_max = max(max(L), 1)
+    S_max = max(max(L), 1024)
     case = W.contig_case(len(L), 16, 4, 128, S_max, seq_lens=L, seed=60, tail="nan")
     p = gd.gqa_decode_plan(case.B, 16, 4, 128, S_max)
-    if p.partition != 1:
-        pytest.skip("short cache: direct plan")
+    assert p.partition == 1 and p.fused == (fold == 2)
     dc = DeviceCase(case)
     out = [dc.run_host() for _ in range(2)]
     compare(out[0], oracle_out(case), f"even shares={shares} {lens}")
@@ -376,37 +382,37 @@ def test_even_shares_contiguous(monkeypatch, lens, shares):
 
 @pytest.mark.parametrize("shares", ["5", "0"])
 @pytest.mark.parametrize("D", [32, 64, 128, 256])
-def test_even_shares_paged(monkeypatch, shares, D):
+def test_even_shares_paged(tune, shares, D):
     say(f"[parity] even shares paged D={D} shares={shares}")
     if shares != "0":
-        monkeypatch.setenv("GQA_DECODE_SHARES", shares)
+        tune(shares=int(shares))
     L = [1, 0, 900, 31, 2000, 16, 0, 1500]
     case = W.paged_case(len(L), 8, 2, D, 32, 250, seq_lens=L, max_len=2048, seed=61 + D)
     assert gd.gqa_decode_plan(case.B, 8, 2, D, 2048, 32).partition == 1
     compare(DeviceCase(case).run_host(), oracle_out(case), f"even paged D={D}")
 
 
-def test_fixed_and_even_agree_with_oracle(monkeypatch):
+def test_fixed_and_even_agree_with_oracle(tune):
     say("[parity] fixed vs even")
     case = W.paged_case(8, 32, 8, 128, 32, 2100, max_len=8192, seed=62)
     dc = DeviceCase(case)
     ref = oracle_out(case)
     even = dc.run_host()
-    monkeypatch.setenv("GQA_DECODE_PARTITION", "fixed")
+    tune(partition=1)
     fixed = dc.run_host()
     compare(even, ref, "even")
     compare(fixed, ref, "fixed")
 
 
 @pytest.mark.parametrize("halve", ["default", "0"])
-def test_even_shares_long_segments(monkeypatch, halve):
+def test_even_shares_long_segments(tune, halve):
     """Contiguous batches whose segments average >= 128 tiles take one share per CU (half the
     launched shares; the rest exit); shorter ones keep two.  Both sides of the rule, with the
     rule switched off, and the many-sequence walk (B > 64), against the oracle and bit-exact
     across runs."""
     say(f"[parity] long segments, halve={halve}")
     if halve == "0":
-        monkeypatch.setenv("GQA_DECODE_HALVE_LONG", "0")
+        tune(halve_long=0)
     rng = np.random.default_rng(70)
     cases = [
         W.contig_case(8, 32, 4, 128, 4096, seq_lens=[4096, 4000, 2048, 3000, 4096, 1, 0, 4095], seed=71),
@@ -422,13 +428,13 @@ def test_even_shares_long_segments(monkeypatch, halve):
 
 
 @pytest.mark.parametrize("nt", ["0", "1"])
-def test_cache_policy_variants(monkeypatch, nt):
+def test_cache_policy_variants(tune, nt):
     """Both K/V load cache policies give the same bits (only the hint differs)."""
-    say(f"[parity] GQA_DECODE_NT={nt}")
+    say(f"[parity] streaming={nt}")
     case = W.contig_case(2, 16, 2, 128, 3000, seq_lens=[3000, 1234], seed=70, tail="nan")
     dc = DeviceCase(case)
     base = dc.run_host()
-    monkeypatch.setenv("GQA_DECODE_NT", nt)
+    tune(streaming=int(nt))
     assert gd.gqa_decode_plan(2, 16, 2, 128, 3000).streaming == int(nt)  # default: 1
     out = dc.run_host()
     assert np.array_equal(out.view(np.uint32), base.view(np.uint32))

@@ -2,9 +2,10 @@
 
 Each case draws the cache kind (contiguous / paged, bf16 / E4M3, one or several query tokens),
 head_dim, group size, kv heads, batch, ragged lengths (zeros included), page size, the split
-count and, for some cases, the even-share count, so that the plan's branches (fixed or even
-partition, one-tile or key-range workgroups, direct or combined, packed or plain PV columns) are
-crossed with each other rather than one at a time.  Tolerance as everywhere:
+count, for some cases the even-share count, and where the partials are folded (by the plan's
+default, in a combine kernel, or in the split kernel itself), so that the plan's branches (fixed or
+even partition, one-tile or key-range workgroups, direct or combined, packed or plain PV columns,
+one launch or two) are crossed with each other rather than one at a time.  Tolerance as everywhere:
 |gpu - oracle| <= 2e-3 + 2e-3 |oracle|, and a second call gives the same bits.
 """
 from __future__ import annotations
@@ -51,8 +52,9 @@ def draw(i: int) -> dict:
     splits = int(rng.choice([0, 0, 1, int(rng.integers(2, 60))]))
     shares = str(int(rng.choice([0, 1, 5, 64, 300]))) if rng.random() < 0.4 else None
     page_size = int(rng.choice([16, 32, 64, 128, 48]))
+    fold = (i // 6) % 3  # 0: the plan's default, 1: combine kernel, 2: in the split kernel
     return dict(kind=kind, D=D, M=M, G=G, Hkv=Hkv, B=B, S_max=S_max, lens=[int(x) for x in lens],
-                splits=splits, shares=shares, page_size=page_size, seed=9000 + i)
+                splits=splits, shares=shares, page_size=page_size, fold=fold, seed=9000 + i)
 
 
 def build(c: dict) -> W.Case:
@@ -77,11 +79,10 @@ def build(c: dict) -> W.Case:
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
-def test_random_case(monkeypatch, i):
+def test_random_case(tune, i):
     c = draw(i)
     say(f"[random] {i}: {c}")
-    if c["shares"] is not None:
-        monkeypatch.setenv("GQA_DECODE_SHARES", c["shares"])
+    tune(shares=int(c["shares"] or 0), fold=c["fold"])
     case = build(c)
     dc = DeviceCase(case)
     got = dc.run_host(c["splits"])

@@ -25,12 +25,22 @@ def lib():
 
 
 def expected_workspace(B, Hq, Hkv, D, p):
-    """Partial blocks (slots) of G x (D + 2) floats, each region rounded up to 256 bytes."""
+    """The arrival counters' header, then partial blocks (slots) of G x (D + 2) floats, each
+    region rounded up to 256 bytes."""
     if p.direct:
         return 0
     align = lambda x: (x + 255) // 256 * 256
     G = Hq // Hkv
-    return align(p.slots * G * D * 4) + align(p.slots * G * 2 * 4)
+    return gd.COUNTER_BYTES + align(p.slots * G * D * 4) + align(p.slots * G * 2 * 4)
+
+
+def tree_nodes(S, F):
+    """Nodes above the leaves of a fold tree over S partials with fan-in F (written out)."""
+    nodes, n = 0, S
+    while n > 1:
+        n = -(-n // F)
+        nodes += n
+    return nodes
 
 
 def declared_functions():
@@ -70,6 +80,12 @@ def test_plan_invariants(shape, cu):
         assert p.slots == p.grid + B * Hkv
         assert p.split_tokens % p.tile_tokens == 0
         assert p.split_tokens * p.grid >= B * Hkv * cap
+        # by default a combine kernel folds the pieces; with the tuning's fold = 2 the split
+        # kernel does, one counter per segment
+        assert p.fused == 0 and p.counters == 0 and p.fold_fanin == 0
+        with gd.tuning(fold=2):
+            f = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, 0, cu)
+            assert f.fused == 1 and f.counters == B * Hkv and f.slots == p.slots
     else:                                      # fixed splits
         assert p.split_tokens % p.tile_tokens == 0
         assert p.num_splits * p.split_tokens >= cap
@@ -77,7 +93,8 @@ def test_plan_invariants(shape, cu):
         assert p.grid == B * Hkv * p.num_splits
         assert p.direct == (p.num_splits == 1)
         assert p.slots == B * Hkv * p.num_splits
-    assert p.pv_mode == 1  # bf16 MFMA PV unless GQA_DECODE_PV=f32
+        assert p.fused == 0 and p.counters == 0   # fixed splits fold in a combine kernel by default
+    assert p.pv_mode == 1  # bf16 MFMA PV unless the tuning selects fp32
     assert p.double_buffer == 0
     assert p.streaming == 1
     assert p.workspace_bytes == expected_workspace(B, Hq, Hkv, D, p)
@@ -86,8 +103,8 @@ def test_plan_invariants(shape, cu):
 
 
 @pytest.mark.parametrize("shape", WORKLOAD_SHAPES)
-def test_fixed_plan_invariants(monkeypatch, shape):
-    monkeypatch.setenv("GQA_DECODE_PARTITION", "fixed")
+def test_fixed_plan_invariants(tune, shape):
+    tune(partition=1)
     B, Hq, Hkv, D, cap, ps = shape
     p = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, 0, 256)
     assert p.partition == 0
@@ -294,3 +311,98 @@ def test_fp8_plan_tiles_and_workspace_bound(shape, splits):
     assert p8.workspace_bytes <= p16.workspace_bytes
     if ps > 0:
         assert ps % p8.tile_tokens == 0
+
+
+# ---- tuning: read from the environment once, at load; replaced only by gqa_decode_set_tuning
+def test_default_tuning():
+    t = gd.gqa_decode_get_tuning().as_dict()
+    assert t == dict(tile_tokens=0, double_buffer=0, pv_mode=1, streaming=1, partition=0, shares=0,
+                     split_keys=0, piece_cost=4, halve_long=1, combine=0, combine_cols=0,
+                     num_splits=0, fold=0)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("tile_tokens", 24), ("tile_tokens", 128), ("double_buffer", 2), ("pv_mode", -1),
+    ("partition", 3), ("shares", -1), ("piece_cost", 1025), ("combine_cols", 3), ("fold", 3),
+    ("num_splits", -2)])
+def test_set_tuning_rejects_out_of_range(field, value):
+    before = gd.gqa_decode_get_tuning().as_dict()
+    t = gd.gqa_decode_get_tuning()
+    setattr(t, field, value)
+    with pytest.raises(gd.GqaError) as e:
+        gd.gqa_decode_set_tuning(t)
+    assert e.value.code == 2
+    assert gd.gqa_decode_get_tuning().as_dict() == before   # nothing changed
+    assert gd.load().gqa_decode_set_tuning(None) == 1
+
+
+def test_tuning_changes_plans_and_is_restored(tune):
+    base = gd.gqa_decode_plan(1, 24, 4, 256, 4096).as_dict()
+    tune(num_splits=16, fold=2)
+    p = gd.gqa_decode_plan(1, 24, 4, 256, 4096)
+    assert p.num_splits == 16 and p.fused == 1 and p.fold_fanin == 16
+    assert gd.gqa_decode_workspace_bytes(1, 24, 4, 256, 4096, 0, 16) == p.workspace_bytes
+    with gd.tuning(num_splits=0, fold=1):
+        assert gd.gqa_decode_plan(1, 24, 4, 256, 4096).as_dict() == base
+    assert gd.gqa_decode_plan(1, 24, 4, 256, 4096).num_splits == 16
+
+
+def test_environment_after_load_changes_nothing(monkeypatch):
+    """The GQA_DECODE_* variables are read when the library is loaded, never per call: setting
+    them between a *_partials call and its gqa_decode_combine (or between any two calls) cannot
+    change the plan, so the combine always reads the partials where the split kernel wrote them."""
+    shapes = [(1, 24, 4, 256, 4096, 0), (32, 32, 8, 128, 8192, 32), (3, 16, 4, 128, 1500, 0)]
+    before = [gd.gqa_decode_plan(*sh, 0, 256).as_dict() for sh in shapes]
+    ws_before = [gd.gqa_decode_workspace_bytes(*sh, 3) for sh in shapes]  # forced: no device query
+    for name, value in [("GQA_DECODE_SPLITS", "7"), ("GQA_DECODE_PARTITION", "fixed"),
+                        ("GQA_DECODE_SHARES", "3"), ("GQA_DECODE_TILE", "32"),
+                        ("GQA_DECODE_FOLD", "fused"), ("GQA_DECODE_PIECE_COST", "0")]:
+        monkeypatch.setenv(name, value)
+    assert [gd.gqa_decode_plan(*sh, 0, 256).as_dict() for sh in shapes] == before
+    assert [gd.gqa_decode_workspace_bytes(*sh, 3) for sh in shapes] == ws_before
+
+
+def test_environment_is_read_at_load():
+    """A fresh process that loads the library with the variables set starts from them."""
+    import subprocess
+    import sys
+    code = ("import decode_attention_04_amd as gd; t = gd.gqa_decode_get_tuning().as_dict(); "
+            "print(t['num_splits'], t['partition'], t['fold'], t['shares'], t['pv_mode'], t['tile_tokens'])")
+    env = dict(os.environ, GQA_DECODE_SPLITS="7", GQA_DECODE_PARTITION="even", GQA_DECODE_FOLD="fused",
+               GQA_DECODE_SHARES="12", GQA_DECODE_PV="f32", GQA_DECODE_TILE="17")  # 17: invalid, ignored
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                         text=True, check=True).stdout.split()
+    assert out == ["7", "2", "2", "12", "0", "0"]
+
+
+# ---- the in-kernel fold's plan
+@pytest.mark.parametrize("S", [2, 5, 16, 17, 64, 100, 256, 1000])
+def test_fused_fixed_tree_plan(tune, S):
+    """Fixed splits folded in the split kernel: a tree of fan-in F (all S in one node up to 16,
+    else the smallest power of two with F * F >= S, at most 16), one counter per node, the inner
+    nodes' partials after the splits'; the workspace grows by exactly those."""
+    tune(fold=2)
+    B, Hq, Hkv, D, cap = 2, 16, 2, 128, 64 * 1024
+    p = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, 0, S, 256)
+    assert p.partition == 0 and p.fused == 1
+    S = p.num_splits   # whole tiles per split: 1000 requested splits become 820
+    F = S if S <= 16 else min(16, next(f for f in (2, 4, 8, 16, 32) if f * f >= S))
+    assert p.fold_fanin == F
+    nodes = tree_nodes(S, F)
+    assert p.counters == B * Hkv * nodes and p.counters * 4 <= gd.COUNTER_BYTES
+    assert p.slots == B * Hkv * S + B * Hkv * (nodes - 1)
+    assert p.workspace_bytes == expected_workspace(B, Hq, Hkv, D, p)
+    with gd.tuning(fold=1):
+        q = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, 0, S, 256)
+        assert q.fused == 0 and q.slots == B * Hkv * S
+
+
+def test_fused_plans_stay_within_the_counter_header(tune):
+    """More (sequence, kv head) segments, or tree nodes, than the header holds: two launches."""
+    tune(fold=2)
+    p = gd.gqa_decode_plan(4096, 8, 2, 128, 4096, 0, 0, 256)   # 8192 segments, even shares
+    assert p.partition == 1 and p.fused == 0 and p.counters == 0
+    p = gd.gqa_decode_plan(300, 8, 2, 128, 4096, 0, 64, 256)   # 600 segments x 9 nodes > 4096
+    assert p.partition == 0 and p.fused == 0
+    p = gd.gqa_decode_plan(100, 8, 2, 128, 4096, 0, 64, 256)   # 200 x 9 = 1800 counters
+    assert p.fused == 1 and p.counters == 1800
