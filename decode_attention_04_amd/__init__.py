@@ -13,6 +13,7 @@ Entry points mirror include/gqa_decode.h:
     gqa_decode_partials / gqa_paged_decode_partials + gqa_decode_combine (the two kernels apart)
     gqa_decode_fp8 / gqa_paged_decode_fp8 (+ _partials, gqa_decode_combine_fp8, gqa_decode_plan_fp8)
     gqa_decode_mq / gqa_paged_decode_mq (M query tokens per sequence)
+    gqa_decode_noalloc (gqa_decode with the library's static scratch instead of a workspace)
     gqa_decode_get_tuning / gqa_decode_set_tuning, and `tuning(**fields)` (a context manager)
     gqa_status_string(code)
 bf16 tensors may be torch.bfloat16 or int16/uint16 views of the bit patterns.
@@ -30,7 +31,7 @@ GQA_OK = 0
 # be zero before a workspace is first used (every call leaves them zero)
 COUNTER_BYTES = 16384
 STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_UNSUPPORTED",
-                4: "GQA_ERR_ALIGN", 5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_HIP"}
+                4: "GQA_ERR_ALIGN", 5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_HIP", 7: "GQA_ERR_TOO_LARGE"}
 
 # every symbol include/gqa_decode.h declares
 EXPORTED = ("gqa_decode_plan", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_paged_decode",
@@ -38,7 +39,7 @@ EXPORTED = ("gqa_decode_plan", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_
             "gqa_decode_fp8", "gqa_paged_decode_fp8", "gqa_decode_fp8_partials",
             "gqa_paged_decode_fp8_partials", "gqa_decode_plan_fp8", "gqa_decode_combine_fp8",
             "gqa_decode_mq", "gqa_paged_decode_mq", "gqa_decode_get_tuning", "gqa_decode_set_tuning",
-            "gqa_status_string")
+            "gqa_decode_noalloc", "gqa_status_string")
 
 
 class GqaError(RuntimeError):
@@ -116,6 +117,8 @@ def load(path: str = LIB_PATH):
     lib.gqa_paged_decode_mq.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, cf, vp,
                                         vp, sz, ci, vp]
     lib.gqa_paged_decode_mq.restype = ci
+    lib.gqa_decode_noalloc.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, vp, ci, vp]
+    lib.gqa_decode_noalloc.restype = ci
     lib.gqa_decode_get_tuning.argtypes = [ctypes.POINTER(Tuning)]
     lib.gqa_decode_get_tuning.restype = None
     lib.gqa_decode_set_tuning.argtypes = [ctypes.POINTER(Tuning)]
@@ -456,3 +459,19 @@ def gqa_decode_combine_fp8(workspace, seq_lens, out, B, Hq, Hkv, head_dim, max_s
     """Fold the partials a gqa_*_fp8_partials call left in `workspace` into `out`."""
     return gqa_decode_combine(workspace, seq_lens, out, B, Hq, Hkv, head_dim, max_seq_len,
                               page_size, num_splits, stream, _entry="gqa_decode_combine_fp8")
+
+
+def gqa_decode_noalloc(q, k_cache, v_cache, seq_lens, scale, out, num_splits=0, stream=None):
+    """gqa_decode without a workspace: the partials live in the library's static per-GPU scratch
+    (4 MiB), so the call allocates nothing; `out` (fp32 [B,Hq,D]) must be given."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    _, Hkv, S_max, _ = k_cache.shape
+    bf = _bf16_types()
+    rc = load().gqa_decode_noalloc(
+        _dev_ptr(q, "q", bf), _dev_ptr(k_cache, "k_cache", bf), _dev_ptr(v_cache, "v_cache", bf),
+        _dev_ptr(seq_lens, "seq_lens", (torch.int32,)), B, Hq, Hkv, D, S_max, float(scale),
+        _dev_ptr(out, "out", (torch.float32,)), int(num_splits), _stream_ptr(stream, q.device))
+    if rc != GQA_OK:
+        raise GqaError(rc, "gqa_decode_noalloc")
+    return out

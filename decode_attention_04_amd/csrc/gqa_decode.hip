@@ -2488,6 +2488,66 @@ gqa_status_t gqa_paged_decode_mq(const void *q, const void *k_pool, const void *
 
 namespace {
 
+// ------------------------------------------------- the allocation-free call
+//
+// gqa_decode_noalloc keeps its partials (and the in-kernel fold's counters) in
+// this file-scope device array instead of a caller's workspace.  In host code
+// the name stands for a host-side shadow, not for device memory: the array's
+// device address on each GPU comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is ever passed on.
+constexpr size_t kScratchBytes = 4u << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The arrival counters must start at zero (every call leaves them zero
+// again): cleared once per device, by a kernel on the first call's stream
+// (capturable; a clear that is replayed is harmless between calls).
+__global__ void clear_counters_kernel(unsigned *counters) {
+    for (int i = threadIdx.x; i < kMaxCounters; i += blockDim.x) counters[i] = 0u;
+}
+
+gqa_status_t scratch_for_device(hipStream_t stream, void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GQA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return GQA_ERR_HIP;
+        hipLaunchKernelGGL(clear_counters_kernel, dim3(1), dim3(256), 0, stream, static_cast<unsigned *>(ptr));
+        if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status_t gqa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *seq_lens, int B, int Hq, int Hkv, int D, int S_max,
+                                float scale, float *out, int num_splits, hipStream_t stream) {
+    // The plan first, so that a call past the array's size is refused before
+    // anything touches the device.
+    gqa_status_t s = check_common(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, scale);
+    if (s != GQA_OK || B == 0) return s;
+    if (S_max < 0 || num_splits < 0) return GQA_ERR_SHAPE;
+    gqa_plan_t plan;
+    if ((s = plan_for_call(B, Hq, Hkv, D, S_max, 0, num_splits, current_tuning(), &plan)) != GQA_OK) return s;
+    if (plan.workspace_bytes > kScratchBytes) return GQA_ERR_TOO_LARGE;
+    void *ws = nullptr;
+    if ((s = scratch_for_device(stream, &ws)) != GQA_OK) return s;
+    return decode_contig(q, k_cache, v_cache, seq_lens, B, 1, Hq, Hkv, D, S_max, scale, kBf16Cache, out, ws,
+                         kScratchBytes, num_splits, stream, kPhaseSplit | kPhaseCombine);
+}
+
+}  // extern "C"
+
+namespace {
+
 gqa_status_t combine_impl(const void *workspace, size_t workspace_bytes, const int32_t *seq_lens, int B, int Hq,
                           int Hkv, int D, int max_seq_len, int page_size, int num_splits, float *out,
                           hipStream_t stream, int elem_bytes) {
@@ -2555,6 +2615,7 @@ const char *gqa_status_string(gqa_status_t status) {
         case GQA_ERR_ALIGN: return "a pointer is not aligned as required";
         case GQA_ERR_WORKSPACE: return "workspace smaller than the plan needs";
         case GQA_ERR_HIP: return "a HIP runtime call or launch failed";
+        case GQA_ERR_TOO_LARGE: return "the call needs more scratch than the library's static buffer holds";
     }
     return "unknown status";
 }

@@ -58,7 +58,8 @@ typedef enum gqa_status {
     GQA_ERR_UNSUPPORTED = 3, /* head_dim not in {32,64,128,256} (E4M3: {64,128,256}), G > 16, page_size % 16 != 0 */
     GQA_ERR_ALIGN = 4,       /* a pointer violates the alignment above */
     GQA_ERR_WORKSPACE = 5,   /* workspace smaller than the plan needs */
-    GQA_ERR_HIP = 6          /* a HIP runtime call or launch failed */
+    GQA_ERR_HIP = 6,         /* a HIP runtime call or launch failed */
+    GQA_ERR_TOO_LARGE = 7    /* gqa_decode_noalloc: the call needs more scratch than its static buffer */
 } gqa_status_t;
 
 /* How a call is laid out on the device (host-side, deterministic). */
@@ -310,6 +311,25 @@ gqa_status_t gqa_paged_decode_mq(const void *q, const void *k_pool, const void *
                                  int Hq, int Hkv, int head_dim, int page_size, int num_pages,
                                  int max_pages, float scale, float *out, void *workspace,
                                  size_t workspace_bytes, int num_splits, hipStream_t stream);
+
+/*
+ * gqa_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the partials live in a static device array of the
+ * library, 4 MiB per GPU (4194304 bytes, held until the process ends), whose
+ * address is looked up on the first call on each device.  The call allocates
+ * nothing; the caller passes inputs and `out` as for gqa_decode (same
+ * arguments without workspace / workspace_bytes, same results bit for bit).
+ * A call whose plan needs more than 4 MiB of scratch
+ * (gqa_decode_workspace_bytes) launches nothing and returns GQA_ERR_TOO_LARGE;
+ * the five reference workloads need at most ~2.4 MB.  Every call on a GPU
+ * shares that GPU's array and its contents: calls that overlap on one GPU
+ * (on different streams, or from different threads without ordering) race.
+ */
+gqa_status_t gqa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *seq_lens, int B, int Hq, int Hkv, int head_dim,
+                                int S_max, float scale, float *out, int num_splits,
+                                hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char *gqa_status_string(gqa_status_t status);

@@ -59,7 +59,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         assert lib.gqa_status_string(code)
     assert b"unknown" in lib.gqa_status_string(99)
 
