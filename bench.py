@@ -4,12 +4,15 @@
 
 A step is one gqa_decode (or gqa_paged_decode) call: the split kernel and the
 combine, over one batch of synthetic seeded inputs already resident in HBM.
-The K timed calls are captured once into a HIP graph and replayed, so the
-host's per-call launch cost (Python + ctypes + hipLaunchKernel) does not
-throttle the GPU; the eager per-call time is reported beside it.
-Consecutive steps cycle through R copies of the inputs (more than 1 GiB in
-total, several times the 256 MB Infinity Cache) so each call reads its K/V
-from HBM, not from cache.  Prints ONE JSON line.
+The K timed calls are captured once into a HIP graph and replayed at least 5
+times; the value is the median replay (min and max beside it), so the host's
+per-call launch cost (Python + ctypes + hipLaunchKernel) does not throttle the
+GPU; the eager per-call time is reported beside it.  Consecutive steps cycle
+through R copies of the inputs (more than 1 GiB in total, several times the
+256 MB Infinity Cache) so each call reads its K/V from HBM, not from cache; the
+same calls on one input set are reported apart as the cache-warm figure.  The
+split and combine kernels are timed alone the same way.  Prints ONE JSON line
+(with --all, one per workload).
 """
 from __future__ import annotations
 
@@ -52,6 +55,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--all", action="store_true",
+                    help="one line per workload (all five), instead of the headline workload only")
+    ap.add_argument("--reps", type=int, default=5,
+                    help="replays of the K-call graph that are timed (at least 5; median reported)")
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's heuristic")
     ap.add_argument("--queries", type=int, default=1,
                     help="query tokens per sequence (multi-query decode, gqa_decode_mq); "
@@ -68,6 +75,11 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) "
                          "of a --copy-calibration run into profiles/traffic.json")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="print a markdown table of the per-dispatch averages of every counter in "
+                         "these rocprofv3 --pmc output directories, per kernel of this library")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the cache-warm figure (one input set), e.g. under a counter run")
     return ap.parse_args()
 
 
@@ -149,16 +161,50 @@ def summarize_pmc(fetch_dir, write_dir, workload):
     print(json.dumps(rec["workloads"][workload]))
 
 
-def main():
-    args = parse()
-    if args.summarize_pmc:
-        from tests import workloads as W
-        summarize_pmc(*args.summarize_pmc, args.workload or W.HEADLINE)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
-              f"(--gpus {args.gpus} requested)", file=sys.stderr)
-        sys.exit(2)
+def combine_read_bytes(case, plan, piece_cost=4):
+    """Bytes the combine kernel reads (the partials of every piece) and writes (the output).
+    Fixed splits: every (sequence, kv head) has num_splits pieces.  Even shares: the pieces of
+    each segment are the shares holding a tile of it (the library's share arithmetic, mirrored
+    here for the byte count only)."""
+    import numpy as np
+    G = case.M * case.Hq // case.Hkv
+    per_piece = G * (case.D + 2) * 4
+    out_bytes = case.B * case.M * case.Hq * case.D * 4
+    if plan.direct:
+        return 0, 0
+    if plan.partition == 0:
+        return case.B * case.Hkv * plan.num_splits * per_piece, out_bytes
+    tt = plan.tile_tokens
+    lens = np.minimum(np.maximum(case.seq_lens.astype(np.int64), 0), case.capacity)
+    tiles = (lens + tt - 1) // tt
+    span = np.where(tiles > 0, tiles + piece_cost, 0)
+    N = int(span.sum()) * case.Hkv
+    P = plan.grid
+    segs = int((tiles > 0).sum()) * case.Hkv
+    long_ok = (not case.paged) and case.kv == "bf16"
+    if long_ok and segs > 0 and N >= (128 + piece_cost) * segs:
+        P = (P + 1) // 2   # one share per CU for long contiguous segments
+    share_of = lambda x: ((x + 1) * P + N - 1) // N - 1
+    begin = lambda w: w * N // P
+    pieces, z = 0, 0
+    for b in range(case.B):
+        for _ in range(case.Hkv):
+            n = int(tiles[b])
+            if n:
+                w0, w1 = share_of(z), share_of(z + n - 1)
+                pieces += sum(1 for w in range(w0, w1 + 1) if begin(w) < begin(w + 1))
+            z += int(span[b])
+    return pieces * per_piece, out_bytes
+
+
+def stats(samples):
+    """median, min, max of per-call times (ms)."""
+    v = sorted(samples)
+    return v[len(v) // 2], v[0], v[-1]
+
+
+def measure(name, args, with_cpu):
+    """One workload: its JSON line (see the module docstring)."""
     import numpy as np
     import torch
 
@@ -166,9 +212,6 @@ def main():
     from tests import workloads as W
     from tests.gpu_util import DeviceCase
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    gd.load()
-    name = args.workload or W.HEADLINE
     case = W.make(name, kv=args.kv)
     if args.queries > 1:
         if args.kv != "bf16":
@@ -194,10 +237,11 @@ def main():
                                          args.splits)
     ws = gd.new_workspace(max(need, gd.COUNTER_BYTES))
     oshape = (case.B, case.Hq, case.D) if case.M == 1 else (case.B, case.M, case.Hq, case.D)
-    outs = [torch.empty(oshape, dtype=torch.float32, device="cuda")
-            for _ in range(R)]
+    outs = [torch.empty(oshape, dtype=torch.float32, device="cuda") for _ in range(R)]
+    rot = [R]   # input sets the calls cycle through (1 for the cache-warm figure)
+
     def full(i, stream):
-        sets[i % R].run(args.splits, out=outs[i % R], workspace=ws, stream=stream)
+        sets[i % rot[0]].run(args.splits, out=outs[i % rot[0]], workspace=ws, stream=stream)
 
     def split_only(i, stream):
         d = sets[i % R]
@@ -227,8 +271,9 @@ def main():
 
     cur = torch.cuda.current_stream()
 
-    def graph_time(fn, k):
-        """ms per call of `fn` over k calls captured in one HIP graph (one untimed replay first)."""
+    def graph_time(fn, k, reps):
+        """ms per call of `fn` for each of `reps` replays of one HIP graph of k calls (after one
+        untimed replay), timed with HIP events on the stream the graph is replayed on."""
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(cur)
@@ -241,12 +286,15 @@ def main():
                 fn(i, gs)
         graph.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(cur)
-        graph.replay()
-        e1.record(cur)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / k
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            graph.replay()
+            e1.record(cur)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) / k)
+        return out
 
     # W untimed warm-up steps, then a short timed eager run (reported beside the value)
     for i in range(args.warmup):
@@ -261,22 +309,32 @@ def main():
     torch.cuda.synchronize()
     eager_us = e0.elapsed_time(e1) * 1e3 / n_eager
 
-    # The timed region: exactly K whole calls, captured once into a HIP graph and replayed,
-    # so the host's per-call launch cost does not throttle the GPU.
-    ms_per_step = graph_time(full, args.steps)
-    us = ms_per_step * 1e3
+    # The timed region: replays of one HIP graph of exactly K whole calls (the host's per-call
+    # launch cost does not throttle the GPU); the value is the median replay.
+    reps = max(5, args.reps)
+    full_ms = graph_time(full, args.steps, reps)
+    ms_per_step, full_min, full_max = stats(full_ms)
     gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
-    # The dominant kernel alone (the split-KV partial kernel; K launches in one graph), and the
-    # combine alone, each on the stream they are launched on.
+    # The split kernel alone (the dominant kernel) and the combine alone, each replayed the same
+    # way, on the stream they are launched on.
     if case.M == 1:
-        split_ms = graph_time(split_only, args.steps)
-        combine_ms = graph_time(combine_only, args.steps) if not plan.direct else 0.0
+        split_ms = stats(graph_time(split_only, args.steps, reps))
+        combine_ms = stats(graph_time(combine_only, args.steps, reps)) if not plan.direct else (0.0,) * 3
     else:   # multi-query calls have no split-only entry point: the roofline uses whole calls
-        split_ms, combine_ms = ms_per_step, 0.0
-    split_gbs = algo_bytes / (split_ms * 1e-3) / 1e9
+        split_ms, combine_ms = (ms_per_step, full_min, full_max), (0.0,) * 3
+    split_gbs = algo_bytes / (split_ms[0] * 1e-3) / 1e9
+    # The same calls on ONE input set: K/V then sit in the 256 MB Infinity Cache when they fit
+    # (reported apart, never as the value).
+    warm_ms = (0.0,) * 3
+    if not args.no_warm:
+        rot[0] = 1
+        warm_ms = stats(graph_time(full, args.steps, reps))
+        rot[0] = R
+    tuning = gd.gqa_decode_get_tuning().as_dict()
+    cread, cwrite = combine_read_bytes(case, plan, tuning["piece_cost"])
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu:
         import oracle
         threads = oracle.max_threads()
         t0 = time.perf_counter()
@@ -307,8 +365,9 @@ def main():
                "sample": f"{calls} full calls of {name} through the fp64 C oracle "
                          f"({el:.1f} s, {threads} OpenMP threads)"}
 
-    traffic = measured_traffic(name) if args.kv == "bf16" else None
-    line = {
+    traffic = measured_traffic(name) if args.kv == "bf16" and case.M == 1 else None
+    us3 = lambda t: round(t * 1e3, 3)
+    return {
         "metric": METRIC if args.kv == "bf16" else METRIC + ", OCP FP8 E4M3 KV cache (1 B/element)",
         "value": round(gbs, 2),
         "unit": "GB/s",
@@ -316,8 +375,12 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
-        "us_per_call": round(us, 3),
+        "us_per_call": us3(ms_per_step),
+        "us_per_call_min": us3(full_min),
+        "us_per_call_max": us3(full_max),
+        "replays": reps,
         "eager_us_per_call": round(eager_us, 3),
+        "mall_warm_us_per_call": us3(warm_ms[0]) if not args.no_warm else None,
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -329,17 +392,82 @@ def main():
                    "q_heads": case.Hq, "kv_heads": case.Hkv,
                    "head_dim": case.D, "capacity": cap, "page_size": case.page_size,
                    "sum_len": int(case.seq_lens.sum()), "algorithmic_bytes": algo_bytes,
-                   "plan": plan.as_dict(), "rotated_sets": R, "parallelism": "single GPU"},
+                   "plan": plan.as_dict(), "tuning": tuning, "rotated_sets": R,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "gqa_split_kernel", "achieved": round(split_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel_us": round(split_ms * 1e3, 3),
-                     "combine_us": round(combine_ms * 1e3, 3),
-                     "timed": "K launches of the split kernel alone in one HIP graph, HIP events"
-                              if case.M == 1 else "K whole multi-query calls in one HIP graph"},
+                     "kernel_us": us3(split_ms[0]), "kernel_us_min": us3(split_ms[1]),
+                     "kernel_us_max": us3(split_ms[2]),
+                     "timed": (f"split kernel alone: median of {reps} replays of a HIP graph of K "
+                               "launches, HIP events on the launch stream")
+                              if case.M == 1 else
+                              f"whole multi-query calls: median of {reps} graph replays",
+                     "combine": {"kernel": "gqa_combine_narrow_kernel" if plan.max_pieces <= 16
+                                 else "gqa_combine_kernel",
+                                 "us": us3(combine_ms[0]), "us_min": us3(combine_ms[1]),
+                                 "us_max": us3(combine_ms[2]),
+                                 "bytes": cread + cwrite, "read_bytes": cread, "write_bytes": cwrite,
+                                 "GB/s": round((cread + cwrite) / (combine_ms[0] * 1e-3) / 1e9, 2)
+                                 if combine_ms[0] > 0 else None}},
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
+
+
+KERNELS = ("gqa_split_kernel", "gqa_combine_narrow_kernel", "gqa_combine_kernel")
+
+
+def summarize_counters(dirs):
+    """Per-dispatch averages of each counter, per kernel: rows of one dispatch and counter are
+    summed (rocprofv3 may report a counter per instance), then averaged over dispatches."""
+    per = {}   # (kernel, counter) -> {dispatch: value}
+    for d in dirs:
+        for r in _counter_rows(d):
+            name = r.get("Kernel_Name", "")
+            kern = next((k for k in KERNELS if k in name), None)
+            if kern is None:
+                continue
+            key = (kern, r["Counter_Name"])
+            disp = (d, r["Dispatch_Id"])
+            per.setdefault(key, {})
+            per[key][disp] = per[key].get(disp, 0.0) + float(r["Counter_Value"])
+    counters = sorted({c for _, c in per})
+    kernels = [k for k in KERNELS if any((k, c) in per for c in counters)]
+    print("| counter | " + " | ".join(kernels) + " |")
+    print("|---|" + "---|" * len(kernels))
+    for c in counters:
+        cells = []
+        for k in kernels:
+            v = per.get((k, c))
+            cells.append(f"{sum(v.values()) / len(v):,.0f} ({len(v)})" if v else "")
+        print(f"| {c} | " + " | ".join(cells) + " |")
+
+
+def main():
+    args = parse()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
+    if args.summarize_pmc:
+        from tests import workloads as W
+        summarize_pmc(*args.summarize_pmc, args.workload or W.HEADLINE)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import decode_attention_04_amd as gd
+    from tests import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    gd.load()
+    names = list(W.WORKLOADS) if args.all else [args.workload or W.HEADLINE]
+    for name in names:
+        line = measure(name, args, with_cpu=not args.no_cpu_baseline)
+        print(json.dumps(line), flush=True)
+        torch.cuda.empty_cache()
     if args.copy_calibration:
         copy_calibration()
 

@@ -56,7 +56,7 @@ class Plan(ctypes.Structure):
                 ("pv_mode", ctypes.c_int),
                 ("double_buffer", ctypes.c_int), ("streaming", ctypes.c_int),
                 ("workspace_bytes", ctypes.c_size_t), ("fused", ctypes.c_int),
-                ("fold_fanin", ctypes.c_int), ("counters", ctypes.c_int64)]
+                ("fold_fanin", ctypes.c_int), ("counters", ctypes.c_int64), ("qk_mode", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -66,7 +66,7 @@ class Tuning(ctypes.Structure):
     """gqa_tuning_t: the plan and kernel-variant choices (see include/gqa_decode.h)."""
     _fields_ = [(name, ctypes.c_int) for name in (
         "tile_tokens", "double_buffer", "pv_mode", "streaming", "partition", "shares", "split_keys",
-        "piece_cost", "halve_long", "combine", "combine_cols", "num_splits", "fold")]
+        "piece_cost", "halve_long", "combine", "combine_cols", "num_splits", "fold", "qk_mode")]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -58,6 +58,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -344,24 +345,103 @@ __device__ __forceinline__ void zero_v_past(Tile<D, NB, KV> &t, int t0, int len,
         }
 }
 
+// How QK^T is computed:
+//   kQkMfma  v_mfma_f32_16x16x32_bf16 with K as the A operand straight from the
+//            load registers and Q resident as the B operand (the default);
+//   kQkValu  the same K registers on the vector ALU: each lane owns a quarter
+//            of the head dims of one key (the A-operand layout), forms its
+//            partial dot product with every query row by v_dot2c_f32_bf16
+//            against a per-wave LDS copy of Q, the four quarters of a key are
+//            summed by two lane swaps, and a per-wave LDS transpose hands
+//            each lane the MFMA result layout.  An A/B variant (bf16 cache,
+//            bf16 PV, one register tile, head_dim 128 or 256).
+constexpr int kQkMfma = 0;
+constexpr int kQkValu = 1;
+
+template <int D, bool VALU>
+struct QkLds {};
+template <int D>
+struct QkLds<D, true> {
+    // 16-byte aligned: both are read and written 16 bytes per lane
+    alignas(16) unsigned q[kWaves][kMaxHeadsPerKv][D / 2];  // each wave's copy of its Q rows, bf16 pairs
+    alignas(16) float x[kWaves][kMaxHeadsPerKv][20];        // each wave's score transpose (rows of 80 bytes)
+};
+
+// A dword as two bf16 values.  (Taken through a scalar parameter: a bit cast
+// of an element of a vector value, __builtin_bit_cast(T, v[j]), compiled to
+// element 0 for every j with hipcc of ROCm 7.2.)
+__device__ __forceinline__ bf16x2_t as_bf16x2(unsigned w) { return __builtin_bit_cast(bf16x2_t, w); }
+
+// Orders a wave's own LDS writes before its following LDS reads by other lanes
+// (a wave's LDS instructions execute in program order; this keeps the
+// compiler from reordering them).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// kQkValu: this wave's Q rows (from the B-operand registers) into its LDS copy.
+template <int D>
+__device__ __forceinline__ void stage_q_valu(const bf16x8_t (&qb)[Shape<D>::KB], unsigned *qtab, int r, int grp) {
+#pragma unroll
+    for (int kb = 0; kb < Shape<D>::KB; ++kb)
+        *reinterpret_cast<u32x4_t *>(qtab + r * (D / 2) + 4 * grp + 16 * kb) = __builtin_bit_cast(u32x4_t, qb[kb]);
+    wave_lds_sync();
+}
+
+// QK^T of block blk (16 keys) of a tile: lane (r, grp) gets the scores of
+// query row r for keys 4*grp .. 4*grp + 3 of the block (rows >= R: zero).
+template <int D, int NB, int KV, int QKM>
+__device__ __forceinline__ f32x4_t qk_block(const Tile<D, NB, KV> &t, int blk, const bf16x8_t (&qb)[Shape<D>::KB],
+                                            const unsigned *qtab, float *xs, int r, int grp, int R) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (QKM == kQkMfma) {
+#pragma unroll
+        for (int kb = 0; kb < Shape<D>::KB; ++kb)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(t, blk, kb), qb[kb], c, 0, 0, 0);
+    } else {
+        static_assert(KV == kKvBf16, "the VALU QK^T variant reads bf16 K registers");
+        float part[kMaxHeadsPerKv];
+#pragma unroll
+        for (int h = 0; h < kMaxHeadsPerKv; ++h) {
+            part[h] = 0.f;
+            if (h < R) {
+                float acc = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < Shape<D>::KB; ++kb) {
+                    const u32x4_t qv = *reinterpret_cast<const u32x4_t *>(qtab + h * (D / 2) + 4 * grp + 16 * kb);
+                    const u32x4_t kw = t.k[blk][kb];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kw[j]), as_bf16x2(qv[j]), acc, false);
+                }
+                part[h] = sum_rows(acc);  // key r, all its head dims (in the four lanes of key r)
+            }
+        }
+        if (grp == 0) {
+#pragma unroll
+            for (int h = 0; h < kMaxHeadsPerKv; ++h) xs[h * 20 + r] = part[h];
+        }
+        wave_lds_sync();
+        c = *reinterpret_cast<const f32x4_t *>(xs + r * 20 + 4 * grp);
+        wave_lds_sync();  // read before the next block's writes
+    }
+    return c;
+}
+
 // QK^T and the online-softmax update for one tile whose first key has index
 // `t0` in the sequence (keys at or beyond `t_end`, this lane's row limit,
 // masked).  On return
 // sc[blk][i] holds the probability of key 16*blk + 4*grp + i for head r
 // (relative to the new running max) and acc has been rescaled.
-template <int D, int NB, int KV>
+template <int D, int NB, int KV, int QKM = kQkMfma>
 __device__ __forceinline__ void qk_softmax(const Tile<D, NB, KV> &t, const bf16x8_t (&qb)[Shape<D>::KB],
                                            WaveState<D> &st, int t0, int t_end, int grp,
-                                           float qk_scale_log2, f32x4_t (&sc)[NB]) {
+                                           float qk_scale_log2, f32x4_t (&sc)[NB], const unsigned *qtab = nullptr,
+                                           float *xs = nullptr, int r = 0, int R = 0) {
     using S = Shape<D>;
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < S::KB; ++kb)
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(t, blk, kb), qb[kb], c, 0, 0, 0);
-        sc[blk] = c;
-    }
+    for (int blk = 0; blk < NB; ++blk) sc[blk] = qk_block<D, NB, KV, QKM>(t, blk, qb, qtab, xs, r, grp, R);
     float mx = -INFINITY;
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
@@ -462,7 +542,7 @@ __device__ __forceinline__ void compute_tile(const Tile<D, NB, KV> &t, const bf1
 // wave's accumulator rows [16][D + 4] fp32 for the fold (+4 floats so that
 // consecutive rows start on other banks).  Each wave only ever touches its
 // own region until the workgroup barrier, so the two uses never overlap.
-template <int D, int NB>
+template <int D, int NB, int QKM = kQkMfma>
 struct FoldLds {
     static constexpr int kFoldBytes = kMaxHeadsPerKv * (D + 4) * 4;
     static constexpr int kStageBytes = 16 * NB * kStageStride<D> * 2;
@@ -472,6 +552,7 @@ struct FoldLds {
     alignas(16) unsigned char region[kWaves][kRegion];
     u32x4_t p[kWaves][NB][64];  // one-tile ranges: each wave's probabilities (bf16 hi, lo), in its lane layout
     unsigned ticket[2];         // in-kernel fold: arrival tickets
+    QkLds<D, QKM == kQkValu> qk;
     __device__ float *acc(int w) { return reinterpret_cast<float *>(region[w]); }
     __device__ unsigned short *stage(int w) { return reinterpret_cast<unsigned short *>(region[w]); }
 };
@@ -682,8 +763,8 @@ struct Prefetch {
 // `pre`, the tile loaded against the cache capacity before the length was
 // known (contiguous cache, single register tile only).  Paged: with have_pages,
 // pages0 already holds the page ids of the wave's first 64 tiles (t_begin = 0).
-template <int D, int NB, bool PAGED, int PV, bool DBUF, int CPOL, int KV, bool SPEC = false>
-__device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB> &lds, int b, int kvh,
+template <int D, int NB, bool PAGED, int PV, bool DBUF, int CPOL, int KV, bool SPEC = false, int QKM = kQkMfma>
+__device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB, QKM> &lds, int b, int kvh,
                                               int len, int t_begin, int t_end, size_t slot, bool direct,
                                               const Prefetch<D, NB, KV> *pre = nullptr, bool have_pages = false,
                                               int pages0 = 0) {
@@ -704,6 +785,13 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
         for (int kb = 0; kb < S::KB; ++kb) qb[kb] = pre->qb[kb];
     } else {
         load_q<D, KV>(a, b, kvh, r, grp, qb);
+    }
+    const unsigned *qtab = nullptr;
+    float *xs = nullptr;
+    if constexpr (QKM == kQkValu) {
+        stage_q_valu<D>(qb, lds.qk.q[wave][0], r, grp);
+        qtab = lds.qk.q[wave][0];
+        xs = lds.qk.x[wave][0];
     }
     // Multi-query: query token i (row r = i * G + g) is position len - M + i
     // and sees keys < len - M + i + 1 (rows r >= R: any limit, never written).
@@ -788,7 +876,7 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
                 if (it == 0) {
                     // The first tile's K arrives before its V (issued first):
                     // QK^T and the softmax run while V is still in flight.
-                    qk_softmax(buf, qb, st, tile_start(it), row_end, grp, a.qk_scale_log2, sc);
+                    qk_softmax<D, NB, KV, QKM>(buf, qb, st, tile_start(it), row_end, grp, a.qk_scale_log2, sc, qtab, xs, r, a.R);
                     if (more) issue(buf, it + 1, kLoadK);
                     if constexpr (SPEC) {
                         // rows past len were read from the capacity; K's are masked above
@@ -801,7 +889,7 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
                     // write latency before PV reads the staged V back.
                     stage_v(buf, r, grp, stage);
                     if (more) issue(buf, it + 1, kLoadV);
-                    qk_softmax(buf, qb, st, tile_start(it), row_end, grp, a.qk_scale_log2, sc);
+                    qk_softmax<D, NB, KV, QKM>(buf, qb, st, tile_start(it), row_end, grp, a.qk_scale_log2, sc, qtab, xs, r, a.R);
                     if (more) issue(buf, it + 1, kLoadK);
                 }
                 pv_tile<D, NB, PV, KV>(buf, sc, st, r, grp, stage);
@@ -906,8 +994,8 @@ __device__ __forceinline__ void process_range(const SplitArgs &a, FoldLds<D, NB>
 //   acc[:, quarter] = sum_w P_w V_w[:, quarter]   (blocks of 16 keys in
 //   ascending pairs, one 32-deep MFMA per pair and part).
 // Tile loads as in process_range; `pf` holds Q and the tile when SPEC.
-template <int D, int NB, bool PAGED, int CPOL, int KV, bool SPEC>
-__device__ __forceinline__ void process_single(const SplitArgs &a, FoldLds<D, NB> &lds, int b, int kvh, int len,
+template <int D, int NB, bool PAGED, int CPOL, int KV, bool SPEC, int QKM = kQkMfma>
+__device__ __forceinline__ void process_single(const SplitArgs &a, FoldLds<D, NB, QKM> &lds, int b, int kvh, int len,
                                                int t_begin, int t_end, size_t slot, bool direct,
                                                Prefetch<D, NB, KV> &pf) {
     using S = Shape<D>;
@@ -953,13 +1041,15 @@ __device__ __forceinline__ void process_single(const SplitArgs &a, FoldLds<D, NB
     // their maximum per head row; the range's maximum is known after one exchange.
     f32x4_t sc[NB];
     float mx = -INFINITY;
+    if constexpr (QKM == kQkValu) stage_q_valu<D>(pf.qb, lds.qk.q[wave][0], r, grp);
     if (has) {
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
-            f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < S::KB; ++kb)
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(tile, blk, kb), pf.qb[kb], c, 0, 0, 0);
+            f32x4_t c;
+            if constexpr (QKM == kQkValu)
+                c = qk_block<D, NB, KV, QKM>(tile, blk, pf.qb, lds.qk.q[wave][0], lds.qk.x[wave][0], r, grp, a.R);
+            else
+                c = qk_block<D, NB, KV, QKM>(tile, blk, pf.qb, nullptr, nullptr, r, grp, a.R);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tok = t0 + 16 * blk + 4 * grp + i;
@@ -1272,12 +1362,12 @@ __device__ __forceinline__ void fold_segment(float *part_acc, float *part_ml, fl
     }
 }
 
-template <int D, int NB, bool PAGED, int PV, bool DBUF, int PART, int CPOL, int KV>
+template <int D, int NB, bool PAGED, int PV, bool DBUF, int PART, int CPOL, int KV, int QKM = kQkMfma>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEu<D, NB, DBUF>)))
 void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const unsigned char *v, const uint16_t *q,
                       int num_splits, int Hkv, int B, int cap, int split_tokens, int qpack, const SplitArgs args) {
     constexpr int TT = 16 * NB;
-    __shared__ FoldLds<D, NB> lds;
+    __shared__ FoldLds<D, NB, QKM> lds;
     // The leading scalar arguments arrive preloaded in SGPRs, so the length,
     // Q and first-tile loads below issue without waiting for the kernel-argument
     // fetch.  qpack = G | M << 5 | R << 10 | qdiv << 15.
@@ -1428,7 +1518,7 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
                                                    a.max_pages);
                     fetched = true;
                 }
-                process_range<D, NB, PAGED, PV, DBUF, CPOL, KV>(a, lds, b, kvh, len, off * TT,
+                process_range<D, NB, PAGED, PV, DBUF, CPOL, KV, false, QKM>(a, lds, b, kvh, len, off * TT,
                                                                 min(len, (off + take) * TT), slot, whole, nullptr,
                                                                 have_pages, pages);
                 cur += take;
@@ -1501,10 +1591,11 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
         // (the one-tile path splits the head dims in quarters of 16-dim blocks: D >= 64)
         if (D >= 64 && !DBUF && PV == kPvBf16 && a.split_tokens <= kWaves * TT) {
             if constexpr (D >= 64)
-                process_single<D, NB, PAGED, CPOL, KV, kSpec>(a, lds, b, kvh, len, t_begin, t_end, slot, direct, pre);
+                process_single<D, NB, PAGED, CPOL, KV, kSpec, QKM>(a, lds, b, kvh, len, t_begin, t_end, slot, direct,
+                                                                   pre);
         } else {
-            process_range<D, NB, PAGED, PV, DBUF, CPOL, KV, kSpec>(a, lds, b, kvh, len, t_begin, t_end, slot, direct,
-                                                                   &pre);
+            process_range<D, NB, PAGED, PV, DBUF, CPOL, KV, kSpec, QKM>(a, lds, b, kvh, len, t_begin, t_end, slot,
+                                                                        direct, &pre);
         }
         if (args.fused && !direct) {
             // In-kernel fold: a tree over the segment's splits, fan-in F.  The
@@ -1828,7 +1919,7 @@ bool tuning_valid(const gqa_tuning_t &t) {
            in(t.halve_long, 0, 1) && in(t.combine, 0, 1) &&
            (t.combine_cols == 0 || t.combine_cols == 2 || t.combine_cols == 4 || t.combine_cols == 8 ||
             t.combine_cols == 16) &&
-           in(t.num_splits, 0, INT32_MAX) && in(t.fold, 0, 2);
+           in(t.num_splits, 0, INT32_MAX) && in(t.fold, 0, 2) && in(t.qk_mode, 0, 1);
 }
 
 // Each variable that is set to a valid value replaces its field; anything
@@ -1864,6 +1955,7 @@ gqa_tuning_t tuning_from_env() {
     num("GQA_DECODE_SPLITS", t.num_splits, 1, INT32_MAX);
     if (is("GQA_DECODE_FOLD", "kernel")) t.fold = 1;
     if (is("GQA_DECODE_FOLD", "fused")) t.fold = 2;
+    if (is("GQA_DECODE_QK", "valu")) t.qk_mode = 1;
     return t;
 }
 
@@ -2042,6 +2134,13 @@ hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, int kv, h
         } else if (plan.double_buffer) {
             even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionEven, 0, kKvBf16>)
                  : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, true, kPartitionFixed, 0, kKvBf16>);
+        } else if (nt && plan.qk_mode == kQkValu) {
+            if constexpr (D >= 128 && NB == 1) {
+                even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, kNonTemporal, kKvBf16, kQkValu>)
+                     : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, kNonTemporal, kKvBf16, kQkValu>);
+            } else {
+                return hipErrorInvalidValue;  // the plan never selects it here
+            }
         } else if (nt) {
             even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, kNonTemporal, kKvBf16>)
                  : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, kNonTemporal, kKvBf16>);
@@ -2199,6 +2298,10 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
     // Infinity Cache, so they stream from HBM (measured faster at every
     // workload size when the inputs are not cache-resident).
     plan->streaming = t.streaming;
+    // QK^T on the vector ALU (A/B variant): the default pipeline only, head_dim
+    // 128 or 256 with 16-key tiles, bf16 cache.
+    plan->qk_mode = (t.qk_mode == kQkValu && elem_bytes == 2 && D >= 128 && tt == 16 && !dbuf && t.pv_mode == kPvBf16 &&
+                     t.streaming) ? kQkValu : kQkMfma;
 
     // Even shares (the default for batches): about two workgroups per CU, each at least
     // one tile per wave at full length; a segment short enough for one

@@ -81,6 +81,7 @@ typedef struct gqa_plan {
                                0: a combine kernel folds them (two launches) */
     int fold_fanin;         /* fused fixed splits: partials per node of the fold tree; otherwise 0 */
     int64_t counters;       /* arrival counters a fused call uses in the workspace header (0 otherwise) */
+    int qk_mode;            /* QK^T contraction: 0 = bf16 MFMA, 1 = vector ALU (see gqa_tuning_t.qk_mode) */
 } gqa_plan_t;
 
 /*
@@ -120,6 +121,10 @@ typedef struct gqa_tuning {
                           node of a fold tree over fixed splits -- in a fixed order, so results stay
                           bit-exact from run to run); 0 (default): the combine kernel, measured faster on
                           MI355X at every workload shape tried */
+    int qk_mode;       /* GQA_DECODE_QK=valu -> 1: QK^T on the vector ALU (v_dot2c_f32_bf16 over each lane's
+                          quarter of the head dims, two lane swaps, an LDS transpose) where the plan allows
+                          it (bf16 cache and PV, one register tile, head_dim 128 or 256, 16-key tiles); an
+                          A/B variant.  0 (default): bf16 MFMA */
 } gqa_tuning_t;
 
 /* The tuning calls use from now on (a copy). */

@@ -439,3 +439,35 @@ def test_cache_policy_variants(tune, nt):
     out = dc.run_host()
     assert np.array_equal(out.view(np.uint32), base.view(np.uint32))
     compare(out, oracle_out(case), f"nt={nt}")
+
+
+# ------------------------------------------------------------------ QK^T on the vector ALU (A/B variant)
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 2), (12, 2), (16, 2), (16, 1), (24, 4)])
+def test_qk_valu_variant(tune, D, Hq, Hkv):
+    """The vector-ALU QK^T (v_dot2c over each lane's head-dim quarter, lane swaps, an LDS
+    transpose) against the oracle, with ragged lengths and a NaN tail, in fixed splits (one-tile
+    and key-range workgroups) and even shares, contiguous and paged; bit-exact across runs."""
+    tune(qk_mode=1)
+    say(f"[parity] qk valu D={D} Hq={Hq} Hkv={Hkv}")
+    lens = [1, 15, 17, 53, 700, 2000]
+    case = W.contig_case(len(lens), Hq, Hkv, D, 2048, seq_lens=lens, seed=130 + D + Hq, tail="nan")
+    assert gd.gqa_decode_plan(case.B, Hq, Hkv, D, 2048).qk_mode == 1
+    dc = DeviceCase(case)
+    ref = oracle_out(case)
+    for splits in (0, 1, 3, 40):
+        a = dc.run_host(splits)
+        compare(a, ref, f"qk valu D={D} G={Hq // Hkv} splits={splits}")
+        assert np.array_equal(a.view(np.uint32), dc.run_host(splits).view(np.uint32))
+    paged = W.paged_case(4, Hq, Hkv, D, 32, 300, seq_lens=[1, 900, 2048, 333], max_len=2048, seed=131 + D)
+    compare(DeviceCase(paged).run_host(), oracle_out(paged), f"qk valu paged D={D}")
+
+
+@pytest.mark.parametrize("name", ["gqa6_d256_ctx4096", "batched_gqa8_d128_ctx16k", "paged_gqa4_d128_ragged8k",
+                                  "long_gqa8_d128_ctx128k_peaky"])
+def test_qk_valu_workloads(tune, name):
+    tune(qk_mode=1)
+    say(f"[parity] qk valu workload {name}")
+    case = W.make(name)
+    assert gd.gqa_decode_plan(case.B, case.Hq, case.Hkv, case.D, case.capacity, case.page_size).qk_mode == 1
+    compare(DeviceCase(case).run_host(), oracle_out(case), f"qk valu {name}")

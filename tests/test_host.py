@@ -318,7 +318,7 @@ def test_default_tuning():
     t = gd.gqa_decode_get_tuning().as_dict()
     assert t == dict(tile_tokens=0, double_buffer=0, pv_mode=1, streaming=1, partition=0, shares=0,
                      split_keys=0, piece_cost=4, halve_long=1, combine=0, combine_cols=0,
-                     num_splits=0, fold=0)
+                     num_splits=0, fold=0, qk_mode=0)
 
 
 @pytest.mark.parametrize("field,value", [
