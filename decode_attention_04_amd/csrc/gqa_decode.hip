@@ -2027,14 +2027,18 @@ WorkspaceLayout workspace_layout(int Hq, int Hkv, int D, int64_t slots) {
 
 // Which plans fold in the split kernel by default (tuning fold = 0).  On
 // MI355X a level of the in-kernel fold costs more than the second launch it
-// saves: the device-scope store acknowledgement and the ticket take ~1.3 us,
-// and one workgroup folding a group is held to a single CU's memory pipe, where
-// the combine kernel spreads the same reads over the whole device.  Measured,
-// us per call (two launches vs one): GQA-6 hd256 4k 8.6 vs 15.1, 128k keys on
-// one kv head 16.2 vs 20.4, ragged paged 8k 107.6 vs 111.3, uniform 16k batch
-// 83.0 vs 82.6.  So both partitions fold in a combine kernel by default.
+// saves unless the fold is small: the device-scope store acknowledgement and
+// the ticket take ~1.3 us, and one workgroup folding a group is held to a
+// single CU's memory pipe, where the combine kernel spreads the same reads
+// over the whole device.  Measured, us per call (two launches vs one): GQA-6
+// hd256 4k 8.6 vs 15.1, 128k keys on one kv head 16.2 vs 20.4, ragged paged 8k
+// 107.6 vs 111.3, uniform 16k batch 83.0 vs 82.6 -- but 512 keys on two kv
+// heads in 4 splits 6.18 vs 5.61 (2, 4 and 8 splits all favour one launch).
+// So fixed splits fold in the kernel when the whole fold is one small node
+// (at most kNarrowPieces partials of at most kSmallFoldBytes per segment),
+// and everything else folds in a combine kernel.
 constexpr bool kFuseEvenByDefault = false;
-constexpr bool kFuseFixedByDefault = false;
+constexpr int64_t kSmallFoldBytes = 16 << 10;
 
 // Fan-in of the fold tree over S fixed splits: one node for up to
 // kNarrowPieces splits, else the smallest power of two F with F * F >= S
@@ -2346,7 +2350,16 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
         S = fill > len_cap ? fill : len_cap;
         const int most = (tiles_total + kWaves - 1) / kWaves;
         if (S > most) S = most;
-        if (tiles_total <= 4 * kWaves) S = 1;
+        if (tiles_total <= 4 * kWaves) {
+            // A short segment fits one workgroup (a direct write), but while
+            // the splits take at most half the device, one tile per wave over
+            // several workgroups and a small fold finish sooner (cold caches,
+            // us per call, direct vs split: 512 keys on two kv heads 7.00 vs
+            // 5.63; 256 keys on 8 kv heads 6.73 vs 6.27; GQA-6 hd256 with 256
+            // keys 10.85 vs 7.64; with the splits filling every CU, 64 kv
+            // heads of 256 keys: 7.02 vs 7.59).
+            S = (most >= 2 && (int64_t)base * most <= cu_count / 2) ? most : 1;
+        }
     }
     if (S > tiles_total) S = tiles_total;
     if (S < 1) S = 1;
@@ -2366,7 +2379,8 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
     if (!plan->direct) {
         // In-kernel fold: a tree over each segment's splits (fan-in F), one
         // counter per node; the inner nodes' partials follow the splits'.
-        const bool fuse = t.fold == 2 || (t.fold == 0 && kFuseFixedByDefault);
+        const bool small = S <= kNarrowPieces && (int64_t)S * (Hq / Hkv) * D * 4 <= kSmallFoldBytes;
+        const bool fuse = t.fold == 2 || (t.fold == 0 && small);
         const int F = fold_fanin(S);
         const int64_t nodes = fold_tree_nodes(S, F);
         if (fuse && (int64_t)base * nodes <= kMaxCounters) {

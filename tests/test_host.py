@@ -93,7 +93,9 @@ def test_plan_invariants(shape, cu):
         assert p.grid == B * Hkv * p.num_splits
         assert p.direct == (p.num_splits == 1)
         assert p.slots == B * Hkv * p.num_splits
-        assert p.fused == 0 and p.counters == 0   # fixed splits fold in a combine kernel by default
+        # fixed splits fold in the split kernel by default only when the fold is one small node
+        small = p.num_splits <= 16 and p.num_splits * (Hq // Hkv) * D * 4 <= 16384
+        assert p.fused == (small and not p.direct)
     assert p.pv_mode == 1  # bf16 MFMA PV unless the tuning selects fp32
     assert p.double_buffer == 0
     assert p.streaming == 1
@@ -125,8 +127,12 @@ def test_plan_fills_the_device():
     # the GQA-6 layer (4 kv heads, 4096 keys) cannot give every wave more than one tile
     p = gd.gqa_decode_plan(1, 24, 4, 256, 4096, 0, 0, 256)
     assert p.grid == 256 and p.split_tokens == 4 * p.tile_tokens
-    # a short cache is one direct split per (sequence, kv head)
+    # a short cache: one tile per wave over several workgroups where the device has room, the
+    # few small partials folded in the split kernel; direct (one workgroup) when it has none
     p = gd.gqa_decode_plan(1, 8, 2, 64, 512, 0, 0, 256)
+    assert p.partition == 0 and p.num_splits == 4 and p.split_tokens == 4 * p.tile_tokens
+    assert p.fused == 1 and p.fold_fanin == 4 and p.counters == 2
+    p = gd.gqa_decode_plan(64, 32, 8, 128, 256, 0, 0, 256)
     assert p.partition == 0 and p.direct == 1 and p.workspace_bytes == 0
 
 
