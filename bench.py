@@ -78,6 +78,10 @@ def parse():
     ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
                     help="print a markdown table of the per-dispatch averages of every counter in "
                          "these rocprofv3 --pmc output directories, per kernel of this library")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="per-kernel durations from a rocprofv3 --kernel-trace output directory of a "
+                         "bench.py run with the same --steps/--reps: all dispatches, and the timed "
+                         "replays of the one-kernel graphs (each kernel's last steps*reps dispatches)")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the cache-warm figure (one input set), e.g. under a counter run")
     return ap.parse_args()
@@ -317,10 +321,11 @@ def measure(name, args, with_cpu):
     gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
     # The split kernel alone (the dominant kernel) and the combine alone, each replayed the same
     # way, on the stream they are launched on.
-    if case.M == 1:
+    one_kernel = plan.direct or plan.fused   # a call is the split kernel alone
+    if case.M == 1 and not one_kernel:
         split_ms = stats(graph_time(split_only, args.steps, reps))
-        combine_ms = stats(graph_time(combine_only, args.steps, reps)) if not plan.direct else (0.0,) * 3
-    else:   # multi-query calls have no split-only entry point: the roofline uses whole calls
+        combine_ms = stats(graph_time(combine_only, args.steps, reps))
+    else:   # one kernel per call (or multi-query calls, which have no split-only entry point)
         split_ms, combine_ms = (ms_per_step, full_min, full_max), (0.0,) * 3
     split_gbs = algo_bytes / (split_ms[0] * 1e-3) / 1e9
     # The same calls on ONE input set: K/V then sit in the 256 MB Infinity Cache when they fit
@@ -401,9 +406,13 @@ def measure(name, args, with_cpu):
                      "kernel_us_max": us3(split_ms[2]),
                      "timed": (f"split kernel alone: median of {reps} replays of a HIP graph of K "
                                "launches, HIP events on the launch stream")
-                              if case.M == 1 else
+                              if case.M == 1 and not one_kernel else
+                              (f"whole calls, one kernel each (the split kernel "
+                               f"{'writes the output directly' if plan.direct else 'folds its own partials'}): "
+                               f"median of {reps} graph replays") if one_kernel else
                               f"whole multi-query calls: median of {reps} graph replays",
-                     "combine": {"kernel": "gqa_combine_narrow_kernel" if plan.max_pieces <= 16
+                     "combine": None if one_kernel else
+                                {"kernel": "gqa_combine_narrow_kernel" if plan.max_pieces <= 16
                                  else "gqa_combine_kernel",
                                  "us": us3(combine_ms[0]), "us_min": us3(combine_ms[1]),
                                  "us_max": us3(combine_ms[2]),
@@ -443,8 +452,34 @@ def summarize_counters(dirs):
         print(f"| {c} | " + " | ".join(cells) + " |")
 
 
+def summarize_trace(directory, timed):
+    """Durations (ns) of this library's kernels in a kernel-trace CSV: every dispatch, and the
+    last `timed` dispatches of each (the timed replays of its one-kernel graph in bench.py)."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    print("| kernel | dispatches | mean ns (all) | timed replays: n | mean ns | median ns | min | max |")
+    print("|---|---|---|---|---|---|---|---|")
+    for k in KERNELS:
+        d = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                   for r in rows if k in r.get("Kernel_Name", "") and
+                   not any(o != k and o in r.get("Kernel_Name", "") and len(o) > len(k) for o in KERNELS))
+        if not d:
+            continue
+        allv = [x for _, x in d]
+        last = sorted(allv[-timed:])
+        print(f"| {k} | {len(allv)} | {sum(allv) / len(allv):,.0f} | {len(last)} | "
+              f"{sum(last) / len(last):,.0f} | {last[len(last) // 2]:,} | {last[0]:,} | {last[-1]:,} |")
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.steps * max(5, args.reps))
+        return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
         return

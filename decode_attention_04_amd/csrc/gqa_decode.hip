@@ -1,45 +1,51 @@
 // Single-token GQA flash-decode attention over a bf16 KV cache, gfx950 only.
 //
-// Two kernels (the split-KV scheme of the AstrAI csrc commit log and the
-// partial/combine structure of sparkinfer PR #877, section Mechanism):
+// The split-KV scheme of the AstrAI csrc commit log (split-KV bullets) with the
+// partial/fold structure of sparkinfer PR #877 (section Mechanism):
 //
-//   gqa_split_kernel   one workgroup per (sequence b, kv head, split s).  Its
-//                      NW waves stripe the split's tiles (tile i goes to wave
-//                      i % NW), each keeping its own running (m, l, acc); the
-//                      waves are folded in LDS in ascending wave order and the
-//                      workgroup emits one unnormalised partial per query head
-//                      (or the final output when there is a single split).
-//   gqa_combine_kernel folds the S partials of each (b, h) with the
-//                      log-sum-exp rescale in a fixed order.
+//   gqa_split_kernel   a workgroup of four waves takes a key range of one
+//                      (sequence b, kv head) segment -- a fixed split, or a
+//                      piece of an even share of the concatenated tiles of all
+//                      segments -- for all G query heads of the kv head, and
+//                      emits one unnormalised partial (m, l, acc) per query
+//                      head, or the output itself when its range is the whole
+//                      segment.
+//   gqa_combine_kernel / gqa_combine_narrow_kernel
+//                      fold the partials of each (b, h) with the log-sum-exp
+//                      rescale in a fixed order (a tree for many partials, one
+//                      thread per column for few).
+//   With the tuning's in-kernel fold, the split workgroup that writes the last
+//   partial of a group (an arrival ticket tells it) folds the group itself and
+//   the combine kernel is not launched.
 //
-// Layout of the work inside one wave (64 lanes, r = lane % 16, grp = lane / 16):
+// The default pipeline inside one wave (64 lanes, r = lane % 16, grp = lane / 16):
 //
-//   QK^T  v_mfma_f32_16x16x32_bf16 with A = 16 keys x 32 dims and
-//         B = 32 dims x 16 query heads (the G heads of the kv head, zero
-//         padded to 16).  Lane (r, grp) loads 16 contiguous bytes of key row r
-//         straight from HBM into the A operand, so K never passes through LDS.
-//         Q is exact bf16 and stays resident in the B operand registers.  The
-//         result gives lane (r, grp) the scores of query head r for keys
-//         4*grp .. 4*grp+3 of each 16-key block.
-//   softmax the scale (times log2 e) is applied to the fp32 scores; the
-//         running max of head r is shared by the four lanes r, r+16, r+32,
-//         r+48 (two xor shuffles per tile); l is kept per lane and summed
-//         once at the end.
-//   PV    v_mfma_f32_16x16x4_f32 computing O^T[d][g] += V^T[d][t] P^T[t][g].
-//         The B operand is the lane's own probability (no data movement), the
-//         A operand one fp32 value of V for the lane's key; lane (r, grp)
-//         loads 16 contiguous bytes of V row (4*grp + j), so P is never
-//         rounded to bf16 and V never needs a transpose.  The accumulator
-//         rows are head dims, its columns query heads: lane (r, grp) owns
-//         head r, so the softmax rescale of acc is lane-local.
+//   K/V   16-byte raw buffer loads with the non-temporal hint; the buffer
+//         bounds end at the sequence length, so rows past it read as zero and
+//         a NaN in an unused cache tail never reaches a sum.  One register tile
+//         per wave (16 keys at head_dim >= 128), refilled part by part as soon
+//         as each part is dead, so the next tile's loads fly during this
+//         tile's math (the role of the shared-memory double buffer of
+//         sparkinfer PR #874, section Summary).
+//   QK^T  v_mfma_f32_16x16x32_bf16 with A = 16 keys x 32 dims straight from the
+//         load registers and B = 32 dims x 16 query rows (the G heads of the kv
+//         head, zero padded); Q is exact bf16, resident in the B operand.  Lane
+//         (r, grp) receives the scores of query row r for keys 4*grp .. +3.
+//   softmax  the scale (times log2 e) applied to the fp32 scores; the running
+//         max of row r is shared by lanes r, r+16, r+32, r+48 through the
+//         gfx950 lane swaps; l is kept per lane and summed once at the end.
+//   PV    bf16 MFMAs with P split into bf16 hi + lo parts (P = hi + lo to about
+//         2^-17 relative); V staged row-major in a per-wave LDS buffer and read
+//         back by transposing LDS reads; the accumulator's column is the lane's
+//         own query row, so the softmax rescale is lane-local.
+//   Ranges of at most four tiles (one per wave) run in lock step instead: two
+//   LDS exchanges (row maxima, then the probabilities against the range's
+//   maximum) and PV split by head-dim quarters, with no fold afterwards.
 //
-// K/V tiles are double-buffered in VGPRs: the loads of the wave's next tile
-// are issued before the current tile's QK / softmax / PV, so HBM latency
-// overlaps compute (the role of the two shared-memory buffers of sparkinfer
-// PR #874, section Summary).  Loads use buffer resources whose size ends at
-// the sequence length, so rows past the end read as zero (the zero-filling
-// predicated copy of the AstrAI csrc commit log) and a NaN in the unused tail
-// of a cache can never reach the sums.
+// A/B variants kept for same-binary comparison (gqa_tuning_t): PV on fp32
+// MFMAs (v_mfma_f32_16x16x4_f32 on V widened from the load registers), two
+// register tiles per wave, QK^T on the vector ALU, the default cache policy,
+// the tree combine for every plan, the in-kernel fold everywhere.
 
 #include <hip/hip_runtime.h>
 
