@@ -28,8 +28,9 @@ _lib = None
 
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
-    """Compile oracle.c with gcc (always recompiles)."""
-    tmp = out + ".tmp"
+    """Compile oracle.c with gcc (always recompiles).  Each process writes its own temporary
+    file and renames it into place, so concurrent builds (parallel test workers) do not collide."""
+    tmp = f"{out}.{os.getpid()}.tmp"
     subprocess.check_call(["gcc", *CFLAGS, src, "-o", tmp, "-lm"])
     os.replace(tmp, out)
     return out
