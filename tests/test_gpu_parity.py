@@ -174,6 +174,33 @@ def test_side_stream_and_reused_workspace():
         compare(o.cpu().numpy(), ref, "side stream")
 
 
+def test_side_stream_internal_buffers():
+    """Kernels launched on stream s while the default stream is current, with no workspace or
+    output passed: the binding allocates both for s, so blocks of the same size that the default
+    stream allocates and fills (NaN bits) meanwhile never alias them while s is still busy."""
+    say("[parity] side stream, internal buffers")
+    case = W.contig_case(2, 8, 2, 128, 4096, seq_lens=[4096, 1333], seed=28)
+    dc = DeviceCase(case)
+    ref = oracle_out(case)
+    need = gd.gqa_decode_workspace_bytes(2, 8, 2, 128, 4096, 0, 0)
+    a = torch.randn(2048, 2048, device="cuda")
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    outs = []
+    for _ in range(4):
+        with torch.cuda.stream(s):
+            for _ in range(4):
+                a = a @ a / 64  # keeps s busy, so the decode kernels are still queued below
+        outs.append(dc.run(0, stream=s))
+        junk = torch.empty(need, dtype=torch.uint8, device="cuda").fill_(255)
+        junk_out = torch.empty((case.B, case.Hq, case.D), dtype=torch.float32, device="cuda").fill_(float("nan"))
+        del junk, junk_out
+    s.synchronize()
+    torch.cuda.synchronize()
+    for o in outs:
+        compare(o.cpu().numpy(), ref, "side stream, internal buffers")
+
+
 # ------------------------------------------------------------------ paged
 @pytest.mark.parametrize("ps", [16, 32, 64, 48])
 @pytest.mark.parametrize("D", [32, 64, 128, 256])
