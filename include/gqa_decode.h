@@ -119,8 +119,10 @@ typedef struct gqa_tuning {
                           the last partial of a group, as counted by an arrival ticket in the workspace
                           header, folds the group -- every piece of a segment in the even partition, a
                           node of a fold tree over fixed splits -- in a fixed order, so results stay
-                          bit-exact from run to run); 0 (default): the combine kernel, measured faster on
-                          MI355X at every workload shape tried */
+                          bit-exact from run to run); 0 (default): the combine kernel, except for fixed
+                          splits whose fold is one node of at most 16 partials, 16 KB in all, per
+                          (sequence, kv head), which the split kernel folds (measured faster there
+                          only) */
     int qk_mode;       /* GQA_DECODE_QK=valu -> 1: QK^T on the vector ALU (v_dot2c_f32_bf16 over each lane's
                           quarter of the head dims, two lane swaps, an LDS transpose) where the plan allows
                           it (bf16 cache and PV, one register tile, head_dim 128 or 256, 16-key tiles); an

@@ -468,6 +468,49 @@ def test_cache_policy_variants(tune, nt):
     compare(out, oracle_out(case), f"nt={nt}")
 
 
+# ------------------------------------------------------------------ tile size and register buffering (A/B variants)
+@pytest.mark.parametrize("dbuf", [0, 1])
+@pytest.mark.parametrize("tile", [16, 32, 64])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_tile_and_buffer_variants(tune, tile, dbuf, D):
+    """Keys per wave tile 16, 32 or 64 (where K+V of a tile fit 16 KB per wave) with one or two
+    register tiles per wave, against the oracle: ragged lengths with a NaN tail over fixed splits
+    (one-tile and key-range workgroups) and even shares, and a paged cache whose page holds 32
+    keys (the tile is halved until it divides the page)."""
+    tune(tile_tokens=tile, double_buffer=dbuf)
+    say(f"[parity] tile={tile} dbuf={dbuf} D={D}")
+    lens = [1, 15, 17, 53, 700, 2000]
+    case = W.contig_case(len(lens), 16, 2, D, 2048, seq_lens=lens, seed=150 + D + tile + dbuf, tail="nan")
+    plan = gd.gqa_decode_plan(case.B, 16, 2, D, 2048)
+    assert plan.double_buffer == dbuf
+    assert plan.tile_tokens == (tile if tile * D * 4 <= 16384 else plan.tile_tokens)
+    dc = DeviceCase(case)
+    ref = oracle_out(case)
+    for splits in (0, 1, 3, 40):
+        a = dc.run_host(splits)
+        compare(a, ref, f"tile={tile} dbuf={dbuf} D={D} splits={splits}")
+        assert np.array_equal(a.view(np.uint32), dc.run_host(splits).view(np.uint32))
+    paged = W.paged_case(4, 16, 2, D, 32, 300, seq_lens=[1, 900, 2048, 333], max_len=2048, seed=151 + D)
+    compare(DeviceCase(paged).run_host(), oracle_out(paged), f"tile={tile} dbuf={dbuf} paged D={D}")
+
+
+@pytest.mark.parametrize("name,fields", [
+    ("batched_gqa8_d128_ctx16k", {"tile_tokens": 32}),
+    ("batched_gqa8_d128_ctx16k", {"double_buffer": 1}),
+    ("paged_gqa4_d128_ragged8k", {"tile_tokens": 32}),
+    ("paged_gqa4_d128_ragged8k", {"double_buffer": 1}),
+    ("paged_gqa4_d128_ragged8k", {"shares": 256, "double_buffer": 1}),
+    ("long_gqa8_d128_ctx128k_peaky", {"tile_tokens": 32}),
+    ("long_gqa8_d128_ctx128k_peaky", {"double_buffer": 1}),
+], ids=lambda x: x if isinstance(x, str) else ",".join(f"{k}={v}" for k, v in x.items()))
+def test_variant_workloads(tune, name, fields):
+    """The full-size workloads under the tile and buffering variants that bench.py --ab times."""
+    tune(**fields)
+    say(f"[parity] variant {fields} workload {name}")
+    case = W.make(name)
+    compare(DeviceCase(case).run_host(), oracle_out(case), f"{fields} {name}")
+
+
 # ------------------------------------------------------------------ QK^T on the vector ALU (A/B variant)
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 2), (12, 2), (16, 2), (16, 1), (24, 4)])
