@@ -23,8 +23,8 @@ FLAGS = [
 
 
 def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Always recompiles; writes atomically."""
-    tmp = out + ".tmp"
+    """Always recompiles; writes atomically (each process through its own temporary file)."""
+    tmp = f"{out}.{os.getpid()}.tmp"
     cmd = [HIPCC, *FLAGS, *(extra or []), "-I", INCLUDE, SRC, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"

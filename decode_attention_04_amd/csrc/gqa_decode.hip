@@ -1004,7 +1004,6 @@ template <int D, int NB, bool PAGED, int CPOL, int KV, bool SPEC, int QKM = kQkM
 __device__ __forceinline__ void process_single(const SplitArgs &a, FoldLds<D, NB, QKM> &lds, int b, int kvh, int len,
                                                int t_begin, int t_end, size_t slot, bool direct,
                                                Prefetch<D, NB, KV> &pf) {
-    using S = Shape<D>;
     constexpr int TT = 16 * NB;
     constexpr int NQ = D / 64;  // 16-dim blocks per quarter of the head dims
     constexpr int RS = kStageStride<D>;
