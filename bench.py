@@ -226,6 +226,10 @@ def parse_ab(spec):
     return out
 
 
+class SkipWorkload(Exception):
+    """A workload this run's options do not apply to (e.g. M * G > 16 query rows per kv head)."""
+
+
 class Workload:
     """One workload on the device: R rotated copies of its seeded inputs (R * KV bytes above
     --rotate-bytes, several times the 256 MB Infinity Cache), one output per copy, one workspace
@@ -244,6 +248,9 @@ class Workload:
         if args.queries > 1:
             if args.kv != "bf16":
                 sys.exit("--queries > 1 runs on the bf16 cache")
+            if args.queries * (case.Hq // case.Hkv) > 16:
+                raise SkipWorkload(f"{name}: {args.queries} queries x G = {case.Hq // case.Hkv} "
+                                   "exceeds the 16 query rows of one kv head; skipped")
             case = W.with_queries(case, args.queries)
         self.case = case
         base = DeviceCase(case)
@@ -518,7 +525,13 @@ def run_lines(names, args):
     reps = max(5, args.reps)
     loads, graphs = [], []
     for name in names:
-        w = Workload(name, args)
+        try:
+            w = Workload(name, args)
+        except SkipWorkload as e:
+            if len(names) == 1:
+                sys.exit(str(e))
+            print(e, file=sys.stderr, flush=True)
+            continue
         w.warm_up()
         graphs += timed_graphs(w, args)
         loads.append(w)
@@ -539,7 +552,13 @@ def run_ab(names, args):
     spec = parse_ab(args.ab)
     reps = max(5, args.reps)
     for name in names:
-        w = Workload(name, args, tunings=({}, spec))
+        try:
+            w = Workload(name, args, tunings=({}, spec))
+        except SkipWorkload as e:
+            if len(names) == 1:
+                sys.exit(str(e))
+            print(e, file=sys.stderr, flush=True)
+            continue
         w.warm_up()
         base = gd.gqa_decode_get_tuning().as_dict()
         plan_a = w.plan()

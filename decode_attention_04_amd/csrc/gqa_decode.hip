@@ -2294,10 +2294,39 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
     if (page_size > 0) {
         while (page_size % tt != 0) tt /= 2;  // a tile never straddles a page (tt >= 16)
     }
-    const int tiles_total = max_seq_len > 0 ? (max_seq_len + tt - 1) / tt : 1;
+    int tiles_total = max_seq_len > 0 ? (max_seq_len + tt - 1) / tt : 1;
     const int base = B > 0 ? B * Hkv : 1;
     const bool want_fixed = t.partition == 1;
     const bool want_even = t.partition == 2;
+
+    // Small jobs: one 16-key tile per wave in fixed splits.  `most16` is the
+    // split count that gives every wave one 16-key tile at full length.
+    //  - A batch whose splits so cut take at most four workgroups per CU runs
+    //    them instead of even shares: the share walk needs the lengths before
+    //    its first tile load (a dependent round trip) and runs the multi-tile
+    //    loop, which a small job cannot amortise (us per call, fixed vs even:
+    //    2 x 4 kv heads x 1024 keys 6.96 vs 10.32; 8 x 1 x 512 7.31 vs 11.46;
+    //    4 x 8 x 1024 8.91 vs 12.55; ragged 8 x 8 x 1..1024 12.96 vs 13.54;
+    //    past four per CU the even shares win on ragged batches: 16 x 8 x
+    //    1..1024 18.72 vs 15.92).
+    //  - Where the default tile is longer (head_dim 32 and 64), a fixed plan
+    //    within half the device takes 16-key tiles, twice the workgroups
+    //    (512 keys on two kv heads at head_dim 64: 5.29 vs 5.74; 4096 keys at
+    //    head_dim 32: 5.39 vs 5.95).
+    const bool auto_tile = t.tile_tokens == 0 && !dbuf;
+    const int64_t most16 = max_seq_len > 0 ? ((int64_t)(max_seq_len + 15) / 16 + kWaves - 1) / kWaves : 0;
+    bool small_fixed = false;
+    if (auto_tile && num_splits == 0 && t.partition == 0 && B > 1 && tiles_total > 4 * kWaves && most16 >= 2 &&
+        (int64_t)base * most16 <= 4 * (int64_t)cu_count) {
+        small_fixed = true;
+    }
+    const bool fixed_by_shape = !(tiles_total > 4 * kWaves && (B > 1 || want_even));
+    if (auto_tile && num_splits == 0 && tt > 16 && most16 >= 2 &&
+        (small_fixed || (fixed_by_shape && (int64_t)base * most16 <= cu_count / 2))) {
+        tt = 16;
+        tiles_total = (max_seq_len + tt - 1) / tt;
+        small_fixed = true;  // one tile per wave (the doubled tile count must not turn a batch to shares)
+    }
     plan->tile_tokens = tt;
     plan->waves = kWaves;
     plan->pv_mode = t.pv_mode;
@@ -2317,7 +2346,7 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
     // workgroup (<= 4 tiles per wave) is written directly instead.
     // A single sequence cannot be ragged: fixed splits give it the same work
     // split without the device-side length scan.
-    if (num_splits == 0 && !want_fixed && tiles_total > 4 * kWaves && (B > 1 || want_even)) {
+    if (num_splits == 0 && !want_fixed && !small_fixed && tiles_total > 4 * kWaves && (B > 1 || want_even)) {
         const int64_t tiles_max = (int64_t)base * tiles_total;
         int64_t P = t.shares > 0 ? t.shares : (B > 1 ? 2 * cu_count : cu_count);
         if (P > (tiles_max + kWaves - 1) / kWaves) P = (tiles_max + kWaves - 1) / kWaves;
@@ -2349,7 +2378,9 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
     // gets a single split.
     const int kMaxSplitTokens = t.split_keys > 0 ? t.split_keys : kDefaultSplitKeys;
     int S = num_splits;
-    if (S == 0) {
+    if (S == 0 && small_fixed) {
+        S = (int)most16;  // one tile per wave
+    } else if (S == 0) {
         const int fill = (cu_count + base - 1) / base;
         const int len_cap = (max_seq_len + kMaxSplitTokens - 1) / kMaxSplitTokens;
         S = fill > len_cap ? fill : len_cap;

@@ -131,14 +131,14 @@ def test_fused_even_matches_combine_bitwise(tune, i):
     case = _even_cases()[i]
     say(f"[fold] even bitwise {case.name}")
     dc = DeviceCase(case)
+    tune(fold=2, partition=2)
     ws = workspace_for(case)
-    tune(fold=2)
     plan_fn = gd.gqa_decode_plan_fp8 if case.kv == "fp8" else gd.gqa_decode_plan
     plan = plan_fn(case.B, case.M * case.Hq, case.Hkv, case.D, case.capacity, case.page_size)
     assert plan.partition == 1 and plan.fused == 1 and plan.max_pieces <= 16
     one = run_with(dc, ws)
     assert counters_zero(ws)
-    tune(fold=1)
+    tune(fold=1, partition=2)
     two = run_with(dc, ws)
     compare(one, oracle_out(case), f"fused even {case.name}")
     assert np.array_equal(one.view(np.uint32), two.view(np.uint32))
@@ -148,7 +148,7 @@ def test_fused_even_matches_combine_bitwise(tune, i):
 def test_empty_sequences_write_zero_rows(tune, fold):
     """No piece covers a sequence of length 0; its output rows are still written (zeros) over an
     output buffer that held NaN, also for sequences past the launched workgroups' count."""
-    tune(fold=fold, shares=3)
+    tune(fold=fold, shares=3, partition=2)
     lens = [0, 2000, 0, 0, 1500, 0, 33, 0]
     case = W.contig_case(len(lens), 16, 4, 128, 2048, seq_lens=lens, seed=88)
     dc = DeviceCase(case)
@@ -195,7 +195,7 @@ def test_more_shares_than_positions(tune, kv, shares, fold):
     """More shares than positions on the tile axis: some shares hold no tile and write no
     partial, and the fold (combine kernel or in-kernel) skips their slots, with a different
     segment in each lane of the combine's waves."""
-    tune(shares=shares, fold=fold)
+    tune(shares=shares, fold=fold, partition=2)
     lens = [0, 0, 205, 0, 175]
     make = W.fp8_contig_case if kv == "fp8" else W.contig_case
     case = make(5, 8, 4, 64, 1240, seq_lens=lens, seed=9080)

@@ -157,7 +157,7 @@ def test_fp8_even_shares(tune):
     ref = oracle_out(case)
     for shares in ("1", "7", "64", "1000"):
         for fold in (1, 2):
-            tune(shares=int(shares), fold=fold)
+            tune(shares=int(shares), fold=fold, partition=2)
             compare(dc.run_host(), ref, f"fp8 even shares={shares} fold={fold}")
 
 

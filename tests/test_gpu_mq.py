@@ -102,7 +102,7 @@ def test_mq_even_shares(tune):
     ref = oracle_out(case)
     for shares in ("1", "7", "64", "1000"):
         for fold in (1, 2):
-            tune(shares=int(shares), fold=fold)
+            tune(shares=int(shares), fold=fold, partition=2)
             compare(dc.run_host(), ref, f"mq even shares={shares} fold={fold}")
 
 

@@ -215,7 +215,7 @@ def test_paged_matrix(ps, D):
         compare(dc.run_host(splits), ref, f"paged ps={ps} D={D} splits={splits}")
 
 
-def test_paged_equals_contiguous_bitwise():
+def test_paged_equals_contiguous_bitwise(tune):
     """Pages holding the same rows as a contiguous cache give the same bits (same plan)."""
     say("[parity] paged == contiguous")
     B, Hq, Hkv, D, ps, S = 3, 32, 8, 128, 32, 1024
@@ -231,11 +231,16 @@ def test_paged_equals_contiguous_bitwise():
             v_pool[pg] = c.v[b, :, i * ps:(i + 1) * ps]
             table[b, i] = pg
     p = W.Case("paged_copy", B, Hq, Hkv, D, c.scale, c.q, k_pool, v_pool, c.seq_lens, table, ps)
-    # even shares; fixed splits of several tiles; one tile per wave (64 splits of 16 keys)
+    # the plan's one-tile-per-wave splits (a small job); fixed splits of several tiles; one tile
+    # per wave (64 splits of 16 keys); then even shares
     for splits in (0, 7, 64):
         a = DeviceCase(c).run_host(splits)
         b = DeviceCase(p).run_host(splits)
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"splits={splits}"
+    tune(partition=2)
+    a = DeviceCase(c).run_host()
+    b = DeviceCase(p).run_host()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "even shares"
 
 
 def test_paged_page_permutation_bitwise():
@@ -389,10 +394,10 @@ EVEN_LENS = {
 @pytest.mark.parametrize("fold", [1, 2], ids=["kernel", "fused"])
 def test_even_shares_contiguous(tune, lens, shares, fold):
     """Equal shares of the concatenated tiles, any share count, ragged and empty sequences
-    (a capacity of at least 1024 keys keeps every case on even shares, short ones included),
-    folded by the combine kernel and in the split kernel."""
+    (the even partition asked for, with a capacity of at least 1024 keys so that short cases
+    take it too), folded by the combine kernel and in the split kernel."""
     say(f"[parity] even shares={shares} lens={lens} fold={fold}")
-    tune(shares=int(shares), fold=fold)
+    tune(shares=int(shares), fold=fold, partition=2)
     L = EVEN_LENS[lens]
     S_max = max(max(L), 1024)
     case = W.contig_case(len(L), 16, 4, 128, S_max, seq_lens=L, seed=60, tail="nan")
@@ -411,8 +416,7 @@ def test_even_shares_contiguous(tune, lens, shares, fold):
 @pytest.mark.parametrize("D", [32, 64, 128, 256])
 def test_even_shares_paged(tune, shares, D):
     say(f"[parity] even shares paged D={D} shares={shares}")
-    if shares != "0":
-        tune(shares=int(shares))
+    tune(shares=int(shares), partition=2)
     L = [1, 0, 900, 31, 2000, 16, 0, 1500]
     case = W.paged_case(len(L), 8, 2, D, 32, 250, seq_lens=L, max_len=2048, seed=61 + D)
     assert gd.gqa_decode_plan(case.B, 8, 2, D, 2048, 32).partition == 1

@@ -2,7 +2,7 @@
 
 Each case draws the cache kind (contiguous / paged, bf16 / E4M3, one or several query tokens),
 head_dim, group size, kv heads, batch, ragged lengths (zeros included), page size, the split
-count, for some cases the even-share count, and where the partials are folded (by the plan's
+count, for some cases the even partition with a share count, and where the partials are folded (by the plan's
 default, in a combine kernel, or in the split kernel itself), so that the plan's branches (fixed or
 even partition, one-tile or key-range workgroups, direct or combined, packed or plain PV columns,
 one launch or two) are crossed with each other rather than one at a time.  Tolerance as everywhere:
@@ -82,7 +82,8 @@ def build(c: dict) -> W.Case:
 def test_random_case(tune, i):
     c = draw(i)
     say(f"[random] {i}: {c}")
-    tune(shares=int(c["shares"] or 0), fold=c["fold"])
+    # a case that names a share count asks for the even partition (small jobs plan fixed splits)
+    tune(shares=int(c["shares"] or 0), fold=c["fold"], partition=2 if c["shares"] is not None else 0)
     case = build(c)
     dc = DeviceCase(case)
     got = dc.run_host(c["splits"])

@@ -129,11 +129,43 @@ def test_plan_fills_the_device():
     assert p.grid == 256 and p.split_tokens == 4 * p.tile_tokens
     # a short cache: one tile per wave over several workgroups where the device has room, the
     # few small partials folded in the split kernel; direct (one workgroup) when it has none
+    # (16-key tiles at head_dim 64 there: twice the workgroups)
     p = gd.gqa_decode_plan(1, 8, 2, 64, 512, 0, 0, 256)
-    assert p.partition == 0 and p.num_splits == 4 and p.split_tokens == 4 * p.tile_tokens
-    assert p.fused == 1 and p.fold_fanin == 4 and p.counters == 2
+    assert p.partition == 0 and p.tile_tokens == 16 and p.num_splits == 8
+    assert p.split_tokens == 4 * p.tile_tokens
+    assert p.fused == 1 and p.fold_fanin == 8 and p.counters == 2
     p = gd.gqa_decode_plan(64, 32, 8, 128, 256, 0, 0, 256)
     assert p.partition == 0 and p.direct == 1 and p.workspace_bytes == 0
+    # with the tile fixed by the tuning, head_dim 64 keeps its 32-key tile
+    with gd.tuning(tile_tokens=32):
+        p = gd.gqa_decode_plan(1, 8, 2, 64, 512, 0, 0, 256)
+    assert p.tile_tokens == 32 and p.num_splits == 4
+
+
+def test_small_batches_take_fixed_splits():
+    """A batch whose one-16-key-tile-per-wave splits take at most four workgroups per CU runs
+    them (fixed splits) instead of even shares; past that, and when the tuning asks for even
+    shares, the shares stay."""
+    for args, splits in (((2, 16, 4, 128, 1024), 16), ((8, 8, 1, 128, 512), 8), ((4, 32, 8, 128, 1024), 16),
+                         ((3, 8, 2, 64, 700), 11), ((4, 24, 4, 256, 2048), 32)):
+        p = gd.gqa_decode_plan(*args, 0, 0, 256)
+        assert p.partition == 0 and p.tile_tokens == 16 and p.num_splits == splits, args
+        assert p.split_tokens == 64 and p.grid == args[0] * args[2] * splits
+        pp = gd.gqa_decode_plan(*args, 32, 0, 256)          # paged: the same rule
+        assert pp.partition == 0 and pp.num_splits == splits
+        pf = gd.gqa_decode_plan_fp8(*args, 32, 0, 256)      # E4M3 (32-key paged tiles otherwise)
+        assert pf.partition == 0 and pf.tile_tokens == 16 and pf.num_splits == splits
+        with gd.tuning(partition=2):
+            assert gd.gqa_decode_plan(*args, 0, 0, 256).partition == 1
+    # a short batch at head_dim 64 (32-key tiles by default): 16-key tiles, still fixed splits
+    p = gd.gqa_decode_plan(2, 16, 4, 64, 512, 0, 0, 256)
+    assert p.partition == 0 and p.tile_tokens == 16 and p.num_splits == 8
+    p = gd.gqa_decode_plan_fp8(8, 8, 1, 128, 512, 32, 0, 256)
+    assert p.partition == 0 and p.tile_tokens == 16 and p.num_splits == 8
+    for args in ((16, 32, 8, 128, 1024), (16, 16, 4, 128, 4096), (32, 32, 8, 128, 8192)):
+        assert gd.gqa_decode_plan(*args, 0, 0, 256).partition == 1, args
+    # fewer CUs: the same job no longer fits four per CU
+    assert gd.gqa_decode_plan(4, 32, 8, 128, 1024, 0, 0, 64).partition == 1
 
 
 def test_forced_splits_are_clamped_to_tiles():
@@ -304,12 +336,14 @@ def test_mq_workspace_is_the_plan_of_m_times_hq_rows():
 @pytest.mark.parametrize("splits", [0, 3])
 def test_fp8_plan_tiles_and_workspace_bound(shape, splits):
     """The E4M3 plan takes 32-key tiles for a paged head_dim-128 cache (when the page holds
-    them) and 16 otherwise as bf16 does; its workspace never exceeds the bf16 plan's, which is
-    what gqa_decode_workspace_bytes reports for both."""
+    them; a small job's one-tile-per-wave splits take 16 there too) and 16 otherwise as bf16
+    does; its workspace never exceeds the bf16 plan's, which is what gqa_decode_workspace_bytes
+    reports for both."""
     B, Hq, Hkv, D, cap, ps = shape
     p16 = gd.gqa_decode_plan(B, Hq, Hkv, D, cap, ps, splits, 256)
     p8 = gd.gqa_decode_plan_fp8(B, Hq, Hkv, D, cap, ps, splits, 256)
-    if ps > 0 and D == 128 and ps % 32 == 0:
+    small = splits == 0 and p16.partition == 0 and p16.split_tokens == 4 * p16.tile_tokens == 64
+    if ps > 0 and D == 128 and ps % 32 == 0 and not small:
         assert p8.tile_tokens == 32
     else:
         assert p8.tile_tokens == p16.tile_tokens
