@@ -14,9 +14,10 @@
 //                      fold the partials of each (b, h) with the log-sum-exp
 //                      rescale in a fixed order (a tree for many partials, one
 //                      thread per column for few).
-//   With the tuning's in-kernel fold, the split workgroup that writes the last
-//   partial of a group (an arrival ticket tells it) folds the group itself and
-//   the combine kernel is not launched.
+//   With the in-kernel fold (the default where a segment's fixed splits make
+//   one small fold, a tuning choice elsewhere), the split workgroup that writes
+//   the last partial of a group (an arrival ticket tells it) folds the group
+//   itself and the combine kernel is not launched.
 //
 // The default pipeline inside one wave (64 lanes, r = lane % 16, grp = lane / 16):
 //
