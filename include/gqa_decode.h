@@ -141,11 +141,13 @@ gqa_status_t gqa_decode_set_tuning(const gqa_tuning_t *tuning);
  * log: fill the device, bounded by the tile count).  max_seq_len is the cache
  * capacity (contiguous S_max, or max_pages * page_size when paged);
  * page_size = 0 means a contiguous cache.  num_splits = 0 picks the layout
- * from cu_count: by default even shares (the concatenated tiles of all
- * sequences cut into equal parts on the device, from seq_lens), or a single
- * direct split for short caches; num_splits > 0 forces that many fixed splits
- * per (sequence, kv head) (clamped to the tile count).  Pure host code: needs
- * no GPU.
+ * from the shapes and cu_count: one sequence takes fixed splits (about one
+ * workgroup per CU); a batch takes even shares (the concatenated tiles of all
+ * sequences cut into equal parts on the device, from seq_lens), unless its
+ * splits of one 16-key tile per wave take at most four workgroups per CU, in
+ * which case it takes those fixed splits; a short cache may take a single
+ * direct split.  num_splits > 0 forces that many fixed splits per (sequence,
+ * kv head) (clamped to the tile count).  Pure host code: needs no GPU.
  */
 gqa_status_t gqa_decode_plan(int B, int Hq, int Hkv, int head_dim, int max_seq_len, int page_size,
                              int num_splits, int cu_count, gqa_plan_t *plan);
