@@ -472,6 +472,39 @@ def test_cache_policy_variants(tune, nt):
     compare(out, oracle_out(case), f"nt={nt}")
 
 
+# ------------------------------------------------------------------ small jobs: fixed splits of one 16-key tile per wave
+def _small_job_cases():
+    return [
+        W.contig_case(2, 16, 4, 128, 1024, seq_lens=[1024, 333], seed=160, tail="nan"),
+        W.contig_case(3, 8, 2, 64, 700, seq_lens=[700, 300, 5], seed=161, tail="nan"),
+        W.contig_case(8, 8, 1, 256, 512, seq_lens=[512, 0, 1, 17, 500, 64, 65, 333], seed=162, scale=1 / 16),
+        W.contig_case(8, 32, 8, 128, 1024, seq_lens=[1024, 3, 0, 999, 512, 1000, 64, 777], seed=163),   # 1024 workgroups
+        W.contig_case(2, 8, 2, 32, 4096, seq_lens=[4096, 4000], seed=164),
+        W.paged_case(4, 8, 2, 128, 32, 100, seq_lens=[1024, 300, 700, 9], max_len=1024, seed=165),
+        W.paged_case(2, 32, 8, 64, 16, 80, seq_lens=[512, 400], max_len=512, seed=166),
+        W.fp8_contig_case(2, 16, 4, 128, 1024, seq_lens=[1024, 77], seed=167),
+        W.fp8_paged_case(4, 8, 2, 128, 32, 100, seq_lens=[1024, 300, 700, 9], max_len=1024, seed=168),
+        W.mq_case(3, 4, 16, 4, 128, 1024, seq_lens=[1024, 4, 600], seed=169, tail="nan"),
+        W.mq_paged_case(2, 2, 16, 4, 128, 32, 80, [1000, 33], max_len=1024, seed=170),
+    ]
+
+
+@pytest.mark.parametrize("i", range(11))
+def test_small_job_plans(i):
+    """Batches small enough that one 16-key tile per wave in fixed splits takes at most four
+    workgroups per CU (contiguous, paged, E4M3, multi-query; ragged lengths, zeros, NaN tails):
+    the plan is those splits, the result matches the oracle and is bit-exact across runs."""
+    case = _small_job_cases()[i]
+    say(f"[parity] small job {case.name} B={case.B} Hkv={case.Hkv} D={case.D} cap={case.capacity}")
+    plan_fn = gd.gqa_decode_plan_fp8 if case.kv == "fp8" else gd.gqa_decode_plan
+    p = plan_fn(case.B, case.M * case.Hq, case.Hkv, case.D, case.capacity, case.page_size)
+    assert p.partition == 0 and p.tile_tokens == 16 and p.split_tokens == 64, p.as_dict()
+    dc = DeviceCase(case)
+    a = dc.run_host()
+    compare(a, oracle_out(case), f"small job {case.name}")
+    assert np.array_equal(np.ascontiguousarray(a).view(np.uint32), np.ascontiguousarray(dc.run_host()).view(np.uint32))
+
+
 # ------------------------------------------------------------------ tile size and register buffering (A/B variants)
 @pytest.mark.parametrize("dbuf", [0, 1])
 @pytest.mark.parametrize("tile", [16, 32, 64])
