@@ -671,7 +671,7 @@ def main():
         summarize_pmc(*args.summarize_pmc, args.workload or W.HEADLINE)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         sys.exit(2)
     import torch
