@@ -23,8 +23,10 @@
  *     aligned.  bf16 tensors are passed as raw 16-bit patterns (E4M3 caches
  *     as raw bytes, see gqa_decode_fp8).
  *   - Calls only enqueue work on `stream` (0 = the null stream): they never
- *     synchronise, never allocate and keep no state besides a cached CU count
- *     per device.  Outputs are ready when the stream reaches them.
+ *     synchronise and never allocate.  The library keeps no state besides a
+ *     cached CU count per device, the process-wide tuning (gqa_tuning_t) and
+ *     the static scratch array of gqa_decode_noalloc.  Outputs are ready when
+ *     the stream reaches them.
  *   - Every argument check runs on the host before any launch; a rejected call
  *     launches nothing and returns the status below.  A failed launch returns
  *     GQA_ERR_HIP.  Nothing throws across this interface.
@@ -213,8 +215,8 @@ gqa_status_t gqa_paged_decode(const void *q, const void *k_pool, const void *v_p
  * unnormalised (m, l, acc) partials in `workspace` (when the plan is direct
  * it writes `out` instead).  gqa_decode_combine then folds those partials
  * into `out` (it launches nothing for a direct plan); its seq_lens, shape
- * arguments, num_splits and the environment must be those of the partials
- * call, so that both compute the same plan (max_seq_len = S_max and
+ * arguments, num_splits and the tuning (gqa_tuning_t) must be those of the
+ * partials call, so that both compute the same plan (max_seq_len = S_max and
  * page_size = 0 for a contiguous cache).  Running the two on one stream gives bit-for-bit the
  * result of the one-call entry point.
  */
@@ -282,7 +284,8 @@ gqa_status_t gqa_paged_decode_fp8_partials(const void *q, const void *k_pool, co
  * rules), and the combine of gqa_decode_fp8_partials /
  * gqa_paged_decode_fp8_partials (gqa_decode_combine's arguments and rules).
  * A paged E4M3 cache at head_dim 128 takes 32-key tiles where bf16 takes 16,
- * so that a wave still reads 4 KB of K and of V in one piece of a page; the
+ * so that a wave still reads 4 KB of K and of V in one piece of a page
+ * (except small jobs, whose one-tile-per-wave splits take 16 for both); the
  * plan therefore depends on the element type, and the combine must recompute
  * the plan of the partials call.  The workspace a bf16 call of the same
  * shapes needs (gqa_decode_workspace_bytes) is always enough: longer tiles
@@ -331,7 +334,8 @@ gqa_status_t gqa_paged_decode_mq(const void *q, const void *k_pool, const void *
  * arguments without workspace / workspace_bytes, same results bit for bit).
  * A call whose plan needs more than 4 MiB of scratch
  * (gqa_decode_workspace_bytes) launches nothing and returns GQA_ERR_TOO_LARGE;
- * the five reference workloads need at most ~2.4 MB.  Every call on a GPU
+ * a batch of 16 sequences x 4 kv heads x 16384 keys at head_dim 128 needs
+ * ~2.4 MB, a GQA-6 head_dim-256 layer of 4096 keys ~1.6 MB.  Every call on a GPU
  * shares that GPU's array and its contents: calls that overlap on one GPU
  * (on different streams, or from different threads without ordering) race.
  */
