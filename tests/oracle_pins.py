@@ -307,6 +307,18 @@ def pin_fp8_values(lib):
     assert np.array_equal(half[:0x7F], pos * 0.5), "v_scale must multiply V"
 
 
+def pin_fp8_values_match_torch(lib):
+    """Every E4M3 byte the oracle dequantises against torch's float8_e4m3fn decode (a library
+    implementation of the same OCP format: bias 7, subnormals at exponent 0, 0x7F / 0xFF NaN,
+    no infinities)."""
+    import torch
+    val = _fp8_values(lib)
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    finite = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(val), ~finite), "NaN bytes differ from float8_e4m3fn"
+    assert np.array_equal(val[finite], ref[finite]), "E4M3 values differ from float8_e4m3fn"
+
+
 def _fp8_as_bf16(lib, case: W.Case) -> W.Case:
     """The same call with K and V dequantised (power-of-two scales: exact in bf16)."""
     table = _fp8_values(lib)
@@ -364,6 +376,33 @@ def pin_mq_rows_are_single_query_calls(lib):
             assert np.array_equal(got[b, i], ref[0]), f"paged mq row b={b} i={i}"
 
 
+def pin_mq_torch_sdpa(lib):
+    """Multi-query calls against torch scaled_dot_product_attention (CPU, float64) with a boolean
+    mask holding the causal limit: query i of sequence b sees keys t <= len - M + i.  Rows with
+    no visible key are zero in the oracle (SDPA leaves them undefined), checked apart."""
+    for c in (W.mq_case(2, 4, 8, 2, 64, 40, seq_lens=[40, 9], seed=78),
+              W.mq_case(1, 3, 6, 1, 128, 25, seq_lens=[25], seed=79, scale=0.2),
+              W.mq_case(2, 5, 4, 4, 32, 12, seq_lens=[12, 2], seed=80)):
+        got = oracle.decode_mq(c.q, c.k, c.v, c.seq_lens, c.scale, lib=lib)
+        q = torch.from_numpy(W.bf16_bits_to_f32(c.q).reshape(c.q.shape).astype(np.float64))
+        k = torch.from_numpy(W.bf16_bits_to_f32(c.k).reshape(c.k.shape).astype(np.float64))
+        v = torch.from_numpy(W.bf16_bits_to_f32(c.v).reshape(c.v.shape).astype(np.float64))
+        for b in range(c.B):
+            n = int(c.seq_lens[b])
+            limit = np.array([n - c.M + i + 1 for i in range(c.M)])   # keys visible to query i
+            seen = limit > 0
+            assert np.all(got[b][~seen] == 0), f"mq rows without keys must be zero (b={b})"
+            if not seen.any():
+                continue
+            kb = k[b, :, :n].repeat_interleave(c.G, dim=0)[None]        # [1, Hq, n, D]
+            vb = v[b, :, :n].repeat_interleave(c.G, dim=0)[None]
+            qb = q[b].permute(1, 0, 2)[None]                             # [1, Hq, M, D]
+            mask = torch.from_numpy(np.arange(n)[None, :] < limit[:, None])  # [M, n]
+            o = torch.nn.functional.scaled_dot_product_attention(qb, kb, vb, attn_mask=mask, scale=c.scale)
+            ref = o[0].permute(1, 0, 2).numpy()                          # [M, Hq, D]
+            _close(got[b][seen], ref[seen], what=f"mq sdpa b={b} M={c.M} G={c.G} D={c.D}")
+
+
 def pin_mq_future_keys_ignored(lib):
     """Changing the keys and values a query may not see (positions > len - M + i) leaves its
     row unchanged, and M = 1 is the single-query call."""
@@ -384,6 +423,8 @@ ALL_PINS = [
     pin_golden_closed_forms, pin_torch_sdpa, pin_brute_force, pin_len_one_is_v0,
     pin_uniform_weights_give_mean, pin_dominant_key, pin_scale_moves_into_q, pin_v_is_linear,
     pin_token_permutation, pin_head_mapping, pin_nan_tail_ignored, pin_split_invariance,
-    pin_paged_equals_gathered, pin_page_permutation, pin_fp8_values, pin_fp8_matches_bf16,
-    pin_fp8_split_invariance, pin_mq_rows_are_single_query_calls, pin_mq_future_keys_ignored,
+    pin_paged_equals_gathered, pin_page_permutation, pin_fp8_values, pin_fp8_values_match_torch,
+    pin_fp8_matches_bf16,
+    pin_fp8_split_invariance, pin_mq_rows_are_single_query_calls, pin_mq_torch_sdpa,
+    pin_mq_future_keys_ignored,
 ]
