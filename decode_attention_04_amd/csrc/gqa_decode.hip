@@ -2359,7 +2359,14 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
         plan->grid = B > 0 ? (int)P : 0;
         plan->direct = 0;
         plan->slots = (int64_t)P + base;
-        plan->max_pieces = (int)std::min<int64_t>(P, (int64_t)tiles_total * P / tiles_max + 1);
+        // Pieces of one segment with every sequence at full length: its tiles
+        // span positions of shares of about N / P positions (N = the segments'
+        // tiles plus K each), so at most floor((tiles - 1) * P / N) + 2 shares.
+        // Shorter sequences elsewhere make shares shorter and can give a
+        // segment more pieces; the combine walks them all either way.
+        const int64_t N_full = (int64_t)base * (tiles_total + (t.piece_cost >= 0 ? t.piece_cost : 0));
+        plan->max_pieces =
+            (int)std::min<int64_t>(std::min<int64_t>(P, tiles_total), ((int64_t)(tiles_total - 1) * P) / N_full + 2);
         // In-kernel fold: one counter per (sequence, kv head); every segment's
         // few pieces are folded by the share that finishes last among them.
         // Not for segments of many pieces (one workgroup would read them all).

@@ -73,7 +73,8 @@ typedef struct gqa_plan {
     int waves;              /* waves (of 64 lanes) per workgroup */
     int grid;               /* workgroups of the split kernel: B * Hkv * S, or the shares */
     int direct;             /* 1: S == 1, the split kernel writes `out` itself */
-    int max_pieces;         /* most partials one (sequence, kv head) can have */
+    int max_pieces;         /* most partials one (sequence, kv head) has with every sequence at full
+                               length (even shares: shorter sequences elsewhere can give more) */
     int64_t slots;          /* partial blocks in the workspace: B*Hkv*S, or shares + B*Hkv */
     int pv_mode;            /* PV contraction: 1 = bf16 MFMA with P split hi+lo, 0 = fp32 MFMA */
     int double_buffer;      /* 1: two tile buffers per wave; 0: one, refilled part by part */

@@ -472,6 +472,40 @@ def test_cache_policy_variants(tune, nt):
     compare(out, oracle_out(case), f"nt={nt}")
 
 
+# ------------------------------------------------------------------ very large batches
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+def test_very_large_batch(paged):
+    """Thousands of short ragged sequences (zeros included): the even shares' length scan runs
+    over dozens of 64-sequence chunks before a share knows its first segment."""
+    rng = np.random.default_rng(180 + paged)
+    B = 1000 if paged else 2000
+    lens = rng.integers(0, 301, B)
+    lens[rng.random(B) < 0.1] = 0
+    say(f"[parity] very large batch B={B} paged={paged}")
+    if paged:
+        case = W.paged_case(B, 8, 2, 128, 32, int(sum((n + 31) // 32 for n in lens)) + 5, seq_lens=lens,
+                            max_len=512, seed=182)
+    else:
+        case = W.contig_case(B, 8, 2, 128, 512, seq_lens=lens, seed=183, tail="nan")
+    p = gd.gqa_decode_plan(case.B, case.Hq, case.Hkv, case.D, case.capacity, case.page_size)
+    assert p.partition == 1, p.as_dict()
+    dc = DeviceCase(case)
+    a = dc.run_host()
+    compare(a, oracle_out(case), f"very large batch B={B} paged={paged}")
+    assert np.array_equal(a.view(np.uint32), dc.run_host().view(np.uint32))
+    assert np.all(a[lens == 0] == 0)
+
+
+def test_multi_head_attention_shape():
+    """G = 1 (16 kv heads, one query head each) over fixed splits and even shares."""
+    say("[parity] G = 1")
+    case = W.contig_case(5, 16, 16, 128, 3000, seq_lens=[3000, 1, 0, 1777, 2999], seed=184, tail="nan")
+    dc = DeviceCase(case)
+    ref = oracle_out(case)
+    for splits in (0, 1, 9):
+        compare(dc.run_host(splits), ref, f"G=1 splits={splits}")
+
+
 # ------------------------------------------------------------------ small jobs: fixed splits of one 16-key tile per wave
 def _small_job_cases():
     return [
