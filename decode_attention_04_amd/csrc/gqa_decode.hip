@@ -2041,7 +2041,7 @@ WorkspaceLayout workspace_layout(int Hq, int Hkv, int D, int64_t slots) {
 // 107.6 vs 111.3, uniform 16k batch 83.0 vs 82.6 -- but 512 keys on two kv
 // heads in 4 splits 6.18 vs 5.61 (2, 4 and 8 splits all favour one launch).
 // So fixed splits fold in the kernel when the whole fold is one small node
-// (at most kNarrowPieces partials of at most kSmallFoldBytes per segment),
+// (at most kNarrowPieces partials, kSmallFoldBytes in all, per segment),
 // and everything else folds in a combine kernel.
 constexpr bool kFuseEvenByDefault = false;
 constexpr int64_t kSmallFoldBytes = 16 << 10;
