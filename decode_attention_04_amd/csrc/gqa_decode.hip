@@ -75,6 +75,9 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;           // waves per workgroup
 constexpr int kPartitionFixed = 0;  // see "work partition" below
 constexpr int kPartitionEven = 1;
+// Proportional splits (a plan partition): run by the even-partition kernels
+// with SplitArgs::prop / CombineArgs::prop set.
+constexpr int kPartitionProp = 2;
 constexpr int kMaxHeadsPerKv = 16;  // G is padded to the MFMA's 16 columns
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords (gfx9 family)
 
@@ -104,6 +107,7 @@ struct SplitArgs {
     unsigned *counters;         // in-kernel fold: the arrival counters (workspace header)
     int fused;                  // 1: this kernel folds the partials itself
     int fanin;                  // fused fixed splits: partials per node of the fold tree
+    int prop;                   // even-partition kernel: proportional splits instead of shares
 };
 
 struct CombineArgs {
@@ -117,6 +121,7 @@ struct CombineArgs {
     int M, Gh;                // query tokens per sequence, query heads per kv head (G = M * Gh)
     int piece_cost;           // even partition: as in SplitArgs
     int halve_long;           // as in SplitArgs
+    int prop;                 // proportional splits (thread-per-column combine only)
 };
 
 __device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
@@ -730,6 +735,81 @@ __device__ __forceinline__ long long share_begin(long long w, long long N, long 
 // Largest workgroup whose share starts at or before tile x (the one holding x).
 __device__ __forceinline__ long long share_of(long long x, long long N, long long P) {
     return ((x + 1) * P + N - 1) / N - 1;
+}
+
+// Proportional splits: with N tiles in all segments and P workgroups (halved,
+// as for even shares, when contiguous segments are long), every workgroup
+// takes at most L = ceil(N / P) tiles: a segment of n tiles gets
+// k = ceil(n / L) splits of n / k tiles (rounded down at each split start), so
+// each workgroup holds exactly one piece.  Workgroups are numbered segment by
+// segment in (sequence, kv head) order; the ones past the last split exit.
+// Every lane of the wave returns the same values.
+struct PropTotals {
+    long long N;  // tiles of all segments
+    int L;        // most tiles per workgroup
+};
+
+__device__ __forceinline__ PropTotals prop_totals(const int32_t *seq_lens, int B, int Hkv, int cap, int TT, long long P0,
+                                                  int halve_long, int lane) {
+    long long tiles = 0, nonempty = 0;
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        const int bb = c0 + lane;
+        const int n = bb < B ? (clamp_len(seq_lens, bb, cap) + TT - 1) / TT : 0;
+        tiles += wave_sum(n);
+        nonempty += wave_sum(n > 0 ? 1 : 0);
+    }
+    const long long N = uniform64(tiles * Hkv), segs = uniform64(nonempty * Hkv);
+    const long long P = shares_for(P0, N, segs, 0, halve_long);
+    return PropTotals{N, N > 0 ? (int)((N + P - 1) / P) : 1};
+}
+
+// The piece of workgroup w: sequence b (< 0: none), kv head, split j of k, the
+// sequence's (clamped) length.
+struct PropPiece {
+    int b, kvh, j, k, len;
+};
+
+__device__ __forceinline__ PropPiece prop_locate(const int32_t *seq_lens, int B, int Hkv, int cap, int TT, int L,
+                                                 long long w, int lane) {
+    PropPiece p{-1, 0, 0, 1, 0};
+    long long run = 0;  // workgroups of the sequences before this chunk
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        const int bb = c0 + lane;
+        const int ln = bb < B ? clamp_len(seq_lens, bb, cap) : 0;
+        const int k = ((ln + TT - 1) / TT + L - 1) / L;  // 0 for an empty sequence
+        const int cnt = k * Hkv;
+        const int incl = wave_scan(cnt, lane);
+        const unsigned long long hit = __ballot(bb < B && run + incl - cnt <= w && w < run + incl);
+        if (p.b < 0 && hit != 0ull) {
+            const int l = __builtin_ctzll(hit);
+            p.b = c0 + l;
+            p.k = __shfl(k, l, 64);
+            p.len = __shfl(ln, l, 64);
+            const long long r = w - (run + __shfl(incl - cnt, l, 64));
+            p.kvh = (int)(r / p.k);
+            p.j = (int)(r - (long long)p.kvh * p.k);
+        }
+        run += __shfl(incl, 63, 64);
+    }
+    p.b = __builtin_amdgcn_readfirstlane(p.b);
+    p.kvh = __builtin_amdgcn_readfirstlane(p.kvh);
+    p.j = __builtin_amdgcn_readfirstlane(p.j);
+    p.k = __builtin_amdgcn_readfirstlane(p.k);
+    p.len = __builtin_amdgcn_readfirstlane(p.len);
+    return p;
+}
+
+// The first workgroup (slot) of sequence b's segments and its split count k.
+__device__ __forceinline__ void prop_prefix(const int32_t *seq_lens, int B, int Hkv, int cap, int TT, int L, int b,
+                                            int lane, long long &before, int &k_b) {
+    long long pre = 0;
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        const int bb = c0 + lane;
+        const int k = bb < B ? ((clamp_len(seq_lens, bb, cap) + TT - 1) / TT + L - 1) / L : 0;
+        pre += wave_sum(bb < b ? k : 0);
+    }
+    before = uniform64(pre * Hkv);
+    k_b = __builtin_amdgcn_readfirstlane(((clamp_len(seq_lens, b, cap) + TT - 1) / TT + L - 1) / L);
 }
 
 // Q of the R = M * G query rows of kv head kvh of sequence b (row r = i * G + g:
@@ -1393,9 +1473,23 @@ void gqa_split_kernel(const int32_t *seq_lens, const unsigned char *k, const uns
     a.Hq = Hkv * a.G;
 
     if constexpr (PART == kPartitionEven) {
+        const int lane = threadIdx.x & 63;
+        if (args.prop) {
+            // Proportional splits: this workgroup's one piece (the partial goes
+            // to slot blockIdx.x; the combine kernel folds each segment's k).
+            const long long P0 = (long long)gridDim.x - (long long)a.B * a.Hkv;
+            const PropTotals tot = prop_totals(a.seq_lens, a.B, a.Hkv, cap, TT, P0, a.halve_long, lane);
+            const PropPiece pc = prop_locate(a.seq_lens, a.B, a.Hkv, cap, TT, tot.L, blockIdx.x, lane);
+            if (pc.b < 0) return;
+            const int n = (pc.len + TT - 1) / TT;
+            const int tb = (int)((long long)pc.j * n / pc.k);
+            const int te = (int)((long long)(pc.j + 1) * n / pc.k);
+            process_range<D, NB, PAGED, PV, DBUF, CPOL, KV, false, QKM>(a, lds, pc.b, pc.kvh, pc.len, tb * TT,
+                                                                        min(pc.len, te * TT), (size_t)blockIdx.x, false);
+            return;
+        }
         // This workgroup's equal share of the tile axis (each segment's tiles
         // plus K positions for its start and fold), walked piece by piece.
-        const int lane = threadIdx.x & 63;
         const int K = a.piece_cost;
         // In-kernel fold: no piece covers a sequence of length 0, so the
         // workgroups zero its output rows (sequences blockIdx.x, + grid, ...).
@@ -1853,6 +1947,14 @@ __global__ __launch_bounds__(kNarrowThreads) void gqa_combine_narrow_kernel(cons
     if constexpr (PART == kPartitionFixed) {
         S = a.num_splits;
         lo = bk * S;
+    } else if (a.prop) {
+        // proportional splits: sequence b's segments hold k consecutive slots each
+        const PropTotals tot = prop_totals(a.seq_lens, a.B, a.Hkv, a.cap, a.tile, a.shares, a.halve_long, lane);
+        long long before;
+        int k;
+        prop_prefix(a.seq_lens, a.B, a.Hkv, a.cap, a.tile, tot.L, b, lane, before, k);
+        S = k;
+        lo = (size_t)(before + (long long)(h / G) * k);
     } else {
         long long before, total;
         long long segs;
@@ -1920,7 +2022,7 @@ gqa_tuning_t default_tuning() {
 bool tuning_valid(const gqa_tuning_t &t) {
     auto in = [](int v, int lo, int hi) { return v >= lo && v <= hi; };
     return (t.tile_tokens == 0 || t.tile_tokens == 16 || t.tile_tokens == 32 || t.tile_tokens == 64) &&
-           in(t.double_buffer, 0, 1) && in(t.pv_mode, 0, 1) && in(t.streaming, 0, 1) && in(t.partition, 0, 2) &&
+           in(t.double_buffer, 0, 1) && in(t.pv_mode, 0, 1) && in(t.streaming, 0, 1) && in(t.partition, 0, 3) &&
            in(t.shares, 0, INT32_MAX / 2) && in(t.split_keys, 0, INT32_MAX) && in(t.piece_cost, 0, 1024) &&
            in(t.halve_long, 0, 1) && in(t.combine, 0, 1) &&
            (t.combine_cols == 0 || t.combine_cols == 2 || t.combine_cols == 4 || t.combine_cols == 8 ||
@@ -1951,6 +2053,7 @@ gqa_tuning_t tuning_from_env() {
     if (is("GQA_DECODE_NT", "0")) t.streaming = 0;
     if (is("GQA_DECODE_PARTITION", "fixed")) t.partition = 1;
     if (is("GQA_DECODE_PARTITION", "even")) t.partition = 2;
+    if (is("GQA_DECODE_PARTITION", "prop")) t.partition = 3;
     num("GQA_DECODE_SHARES", t.shares, 1, INT32_MAX / 2);
     num("GQA_DECODE_SPLIT_KEYS", t.split_keys, 1, INT32_MAX);
     num("GQA_DECODE_PIECE_COST", t.piece_cost, 0, 1024);
@@ -2074,17 +2177,21 @@ hipError_t launch_combine(const gqa_plan_t &plan, const gqa_tuning_t &t, const f
                           int D, int cap, int halve_long, hipStream_t stream) {
     // rows: M query tokens x Hq heads per sequence, M * G per (sequence, kv head)
     const int rows = M * Hq;
+    const bool prop = plan.partition == kPartitionProp;
+    // the split kernel's share count: the launched grid, less one workgroup per segment for proportional splits
+    const int shares = prop ? plan.grid - B * Hkv : plan.grid;
     CombineArgs ca{part_acc, part_ml, out, seq_lens, D, rows / Hkv, rows, plan.num_splits,
-                   B, Hkv, cap, plan.tile_tokens, plan.grid, M, Hq / Hkv, t.piece_cost, halve_long};
+                   B, Hkv, cap, plan.tile_tokens, shares, M, Hq / Hkv, t.piece_cost, halve_long, prop ? 1 : 0};
     // The widest dim chunk (NCOL = 16, 8, 4 or 2 columns of 4 dims) that
     // still gives at least 128 workgroups: narrower chunks put more threads on
     // the pieces of a column (measured best for few heads with many pieces).
     // The tuning's combine_cols (2, 4, 8 or 16) overrides it.
     const int64_t heads = (int64_t)B * rows;
-    const bool even = plan.partition == kPartitionEven;
+    const bool even = plan.partition == kPartitionEven || prop;
     // Few pieces per segment (at full length): one thread per column folds
     // them (no tree).  The tuning's combine = 1 keeps the tree for A/B runs.
-    if (t.combine == 0 && plan.max_pieces <= kNarrowPieces) {
+    // Proportional splits always take the thread-per-column combine.
+    if ((t.combine == 0 && plan.max_pieces <= kNarrowPieces) || prop) {
         const int64_t waves = (int64_t)B * ((rows * (D / 4) + 63) / 64);
         auto go = [&](auto kernel) {
             hipLaunchKernelGGL(kernel, dim3((unsigned)waves), dim3(kNarrowThreads), 0, stream, ca.part_acc,
@@ -2118,7 +2225,7 @@ hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, int kv, h
     } else {
         const dim3 grid((unsigned)plan.grid), block(64 * kWaves);
         const int cap = PAGED ? a.max_pages * a.page_size : a.S_max;
-        const bool even = plan.partition == kPartitionEven;
+        const bool even = plan.partition == kPartitionEven || plan.partition == kPartitionProp;
         const bool nt = plan.streaming != 0;
         const int qpack = a.G | a.M << 5 | a.R << 10 | a.qdiv << 15;  // each field <= 16, qdiv <= 256
         auto go = [&](auto kernel) {
@@ -2198,6 +2305,7 @@ gqa_status_t run(const gqa_plan_t &plan, const gqa_tuning_t &t, SplitArgs &a, in
     // every partial for gqa_decode_combine.
     a.fused = plan.fused && phases == (kPhaseSplit | kPhaseCombine) ? 1 : 0;
     a.fanin = plan.fold_fanin;
+    a.prop = plan.partition == kPartitionProp ? 1 : 0;
     hipError_t e = hipSuccess;
     if (phases & kPhaseSplit) {
         switch (D) {
@@ -2299,6 +2407,7 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
     const int base = B > 0 ? B * Hkv : 1;
     const bool want_fixed = t.partition == 1;
     const bool want_even = t.partition == 2;
+    const bool want_prop = t.partition == 3;
 
     // Small jobs: one 16-key tile per wave in fixed splits.  `most16` is the
     // split count that gives every wave one 16-key tile at full length.
@@ -2321,7 +2430,7 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
         (int64_t)base * most16 <= 4 * (int64_t)cu_count) {
         small_fixed = true;
     }
-    const bool fixed_by_shape = !(tiles_total > 4 * kWaves && (B > 1 || want_even));
+    const bool fixed_by_shape = !(tiles_total > 4 * kWaves && (B > 1 || want_even || want_prop));
     if (auto_tile && num_splits == 0 && tt > 16 && most16 >= 2 &&
         (small_fixed || (fixed_by_shape && (int64_t)base * most16 <= cu_count / 2))) {
         tt = 16;
@@ -2347,12 +2456,29 @@ gqa_status_t plan_impl(int B, int Hq, int Hkv, int D, int max_seq_len, int page_
     // workgroup (<= 4 tiles per wave) is written directly instead.
     // A single sequence cannot be ragged: fixed splits give it the same work
     // split without the device-side length scan.
-    if (num_splits == 0 && !want_fixed && !small_fixed && tiles_total > 4 * kWaves && (B > 1 || want_even)) {
+    if (num_splits == 0 && !want_fixed && !small_fixed && tiles_total > 4 * kWaves &&
+        (B > 1 || want_even || want_prop)) {
         const int64_t tiles_max = (int64_t)base * tiles_total;
         int64_t P = t.shares > 0 ? t.shares : (B > 1 ? 2 * cu_count : cu_count);
         if (P > (tiles_max + kWaves - 1) / kWaves) P = (tiles_max + kWaves - 1) / kWaves;
         if (P < 1) P = 1;
         if (P > INT32_MAX / 2) return GQA_ERR_SHAPE;
+        if (want_prop) {
+            // Proportional splits: P workgroups' worth of at most L tiles each
+            // (decided on the device from seq_lens), plus up to one more per
+            // segment for the rounding of each segment's split count.
+            const int64_t L = (tiles_max + P - 1) / P;  // at full length, P not halved
+            if (P + base > INT32_MAX / 2) return GQA_ERR_SHAPE;
+            plan->partition = kPartitionProp;
+            plan->num_splits = 0;
+            plan->split_tokens = (int)std::min<int64_t>(L * tt, INT32_MAX);
+            plan->grid = B > 0 ? (int)(P + base) : 0;
+            plan->direct = 0;
+            plan->slots = P + base;
+            plan->max_pieces = (int)std::min<int64_t>(P, (tiles_total + L - 1) / L);
+            plan->workspace_bytes = workspace_layout(Hq, Hkv, D, plan->slots).total;
+            return GQA_OK;
+        }
         plan->partition = kPartitionEven;
         plan->num_splits = 0;
         plan->split_tokens = (int)((tiles_max + P - 1) / P) * tt;  // keys per share at full length

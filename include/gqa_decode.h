@@ -66,7 +66,8 @@ typedef enum gqa_status {
 
 /* How a call is laid out on the device (host-side, deterministic). */
 typedef struct gqa_plan {
-    int partition;          /* 0: fixed splits per (sequence, kv head); 1: even shares */
+    int partition;          /* 0: fixed splits per (sequence, kv head); 1: even shares;
+                               2: proportional splits (gqa_tuning_t.partition = 3) */
     int num_splits;         /* fixed: S, KV partitions per (sequence, kv head); even: 0 */
     int split_tokens;       /* fixed: keys per split; even: keys per share at full length */
     int tile_tokens;        /* keys one wave stages per pipeline step */
@@ -104,7 +105,11 @@ typedef struct gqa_tuning {
     int double_buffer; /* GQA_DECODE_DBUF=1: two register tiles per wave (A/B variant); 0 (default): one */
     int pv_mode;       /* GQA_DECODE_PV=f32 -> 0: fp32-MFMA PV (A/B variant); 1 (default): bf16 MFMA, P hi+lo */
     int streaming;     /* GQA_DECODE_NT=0 -> 0: default cache policy; 1 (default): non-temporal K/V loads */
-    int partition;     /* GQA_DECODE_PARTITION=fixed|even -> 1|2; 0 (default): by shape */
+    int partition;     /* GQA_DECODE_PARTITION=fixed|even|prop -> 1|2|3; 0 (default): by shape.
+                          prop (an A/B variant): every (sequence, kv head) of n tiles cut into
+                          ceil(n / L) equal splits, L = ceil(all tiles / shares), decided on the
+                          device from seq_lens -- one piece per workgroup, up to one more
+                          workgroup per segment than shares; the combine kernel folds them */
     int shares;        /* GQA_DECODE_SHARES: even-share workgroups; 0 (default): two per CU for batches
                           (one per CU for long contiguous segments), one per CU for one sequence */
     int split_keys;    /* GQA_DECODE_SPLIT_KEYS: most keys per fixed split; 0 (default): 2048 */

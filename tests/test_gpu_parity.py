@@ -472,6 +472,53 @@ def test_cache_policy_variants(tune, nt):
     compare(out, oracle_out(case), f"nt={nt}")
 
 
+# ------------------------------------------------------------------ proportional splits (partition = 3)
+def _prop_cases():
+    rng = np.random.default_rng(190)
+    return [
+        W.contig_case(10, 16, 4, 128, 5000, seq_lens=[1, 0, 700, 3, 5000, 17, 0, 2048, 1, 33], seed=191, tail="nan"),
+        W.paged_case(16, 32, 8, 128, 32, 4000, max_len=8192, seed=192),
+        W.contig_case(70, 16, 2, 128, 2304, seq_lens=rng.integers(0, 2305, 70), seed=193),
+        W.contig_case(100, 16, 4, 128, 1024, seq_lens=[(7 * i) % 40 for i in range(100)], seed=194),
+        W.contig_case(3, 16, 4, 128, 1024, seq_lens=[0, 0, 0], seed=195),
+        W.contig_case(4, 32, 4, 128, 20000, seq_lens=[0, 0, 20000, 0], seed=196),
+        W.contig_case(8, 32, 4, 128, 4096, seed=197),
+        W.mq_case(12, 3, 16, 4, 128, 3000, seq_lens=[3000, 2, 0, 999, 1500, 2500] * 2, seed=198),
+        W.fp8_contig_case(18, 16, 2, 128, 3000, seq_lens=[3000, 1, 0, 1500, 77, 2999] * 3, seed=199),
+        W.fp8_paged_case(10, 16, 4, 128, 32, 400, seq_lens=[2048, 1, 0, 777, 1500] * 2, max_len=2048, seed=200),
+        W.paged_case(6, 8, 2, 64, 48, 300, seq_lens=[1, 2000, 47, 49, 0, 1500], max_len=2400, seed=201),
+        W.contig_case(2, 24, 4, 256, 4096, seq_lens=[4096, 3001], seed=202, scale=1 / 16),
+    ]
+
+
+_PROP_REF = {}
+
+
+@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("shares", ["0", "7", "1000"])
+def test_proportional_splits(tune, i, shares):
+    """Proportional splits: each (sequence, kv head) segment cut into ceil(n / L) equal splits,
+    one piece per workgroup, folded by the thread-per-column combine -- ragged lengths with zeros
+    and NaN tails, paged (page 32 and 48), more than 64 sequences, all sequences empty, one long
+    sequence among empty ones, uniform lengths, multi-query rows, E4M3, head_dim 64 and 256,
+    several share counts; against the oracle and bit-exact across runs."""
+    tune(partition=3, shares=int(shares))
+    case = _prop_cases()[i]
+    say(f"[parity] proportional splits {case.name} B={case.B} shares={shares}")
+    plan_fn = gd.gqa_decode_plan_fp8 if case.kv == "fp8" else gd.gqa_decode_plan
+    p = plan_fn(case.B, case.M * case.Hq, case.Hkv, case.D, case.capacity, case.page_size)
+    assert p.partition == 2, p.as_dict()
+    dc = DeviceCase(case)
+    a = dc.run_host()
+    if i not in _PROP_REF:
+        _PROP_REF[i] = oracle_out(case)
+    compare(a, _PROP_REF[i], f"proportional {case.name} shares={shares}")
+    assert np.array_equal(np.ascontiguousarray(a).view(np.uint32), np.ascontiguousarray(dc.run_host()).view(np.uint32))
+    lens = np.asarray(case.seq_lens)
+    if case.M == 1:
+        assert np.all(a[lens == 0] == 0)
+
+
 # ------------------------------------------------------------------ very large batches
 @pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
 def test_very_large_batch(paged):
@@ -573,6 +620,10 @@ def test_tile_and_buffer_variants(tune, tile, dbuf, D):
     ("paged_gqa4_d128_ragged8k", {"shares": 256, "double_buffer": 1}),
     ("long_gqa8_d128_ctx128k_peaky", {"tile_tokens": 32}),
     ("long_gqa8_d128_ctx128k_peaky", {"double_buffer": 1}),
+    ("batched_gqa8_d128_ctx16k", {"partition": 3}),
+    ("paged_gqa4_d128_ragged8k", {"partition": 3}),
+    ("gqa6_d256_ctx4096", {"partition": 3}),
+    ("long_gqa8_d128_ctx128k_peaky", {"partition": 3}),
 ], ids=lambda x: x if isinstance(x, str) else ",".join(f"{k}={v}" for k, v in x.items()))
 def test_variant_workloads(tune, name, fields):
     """The full-size workloads under the tile and buffering variants that bench.py --ab times."""

@@ -168,6 +168,28 @@ def test_small_batches_take_fixed_splits():
     assert gd.gqa_decode_plan(4, 32, 8, 128, 1024, 0, 0, 64).partition == 1
 
 
+def test_proportional_split_plan():
+    """partition = 3 (proportional splits): the grid is the share count plus one workgroup per
+    segment (each segment's split count is rounded up on the device), every workgroup writes one
+    partial slot, the combine is the thread-per-column one, and the E4M3 plan needs no more."""
+    with gd.tuning(partition=3):
+        p = gd.gqa_decode_plan(16, 32, 4, 128, 16384, 0, 0, 256)
+        assert p.partition == 2 and p.num_splits == 0 and p.fused == 0
+        assert p.grid == 512 + 64 and p.slots == p.grid
+        assert p.split_tokens == 16 * ((64 * 1024 + 511) // 512)      # L tiles at full length
+        assert p.max_pieces == 1024 // (p.split_tokens // 16)
+        pp = gd.gqa_decode_plan(32, 32, 8, 128, 8192, 32, 0, 256)
+        assert pp.partition == 2 and pp.grid == 512 + 256
+        pf = gd.gqa_decode_plan_fp8(32, 32, 8, 128, 8192, 32, 0, 256)
+        assert pf.partition == 2 and pf.workspace_bytes <= pp.workspace_bytes
+        # a single sequence asked for proportional splits takes them too
+        p1 = gd.gqa_decode_plan(1, 8, 1, 128, 131072, 0, 0, 256)
+        assert p1.partition == 2 and p1.grid == 256 + 1
+        # small jobs, forced split counts and short caches keep their fixed plans
+        assert gd.gqa_decode_plan(2, 16, 4, 128, 256, 0, 0, 256).partition == 0
+        assert gd.gqa_decode_plan(16, 32, 4, 128, 16384, 0, 7, 256).partition == 0
+
+
 def test_forced_splits_are_clamped_to_tiles():
     p = gd.gqa_decode_plan(1, 8, 2, 64, 512, 0, 1000, 256)
     assert p.partition == 0 and p.num_splits == 512 // p.tile_tokens
@@ -363,7 +385,7 @@ def test_default_tuning():
 
 @pytest.mark.parametrize("field,value", [
     ("tile_tokens", 24), ("tile_tokens", 128), ("double_buffer", 2), ("pv_mode", -1),
-    ("partition", 3), ("shares", -1), ("piece_cost", 1025), ("combine_cols", 3), ("fold", 3),
+    ("partition", 4), ("shares", -1), ("piece_cost", 1025), ("combine_cols", 3), ("fold", 3),
     ("num_splits", -2)])
 def test_set_tuning_rejects_out_of_range(field, value):
     before = gd.gqa_decode_get_tuning().as_dict()
