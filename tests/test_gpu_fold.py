@@ -109,16 +109,14 @@ def test_fused_fixed_split_counts(tune, splits):
 
 
 def _even_cases():
-    rng = np.random.default_rng(81)
+    lens70 = np.random.default_rng(81).integers(0, 2305, 70)
     return [
-        W.contig_case(10, 16, 4, 128, 5000, seq_lens=[1, 0, 700, 3, 5000, 17, 0, 2048, 1, 33],
-                      seed=82, tail="nan"),
-        W.paged_case(16, 32, 8, 128, 32, 4000, max_len=8192, seed=83),
-        W.contig_case(70, 16, 2, 128, 2304, seq_lens=rng.integers(0, 2305, 70), seed=84),
-        W.mq_case(12, 3, 16, 4, 128, 3000, seq_lens=[3000, 2, 0, 999, 1500, 2500] * 2, seed=85),
-        W.fp8_contig_case(18, 16, 2, 128, 3000, seq_lens=[3000, 1, 0, 1500, 77, 2999] * 3, seed=86),
-        W.fp8_paged_case(10, 16, 4, 128, 32, 400, seq_lens=[2048, 1, 0, 777, 1500] * 2, max_len=2048,
-                         seed=87),
+        lambda: W.contig_case(10, 16, 4, 128, 5000, seq_lens=[1, 0, 700, 3, 5000, 17, 0, 2048, 1, 33], seed=82, tail="nan"),
+        lambda: W.paged_case(16, 32, 8, 128, 32, 4000, max_len=8192, seed=83),
+        lambda: W.contig_case(70, 16, 2, 128, 2304, seq_lens=lens70, seed=84),
+        lambda: W.mq_case(12, 3, 16, 4, 128, 3000, seq_lens=[3000, 2, 0, 999, 1500, 2500] * 2, seed=85),
+        lambda: W.fp8_contig_case(18, 16, 2, 128, 3000, seq_lens=[3000, 1, 0, 1500, 77, 2999] * 3, seed=86),
+        lambda: W.fp8_paged_case(10, 16, 4, 128, 32, 400, seq_lens=[2048, 1, 0, 777, 1500] * 2, max_len=2048, seed=87),
     ]
 
 
@@ -128,7 +126,7 @@ def test_fused_even_matches_combine_bitwise(tune, i):
     combine's arithmetic, in the same order, and writes a segment held by one share straight to
     `out` -- so one launch and two give the same bits (bf16, paged, many sequences, multi-query
     rows, E4M3)."""
-    case = _even_cases()[i]
+    case = _even_cases()[i]()
     say(f"[fold] even bitwise {case.name}")
     dc = DeviceCase(case)
     tune(fold=2, partition=2)

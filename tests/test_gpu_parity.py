@@ -474,28 +474,30 @@ def test_cache_policy_variants(tune, nt):
 
 # ------------------------------------------------------------------ proportional splits (partition = 3)
 def _prop_cases():
-    rng = np.random.default_rng(190)
+    """Factories (each test builds only its own case)."""
+    lens70 = np.random.default_rng(190).integers(0, 2305, 70)
     return [
-        W.contig_case(10, 16, 4, 128, 5000, seq_lens=[1, 0, 700, 3, 5000, 17, 0, 2048, 1, 33], seed=191, tail="nan"),
-        W.paged_case(16, 32, 8, 128, 32, 4000, max_len=8192, seed=192),
-        W.contig_case(70, 16, 2, 128, 2304, seq_lens=rng.integers(0, 2305, 70), seed=193),
-        W.contig_case(100, 16, 4, 128, 1024, seq_lens=[(7 * i) % 40 for i in range(100)], seed=194),
-        W.contig_case(3, 16, 4, 128, 1024, seq_lens=[0, 0, 0], seed=195),
-        W.contig_case(4, 32, 4, 128, 20000, seq_lens=[0, 0, 20000, 0], seed=196),
-        W.contig_case(8, 32, 4, 128, 4096, seed=197),
-        W.mq_case(12, 3, 16, 4, 128, 3000, seq_lens=[3000, 2, 0, 999, 1500, 2500] * 2, seed=198),
-        W.fp8_contig_case(18, 16, 2, 128, 3000, seq_lens=[3000, 1, 0, 1500, 77, 2999] * 3, seed=199),
-        W.fp8_paged_case(10, 16, 4, 128, 32, 400, seq_lens=[2048, 1, 0, 777, 1500] * 2, max_len=2048, seed=200),
-        W.paged_case(6, 8, 2, 64, 48, 300, seq_lens=[1, 2000, 47, 49, 0, 1500], max_len=2400, seed=201),
-        W.contig_case(2, 24, 4, 256, 4096, seq_lens=[4096, 3001], seed=202, scale=1 / 16),
+        lambda: W.contig_case(10, 16, 4, 128, 5000, seq_lens=[1, 0, 700, 3, 5000, 17, 0, 2048, 1, 33], seed=191, tail="nan"),
+        lambda: W.paged_case(16, 32, 8, 128, 32, 4000, max_len=8192, seed=192),
+        lambda: W.contig_case(70, 16, 2, 128, 2304, seq_lens=lens70, seed=193),
+        lambda: W.contig_case(100, 16, 4, 128, 1024, seq_lens=[(7 * i) % 40 for i in range(100)], seed=194),
+        lambda: W.contig_case(3, 16, 4, 128, 1024, seq_lens=[0, 0, 0], seed=195),
+        lambda: W.contig_case(4, 32, 4, 128, 20000, seq_lens=[0, 0, 20000, 0], seed=196),
+        lambda: W.contig_case(8, 32, 4, 128, 4096, seed=197),
+        lambda: W.mq_case(12, 3, 16, 4, 128, 3000, seq_lens=[3000, 2, 0, 999, 1500, 2500] * 2, seed=198),
+        lambda: W.fp8_contig_case(18, 16, 2, 128, 3000, seq_lens=[3000, 1, 0, 1500, 77, 2999] * 3, seed=199),
+        lambda: W.fp8_paged_case(10, 16, 4, 128, 32, 400, seq_lens=[2048, 1, 0, 777, 1500] * 2, max_len=2048, seed=200),
+        lambda: W.paged_case(6, 8, 2, 64, 48, 300, seq_lens=[1, 2000, 47, 49, 0, 1500], max_len=2400, seed=201),
+        lambda: W.contig_case(2, 24, 4, 256, 4096, seq_lens=[4096, 3001], seed=202, scale=1 / 16),
     ]
 
 
 _PROP_REF = {}
+_PROP_CASE = {}
 
 
-@pytest.mark.parametrize("i", range(12))
 @pytest.mark.parametrize("shares", ["0", "7", "1000"])
+@pytest.mark.parametrize("i", range(12))
 def test_proportional_splits(tune, i, shares):
     """Proportional splits: each (sequence, kv head) segment cut into ceil(n / L) equal splits,
     one piece per workgroup, folded by the thread-per-column combine -- ragged lengths with zeros
@@ -503,7 +505,10 @@ def test_proportional_splits(tune, i, shares):
     sequence among empty ones, uniform lengths, multi-query rows, E4M3, head_dim 64 and 256,
     several share counts; against the oracle and bit-exact across runs."""
     tune(partition=3, shares=int(shares))
-    case = _prop_cases()[i]
+    if i not in _PROP_CASE:
+        _PROP_CASE.clear()   # one case held at a time (the share counts of one case run together or not)
+        _PROP_CASE[i] = _prop_cases()[i]()
+    case = _PROP_CASE[i]
     say(f"[parity] proportional splits {case.name} B={case.B} shares={shares}")
     plan_fn = gd.gqa_decode_plan_fp8 if case.kv == "fp8" else gd.gqa_decode_plan
     p = plan_fn(case.B, case.M * case.Hq, case.Hkv, case.D, case.capacity, case.page_size)
@@ -556,17 +561,17 @@ def test_multi_head_attention_shape():
 # ------------------------------------------------------------------ small jobs: fixed splits of one 16-key tile per wave
 def _small_job_cases():
     return [
-        W.contig_case(2, 16, 4, 128, 1024, seq_lens=[1024, 333], seed=160, tail="nan"),
-        W.contig_case(3, 8, 2, 64, 700, seq_lens=[700, 300, 5], seed=161, tail="nan"),
-        W.contig_case(8, 8, 1, 256, 512, seq_lens=[512, 0, 1, 17, 500, 64, 65, 333], seed=162, scale=1 / 16),
-        W.contig_case(8, 32, 8, 128, 1024, seq_lens=[1024, 3, 0, 999, 512, 1000, 64, 777], seed=163),   # 1024 workgroups
-        W.contig_case(2, 8, 2, 32, 4096, seq_lens=[4096, 4000], seed=164),
-        W.paged_case(4, 8, 2, 128, 32, 100, seq_lens=[1024, 300, 700, 9], max_len=1024, seed=165),
-        W.paged_case(2, 32, 8, 64, 16, 80, seq_lens=[512, 400], max_len=512, seed=166),
-        W.fp8_contig_case(2, 16, 4, 128, 1024, seq_lens=[1024, 77], seed=167),
-        W.fp8_paged_case(4, 8, 2, 128, 32, 100, seq_lens=[1024, 300, 700, 9], max_len=1024, seed=168),
-        W.mq_case(3, 4, 16, 4, 128, 1024, seq_lens=[1024, 4, 600], seed=169, tail="nan"),
-        W.mq_paged_case(2, 2, 16, 4, 128, 32, 80, [1000, 33], max_len=1024, seed=170),
+        lambda: W.contig_case(2, 16, 4, 128, 1024, seq_lens=[1024, 333], seed=160, tail="nan"),
+        lambda: W.contig_case(3, 8, 2, 64, 700, seq_lens=[700, 300, 5], seed=161, tail="nan"),
+        lambda: W.contig_case(8, 8, 1, 256, 512, seq_lens=[512, 0, 1, 17, 500, 64, 65, 333], seed=162, scale=1 / 16),
+        lambda: W.contig_case(8, 32, 8, 128, 1024, seq_lens=[1024, 3, 0, 999, 512, 1000, 64, 777], seed=163),   # 1024 workgroups
+        lambda: W.contig_case(2, 8, 2, 32, 4096, seq_lens=[4096, 4000], seed=164),
+        lambda: W.paged_case(4, 8, 2, 128, 32, 100, seq_lens=[1024, 300, 700, 9], max_len=1024, seed=165),
+        lambda: W.paged_case(2, 32, 8, 64, 16, 80, seq_lens=[512, 400], max_len=512, seed=166),
+        lambda: W.fp8_contig_case(2, 16, 4, 128, 1024, seq_lens=[1024, 77], seed=167),
+        lambda: W.fp8_paged_case(4, 8, 2, 128, 32, 100, seq_lens=[1024, 300, 700, 9], max_len=1024, seed=168),
+        lambda: W.mq_case(3, 4, 16, 4, 128, 1024, seq_lens=[1024, 4, 600], seed=169, tail="nan"),
+        lambda: W.mq_paged_case(2, 2, 16, 4, 128, 32, 80, [1000, 33], max_len=1024, seed=170),
     ]
 
 
@@ -575,7 +580,7 @@ def test_small_job_plans(i):
     """Batches small enough that one 16-key tile per wave in fixed splits takes at most four
     workgroups per CU (contiguous, paged, E4M3, multi-query; ragged lengths, zeros, NaN tails):
     the plan is those splits, the result matches the oracle and is bit-exact across runs."""
-    case = _small_job_cases()[i]
+    case = _small_job_cases()[i]()
     say(f"[parity] small job {case.name} B={case.B} Hkv={case.Hkv} D={case.D} cap={case.capacity}")
     plan_fn = gd.gqa_decode_plan_fp8 if case.kv == "fp8" else gd.gqa_decode_plan
     p = plan_fn(case.B, case.M * case.Hq, case.Hkv, case.D, case.capacity, case.page_size)
