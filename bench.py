@@ -189,11 +189,20 @@ def combine_read_bytes(case, plan, piece_cost=4):
     tt = plan.tile_tokens
     lens = np.minimum(np.maximum(case.seq_lens.astype(np.int64), 0), case.capacity)
     tiles = (lens + tt - 1) // tt
+    long_ok = (not case.paged) and case.kv == "bf16"
+    if plan.partition == 2:   # proportional splits: ceil(n / L) pieces per segment
+        P = plan.grid - case.B * case.Hkv
+        N = int(tiles.sum()) * case.Hkv
+        segs = int((tiles > 0).sum()) * case.Hkv
+        if long_ok and segs > 0 and N >= 128 * segs:
+            P = (P + 1) // 2
+        L = max(1, -(-N // P)) if N > 0 else 1
+        pieces = int(((tiles + L - 1) // L).sum()) * case.Hkv
+        return pieces * per_piece, out_bytes
     span = np.where(tiles > 0, tiles + piece_cost, 0)
     N = int(span.sum()) * case.Hkv
     P = plan.grid
     segs = int((tiles > 0).sum()) * case.Hkv
-    long_ok = (not case.paged) and case.kv == "bf16"
     if long_ok and segs > 0 and N >= (128 + piece_cost) * segs:
         P = (P + 1) // 2   # one share per CU for long contiguous segments
     share_of = lambda x: ((x + 1) * P + N - 1) // N - 1
