@@ -201,6 +201,57 @@ def test_side_stream_internal_buffers():
         compare(o.cpu().numpy(), ref, "side stream, internal buffers")
 
 
+def test_concurrent_host_threads():
+    """Four host threads call the library at once (ctypes drops the GIL for the call), each on
+    its own stream with its own workspace and outputs, one plan kind per thread: the small-job
+    in-kernel fold, fixed splits, even shares and a paged cache. Every result equals the same call
+    made alone, bit for bit, and that call matches the oracle."""
+    import threading
+    say("[parity] concurrent host threads")
+    cases = [W.make("tiny_gqa4_d64_ctx512"),
+             W.contig_case(1, 24, 4, 256, 2048, seed=93, name="fixed"),
+             W.contig_case(12, 32, 4, 128, 3000, seq_lens=[3000, 17, 2500, 0, 999, 3000, 1, 2048,
+                                                           640, 2999, 1500, 33], seed=94, name="even"),
+             W.paged_case(6, 16, 4, 128, 32, 400, seq_lens=[1, 700, 2048, 31, 1200, 999], max_len=2048,
+                          seed=95, name="paged")]
+    dcs = [DeviceCase(c) for c in cases]
+    alone = []
+    for c, dc in zip(cases, dcs):
+        o = dc.run_host()
+        compare(o, oracle_out(c), f"concurrent threads, alone: {c.name}")
+        alone.append(o)
+    torch.cuda.synchronize()
+    calls = 25
+    results = [None] * len(cases)
+    errors = []
+
+    def work(i):
+        try:
+            c, dc = cases[i], dcs[i]
+            need = gd.gqa_decode_workspace_bytes(c.B, c.Hq, c.Hkv, c.D, c.capacity, c.page_size, 0)
+            s = torch.cuda.Stream()
+            ws = gd.new_workspace(max(need, gd.COUNTER_BYTES), stream=s)  # zeroed on s
+            with torch.cuda.stream(s):
+                outs = [torch.empty((c.B, c.Hq, c.D), dtype=torch.float32, device="cuda") for _ in range(calls)]
+            for o in outs:
+                dc.run(0, out=o, workspace=ws, stream=s)
+            s.synchronize()
+            results[i] = [o.cpu().numpy() for o in outs]
+        except Exception as e:  # reported on the main thread
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads), "a host thread did not finish"
+    assert not errors, errors
+    for i, c in enumerate(cases):
+        for o in results[i]:
+            assert np.array_equal(o.view(np.uint32), alone[i].view(np.uint32)), f"{c.name}: differs from the call alone"
+
+
 # ------------------------------------------------------------------ paged
 @pytest.mark.parametrize("ps", [16, 32, 64, 48])
 @pytest.mark.parametrize("D", [32, 64, 128, 256])
