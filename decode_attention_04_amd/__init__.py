@@ -196,14 +196,26 @@ def gqa_decode_workspace_bytes(B, Hq, Hkv, head_dim, max_seq_len, page_size=0, n
 
 
 # ------------------------------------------------------------------ tensor marshalling
+# Per-call marshalling is on the host's critical path for eager callers (a call of the
+# binding costs more host time than the two kernel launches it makes), so the torch
+# module, the dtype sets and the raw current-stream query are looked up once.
+_TORCH = None
+_BF16_TYPES = None
+_RAW_STREAM = None  # torch's raw current-stream query, when this torch build has it
+
+
 def _torch():
-    import torch
-    return torch
+    global _TORCH, _BF16_TYPES, _RAW_STREAM
+    if _TORCH is None:
+        import torch
+        _BF16_TYPES = (torch.bfloat16, torch.int16, torch.uint16)
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _TORCH = torch
+    return _TORCH
 
 
 def _dev_ptr(t, name, dtypes):
-    torch = _torch()
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+    if not isinstance(t, _torch().Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a device tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
@@ -213,14 +225,19 @@ def _dev_ptr(t, name, dtypes):
 
 
 def _bf16_types():
-    torch = _torch()
-    return (torch.bfloat16, torch.int16, torch.uint16)
+    _torch()
+    return _BF16_TYPES
 
 
 def _stream_ptr(stream, device):
+    """The raw hipStream_t of `stream`, else of the current stream of `device` (a tensor's
+    device)."""
+    if stream is not None:
+        return stream.cuda_stream
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return s.cuda_stream
+    if _RAW_STREAM is not None and device.type == "cuda" and device.index is not None:
+        return _RAW_STREAM(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _alloc(shape, dtype, device, stream, zero=False):
@@ -242,10 +259,14 @@ def new_workspace(nbytes, device="cuda", stream=None):
 
 
 def _workspace(workspace, need, device, stream):
-    if need == 0:
+    """(workspace, its bytes): the caller's, whose size the library checks against the plan,
+    or one allocated for the call when `need()` (the plan's bytes) is not 0."""
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    n = need()
+    if n == 0:
         return None, 0
-    if workspace is None:
-        workspace = new_workspace(need, device, stream)
+    workspace = new_workspace(n, device, stream)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -261,7 +282,7 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None, n
     _, Hkv, S_max, _ = k_cache.shape
     if out is None:
         out = _alloc((B, Hq, D), torch.float32, q.device, stream)
-    need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, S_max, 0, num_splits)
+    need = lambda: gqa_decode_workspace_bytes(B, Hq, Hkv, D, S_max, 0, num_splits)
     workspace, ws_bytes = _workspace(workspace, need, q.device, stream)
     bf = _bf16_types()
     rc = getattr(load(), _entry)(
@@ -284,7 +305,7 @@ def gqa_paged_decode(q, k_pool, v_pool, seq_lens, page_table, scale, out=None, w
     max_pages = page_table.shape[1]
     if out is None:
         out = _alloc((B, Hq, D), torch.float32, q.device, stream)
-    need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, max_pages * page_size, page_size, num_splits)
+    need = lambda: gqa_decode_workspace_bytes(B, Hq, Hkv, D, max_pages * page_size, page_size, num_splits)
     workspace, ws_bytes = _workspace(workspace, need, q.device, stream)
     bf = _bf16_types()
     rc = getattr(load(), _entry)(
@@ -313,7 +334,7 @@ def gqa_decode_fp8(q, k_cache, v_cache, seq_lens, scale, k_scale, v_scale, out=N
     _, Hkv, S_max, _ = k_cache.shape
     if out is None:
         out = _alloc((B, Hq, D), torch.float32, q.device, stream)
-    need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, S_max, 0, num_splits)
+    need = lambda: gqa_decode_workspace_bytes(B, Hq, Hkv, D, S_max, 0, num_splits)
     workspace, ws_bytes = _workspace(workspace, need, q.device, stream)
     f8 = _fp8_types()
     rc = getattr(load(), _entry)(
@@ -338,7 +359,7 @@ def gqa_paged_decode_fp8(q, k_pool, v_pool, seq_lens, page_table, scale, k_scale
     max_pages = page_table.shape[1]
     if out is None:
         out = _alloc((B, Hq, D), torch.float32, q.device, stream)
-    need = gqa_decode_workspace_bytes(B, Hq, Hkv, D, max_pages * page_size, page_size, num_splits)
+    need = lambda: gqa_decode_workspace_bytes(B, Hq, Hkv, D, max_pages * page_size, page_size, num_splits)
     workspace, ws_bytes = _workspace(workspace, need, q.device, stream)
     f8 = _fp8_types()
     rc = getattr(load(), _entry)(
@@ -382,7 +403,7 @@ def gqa_decode_mq(q, k_cache, v_cache, seq_lens, scale, out=None, workspace=None
     _, Hkv, S_max, _ = k_cache.shape
     if out is None:
         out = _alloc((B, M, Hq, D), torch.float32, q.device, stream)
-    need = gqa_decode_workspace_bytes(B, M * Hq, Hkv, D, S_max, 0, num_splits)
+    need = lambda: gqa_decode_workspace_bytes(B, M * Hq, Hkv, D, S_max, 0, num_splits)
     workspace, ws_bytes = _workspace(workspace, need, q.device, stream)
     bf = _bf16_types()
     rc = load().gqa_decode_mq(
@@ -405,7 +426,7 @@ def gqa_paged_decode_mq(q, k_pool, v_pool, seq_lens, page_table, scale, out=None
     max_pages = page_table.shape[1]
     if out is None:
         out = _alloc((B, M, Hq, D), torch.float32, q.device, stream)
-    need = gqa_decode_workspace_bytes(B, M * Hq, Hkv, D, max_pages * page_size, page_size,
+    need = lambda: gqa_decode_workspace_bytes(B, M * Hq, Hkv, D, max_pages * page_size, page_size,
                                       num_splits)
     workspace, ws_bytes = _workspace(workspace, need, q.device, stream)
     bf = _bf16_types()
