@@ -5,9 +5,10 @@
  *
  *   gqa_c_caller host   argument checks, plans, tuning and status strings
  *                       (host code only: needs no GPU)
- *   gqa_c_caller gpu    gqa_decode, gqa_paged_decode and gqa_decode_noalloc on
- *                       small ragged cases against the oracle, elementwise
- *                       |gpu - oracle| <= 2e-3 + 2e-3 |oracle|
+ *   gqa_c_caller gpu    gqa_decode, gqa_paged_decode, gqa_decode_noalloc,
+ *                       gqa_decode_partials + gqa_decode_combine, gqa_decode_fp8
+ *                       and gqa_decode_mq on small ragged cases against the
+ *                       oracle, elementwise |gpu - oracle| <= 2e-3 + 2e-3 |oracle|
  *
  * Exit status 0 when every check passes, 1 otherwise.
  */
@@ -27,6 +28,11 @@ int oracle_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
 int oracle_paged_decode(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                         const int32_t *seq_lens, const int32_t *page_table, int B, int Hq, int Hkv, int D,
                         int page_size, int num_pages, int max_pages, float scale, double *out);
+int oracle_decode_fp8(const uint16_t *q, const uint8_t *k, const uint8_t *v, const int32_t *seq_lens, int B,
+                      int Hq, int Hkv, int D, int S_max, float scale, float k_scale, float v_scale, int chunk,
+                      double *out);
+int oracle_decode_mq(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *seq_lens, int B,
+                     int M, int Hq, int Hkv, int D, int S_max, float scale, int chunk, double *out);
 
 static int failures = 0;
 
@@ -63,6 +69,14 @@ static void fill_bf16(uint16_t *dst, size_t n, uint64_t seed) {
     }
 }
 
+/* E4M3 bytes from the same generator, the two NaN codes (0x7F, 0xFF) replaced by +-448. */
+static void fill_e4m3(uint8_t *dst, size_t n, uint64_t seed) {
+    for (size_t i = 0; i < n; ++i) {
+        const uint8_t x = (uint8_t)(splitmix64(seed * 0x100000001B3ull + i) >> 56);
+        dst[i] = (x & 0x7F) == 0x7F ? (uint8_t)(x - 1) : x;
+    }
+}
+
 static int compare(const float *got, const double *ref, size_t n, const char *what) {
     size_t bad = 0;
     double worst = 0.0;
@@ -90,6 +104,13 @@ static void *dev_copy(const void *host, size_t bytes) {
     HIP_OK(hipMalloc(&d, bytes > 0 ? bytes : 16));
     if (bytes > 0) HIP_OK(hipMemcpy(d, host, bytes, hipMemcpyHostToDevice));
     return d;
+}
+
+static void *zeroed_workspace(size_t bytes) {
+    void *ws = NULL;
+    HIP_OK(hipMalloc(&ws, bytes > 0 ? bytes : 16));
+    HIP_OK(hipMemset(ws, 0, bytes > 0 ? bytes : 16)); /* the counter header starts at zero */
+    return ws;
 }
 
 /* ------------------------------------------------------------------ host mode */
@@ -219,6 +240,100 @@ static void paged_case(int B, int Hq, int Hkv, int D, int page_size, int max_pag
     free(q), free(k), free(v), free(table), free(got), free(ref);
 }
 
+/* The two kernels apart: gqa_decode_partials, then gqa_decode_combine on the same workspace. */
+static void two_step_case(int B, int Hq, int Hkv, int D, int S_max, const int32_t *lens, float scale,
+                          uint64_t seed) {
+    const size_t nq = (size_t)B * Hq * D, nkv = (size_t)B * Hkv * S_max * D;
+    uint16_t *q = malloc(nq * 2), *k = malloc(nkv * 2), *v = malloc(nkv * 2);
+    float *got = malloc(nq * 4);
+    double *ref = malloc(nq * 8);
+    fill_bf16(q, nq, seed);
+    fill_bf16(k, nkv, seed + 1);
+    fill_bf16(v, nkv, seed + 2);
+    void *dq = dev_copy(q, nq * 2), *dk = dev_copy(k, nkv * 2), *dv = dev_copy(v, nkv * 2);
+    void *dl = dev_copy(lens, (size_t)B * 4);
+    float *dout = NULL;
+    HIP_OK(hipMalloc((void **)&dout, nq * 4));
+    const size_t ws_bytes = gqa_decode_workspace_bytes(B, Hq, Hkv, D, S_max, 0, 0);
+    void *ws = zeroed_workspace(ws_bytes);
+    gqa_status_t s = gqa_decode_partials(dq, dk, dv, dl, B, Hq, Hkv, D, S_max, scale, dout, ws, ws_bytes, 0, NULL);
+    CHECK(s == GQA_OK, "gqa_decode_partials returned %s", gqa_status_string(s));
+    if (s == GQA_OK) {
+        s = gqa_decode_combine(ws, ws_bytes, dl, B, Hq, Hkv, D, S_max, 0, 0, dout, NULL);
+        CHECK(s == GQA_OK, "gqa_decode_combine returned %s", gqa_status_string(s));
+    }
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(got, dout, nq * 4, hipMemcpyDeviceToHost));
+    CHECK(oracle_decode(q, k, v, lens, B, Hq, Hkv, D, S_max, scale, ref) == 0, "oracle");
+    char what[96];
+    snprintf(what, sizeof what, "partials + combine B=%d Hq=%d Hkv=%d D=%d", B, Hq, Hkv, D);
+    if (s == GQA_OK) compare(got, ref, nq, what);
+    hipFree(dq), hipFree(dk), hipFree(dv), hipFree(dl), hipFree(dout), hipFree(ws);
+    free(q), free(k), free(v), free(got), free(ref);
+}
+
+/* An E4M3 cache with per-tensor scales; the workspace from the E4M3 plan on this device. */
+static void fp8_case(int B, int Hq, int Hkv, int D, int S_max, const int32_t *lens, float scale, float k_scale,
+                     float v_scale, uint64_t seed) {
+    const size_t nq = (size_t)B * Hq * D, nkv = (size_t)B * Hkv * S_max * D;
+    uint16_t *q = malloc(nq * 2);
+    uint8_t *k = malloc(nkv), *v = malloc(nkv);
+    float *got = malloc(nq * 4);
+    double *ref = malloc(nq * 8);
+    fill_bf16(q, nq, seed);
+    fill_e4m3(k, nkv, seed + 1);
+    fill_e4m3(v, nkv, seed + 2);
+    void *dq = dev_copy(q, nq * 2), *dk = dev_copy(k, nkv), *dv = dev_copy(v, nkv);
+    void *dl = dev_copy(lens, (size_t)B * 4);
+    float *dout = NULL;
+    HIP_OK(hipMalloc((void **)&dout, nq * 4));
+    int dev = 0, cus = 0;
+    HIP_OK(hipGetDevice(&dev));
+    HIP_OK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    gqa_plan_t plan;
+    CHECK(gqa_decode_plan_fp8(B, Hq, Hkv, D, S_max, 0, 0, cus, &plan) == GQA_OK, "E4M3 plan");
+    void *ws = zeroed_workspace(plan.workspace_bytes);
+    const gqa_status_t s = gqa_decode_fp8(dq, dk, dv, dl, B, Hq, Hkv, D, S_max, scale, k_scale, v_scale, dout, ws,
+                                          plan.workspace_bytes, 0, NULL);
+    char what[96];
+    snprintf(what, sizeof what, "gqa_decode_fp8 B=%d Hq=%d Hkv=%d D=%d", B, Hq, Hkv, D);
+    CHECK(s == GQA_OK, "%s returned %s", what, gqa_status_string(s));
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(got, dout, nq * 4, hipMemcpyDeviceToHost));
+    CHECK(oracle_decode_fp8(q, k, v, lens, B, Hq, Hkv, D, S_max, scale, k_scale, v_scale, 0, ref) == 0, "oracle");
+    if (s == GQA_OK) compare(got, ref, nq, what);
+    hipFree(dq), hipFree(dk), hipFree(dv), hipFree(dl), hipFree(dout), hipFree(ws);
+    free(q), free(k), free(v), free(got), free(ref);
+}
+
+/* M query tokens per sequence (the last M positions, causal); q and out [B][M][Hq][D]. */
+static void mq_case(int B, int M, int Hq, int Hkv, int D, int S_max, const int32_t *lens, float scale,
+                    uint64_t seed) {
+    const size_t nq = (size_t)B * M * Hq * D, nkv = (size_t)B * Hkv * S_max * D;
+    uint16_t *q = malloc(nq * 2), *k = malloc(nkv * 2), *v = malloc(nkv * 2);
+    float *got = malloc(nq * 4);
+    double *ref = malloc(nq * 8);
+    fill_bf16(q, nq, seed);
+    fill_bf16(k, nkv, seed + 1);
+    fill_bf16(v, nkv, seed + 2);
+    void *dq = dev_copy(q, nq * 2), *dk = dev_copy(k, nkv * 2), *dv = dev_copy(v, nkv * 2);
+    void *dl = dev_copy(lens, (size_t)B * 4);
+    float *dout = NULL;
+    HIP_OK(hipMalloc((void **)&dout, nq * 4));
+    const size_t ws_bytes = gqa_decode_workspace_bytes(B, M * Hq, Hkv, D, S_max, 0, 0);
+    void *ws = zeroed_workspace(ws_bytes);
+    const gqa_status_t s = gqa_decode_mq(dq, dk, dv, dl, B, M, Hq, Hkv, D, S_max, scale, dout, ws, ws_bytes, 0, NULL);
+    char what[96];
+    snprintf(what, sizeof what, "gqa_decode_mq B=%d M=%d Hq=%d Hkv=%d D=%d", B, M, Hq, Hkv, D);
+    CHECK(s == GQA_OK, "%s returned %s", what, gqa_status_string(s));
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(got, dout, nq * 4, hipMemcpyDeviceToHost));
+    CHECK(oracle_decode_mq(q, k, v, lens, B, M, Hq, Hkv, D, S_max, scale, 0, ref) == 0, "oracle");
+    if (s == GQA_OK) compare(got, ref, nq, what);
+    hipFree(dq), hipFree(dk), hipFree(dv), hipFree(dl), hipFree(dout), hipFree(ws);
+    free(q), free(k), free(v), free(got), free(ref);
+}
+
 static void gpu_checks(void) {
     int n = 0;
     HIP_OK(hipGetDeviceCount(&n));
@@ -235,6 +350,13 @@ static void gpu_checks(void) {
     const int32_t l4[4] = {1000, 33, 0, 512};
     paged_case(4, 32, 8, 128, 32, 32, l4, 0.08838834764831845f, 16);
     paged_case(4, 8, 2, 64, 16, 64, l4, 0.125f, 17);
+    const int32_t l5[5] = {3000, 1, 0, 2048, 777};
+    two_step_case(5, 32, 8, 128, 3000, l5, 0.08838834764831845f, 18);         /* even shares */
+    two_step_case(1, 24, 4, 256, 4096, l2, 0.0625f, 19);                       /* fixed splits */
+    fp8_case(3, 16, 4, 128, 700, l1, 0.08838834764831845f, 1.0f / 16, 1.0f / 16, 20);
+    fp8_case(1, 24, 4, 256, 4096, l2, 0.0625f, 1.0f / 32, 1.0f / 8, 21);
+    const int32_t l6[3] = {900, 2, 64};                                         /* len 2 < M: row 0 is zero */
+    mq_case(3, 3, 16, 4, 128, 900, l6, 0.08838834764831845f, 22);             /* M * G = 12 query rows */
     printf("gpu checks: %s\n", failures == 0 ? "ok" : "FAILED");
 }
 

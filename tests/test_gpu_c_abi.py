@@ -1,6 +1,7 @@
 """The C ABI from a plain C program (tests/c_abi/gqa_c_caller.c, built by the package build):
-hipMalloc'd buffers, gqa_decode / gqa_paged_decode / gqa_decode_noalloc on ragged cases,
-checked against the CPU oracle elementwise (|gpu - oracle| <= 2e-3 + 2e-3 |oracle|)."""
+hipMalloc'd buffers, gqa_decode / gqa_paged_decode / gqa_decode_noalloc, gqa_decode_partials +
+gqa_decode_combine, gqa_decode_fp8 and gqa_decode_mq on ragged cases, checked against the CPU
+oracle elementwise (|gpu - oracle| <= 2e-3 + 2e-3 |oracle|)."""
 from __future__ import annotations
 
 import os
