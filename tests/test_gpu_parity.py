@@ -201,6 +201,19 @@ def test_side_stream_internal_buffers():
         compare(o.cpu().numpy(), ref, "side stream, internal buffers")
 
 
+def test_binding_launches_on_the_current_stream():
+    """The binding's current-stream query (torch's raw query where the build has it) names the
+    stream torch considers current, outside and inside `torch.cuda.stream(s)`, and an explicit
+    stream wins over it."""
+    t = torch.empty(4, device="cuda")
+    s = torch.cuda.Stream()
+    assert gd._stream_ptr(None, t.device) == torch.cuda.current_stream().cuda_stream
+    with torch.cuda.stream(s):
+        assert gd._stream_ptr(None, t.device) == s.cuda_stream
+    assert gd._stream_ptr(None, t.device) == torch.cuda.current_stream().cuda_stream
+    assert gd._stream_ptr(s, t.device) == s.cuda_stream
+
+
 def test_concurrent_host_threads():
     """Four host threads call the library at once (ctypes drops the GIL for the call), each on
     its own stream with its own workspace and outputs, one plan kind per thread: the small-job
