@@ -279,6 +279,24 @@ def test_paged_matrix(ps, D):
         compare(dc.run_host(splits), ref, f"paged ps={ps} D={D} splits={splits}")
 
 
+@pytest.mark.parametrize("ps", [256, 1024, 208])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_large_pages(ps, kv):
+    """Pages far longer than a tile (many tiles per page, one page-table entry serving them all)
+    and a page size that is no power of two: ragged lengths on both sides of page boundaries,
+    fixed splits, even shares and one tile per wave."""
+    say(f"[parity] large pages ps={ps} kv={kv}")
+    lens = [1, ps - 1, ps, ps + 1, 3 * ps + 17, 0, 2 * ps - 5]
+    max_len = 4 * ps
+    pages = sum((n + ps - 1) // ps for n in lens) + 2
+    make = W.paged_case if kv == "bf16" else W.fp8_paged_case
+    case = make(len(lens), 16, 4, 128, ps, pages, seq_lens=lens, max_len=max_len, seed=ps + (kv == "fp8"))
+    dc = DeviceCase(case)
+    ref = oracle_out(case)
+    for splits in (0, 1, 7, 1000):
+        compare(dc.run_host(splits), ref, f"ps={ps} {kv} splits={splits}")
+
+
 def test_paged_equals_contiguous_bitwise(tune):
     """Pages holding the same rows as a contiguous cache give the same bits (same plan)."""
     say("[parity] paged == contiguous")
