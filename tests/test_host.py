@@ -468,3 +468,22 @@ def test_fused_plans_stay_within_the_counter_header(tune):
     assert p.partition == 0 and p.fused == 0
     p = gd.gqa_decode_plan(100, 8, 2, 128, 4096, 0, 64, 256)   # 200 x 9 = 1800 counters
     assert p.fused == 1 and p.counters == 1800
+
+
+def test_binding_sizes_a_passed_workspace_without_the_plan():
+    """A workspace the caller passes is handed on with its byte size (the library checks it
+    against the plan), without a size query; without one, the plan's size is queried, and no
+    workspace is made for a plan that needs none."""
+    import torch
+
+    def no_query():
+        raise AssertionError("size queried although a workspace was passed")
+
+    ws = torch.zeros(100, dtype=torch.float32)
+    got, n = gd._workspace(ws, no_query, torch.device("cpu"), None)
+    assert got is ws and n == 400
+    asked = []
+    got, n = gd._workspace(None, lambda: asked.append(1) or 0, torch.device("cpu"), None)
+    assert got is None and n == 0 and asked == [1]
+    got, n = gd._workspace(None, lambda: 4096, torch.device("cpu"), None)
+    assert got.dtype == torch.uint8 and n == 4096 and bool((got == 0).all())
