@@ -214,6 +214,52 @@ def test_binding_launches_on_the_current_stream():
     assert gd._stream_ptr(s, t.device) == s.cuda_stream
 
 
+def test_tuning_changed_by_another_thread_during_calls(tune):
+    """One thread replaces the process-wide tuning over and over (plan partition, fold, combine
+    kind) while another calls the library: each call copies the tuning once, so its split and
+    combine launches always follow one plan, and every result matches the oracle."""
+    import threading
+    say("[parity] tuning changed during calls")
+    case = W.contig_case(6, 32, 8, 128, 2048, seq_lens=[2048, 100, 0, 1500, 2047, 640], seed=96)
+    dc = DeviceCase(case)
+    ref = oracle_out(case)
+    variants = [dict(partition=0, fold=0), dict(partition=1, fold=0), dict(partition=2, fold=2),
+                dict(partition=1, combine=1), dict(partition=3, fold=0), dict(partition=2, fold=0)]
+    need = 0
+    for v in variants:
+        with gd.tuning(**v):
+            need = max(need, gd.gqa_decode_workspace_bytes(case.B, case.Hq, case.Hkv, case.D, case.capacity, 0, 0))
+    ws = gd.new_workspace(max(need, gd.COUNTER_BYTES))
+    base = gd.gqa_decode_get_tuning()
+    stop = threading.Event()
+    errors = []
+
+    def flip():
+        try:
+            i = 0
+            while not stop.is_set():
+                t = gd.Tuning.from_buffer_copy(base)
+                for k, val in variants[i % len(variants)].items():
+                    setattr(t, k, val)
+                gd.gqa_decode_set_tuning(t)
+                i += 1
+        except Exception as e:  # reported on the main thread
+            errors.append(repr(e))
+
+    th = threading.Thread(target=flip)
+    th.start()
+    try:
+        outs = [dc.run(0, workspace=ws) for _ in range(60)]
+        torch.cuda.synchronize()
+    finally:
+        stop.set()
+        th.join(timeout=30)
+        gd.gqa_decode_set_tuning(base)
+    assert not errors, errors
+    for o in outs:
+        compare(o.cpu().numpy(), ref, "tuning changed during calls")
+
+
 def test_concurrent_host_threads():
     """Four host threads call the library at once (ctypes drops the GIL for the call), each on
     its own stream with its own workspace and outputs, one plan kind per thread: the small-job
