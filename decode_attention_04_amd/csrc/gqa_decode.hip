@@ -58,6 +58,9 @@
 #include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <tuple>
+#include <unordered_map>
+#include <utility>
 
 #include "gqa_decode.h"
 
@@ -2002,6 +2005,51 @@ constexpr int kDefaultPieceCost = 4;
 constexpr int kDefaultSplitKeys = 2048;
 std::atomic<int> g_cu_count[kMaxDevices];
 
+// ------------------------------------------------------------------ launches
+//
+// Kernels are launched through the module API with their function handles
+// looked up once per (kernel, device): hipLaunchKernelGGL resolves the handle
+// on every launch, which costs about half a microsecond of host time per
+// launch (measured on MI355X), and a call's host time bounds callers that do
+// not replay graphs.
+std::mutex g_func_mu;
+std::unordered_map<uint64_t, hipFunction_t> g_funcs;  // key: kernel address * kMaxDevices + device
+
+hipError_t function_of(const void *kernel, hipFunction_t *f) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    const uint64_t key = (uint64_t)(uintptr_t)kernel * kMaxDevices + (uint64_t)dev;
+    std::lock_guard<std::mutex> lock(g_func_mu);
+    const auto it = g_funcs.find(key);
+    if (it != g_funcs.end()) {
+        *f = it->second;
+        return hipSuccess;
+    }
+    e = hipGetFuncBySymbol(f, kernel);
+    if (e == hipSuccess) g_funcs.emplace(key, *f);
+    return e;
+}
+
+template <typename... P, typename... A, size_t... I>
+hipError_t launch_indexed(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, std::index_sequence<I...>,
+                          A &&...args) {
+    // each argument converted to its parameter's exact type, then passed by address
+    std::tuple<std::decay_t<P>...> values(std::forward<A>(args)...);
+    void *params[] = {static_cast<void *>(&std::get<I>(values))...};
+    hipFunction_t f = nullptr;
+    const hipError_t e = function_of(reinterpret_cast<const void *>(kernel), &f);
+    if (e != hipSuccess) return e;
+    return hipModuleLaunchKernel(f, grid.x, grid.y, grid.z, block.x, block.y, block.z, 0, stream, params, nullptr);
+}
+
+template <typename... P, typename... A>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, A &&...args) {
+    static_assert(sizeof...(P) == sizeof...(A), "one value per kernel parameter");
+    return launch_indexed(kernel, grid, block, stream, std::index_sequence_for<P...>{}, std::forward<A>(args)...);
+}
+
 // ------------------------------------------------------------------ tuning
 //
 // The plan and kernel-variant choices every call makes, process-wide.  The
@@ -2194,11 +2242,10 @@ hipError_t launch_combine(const gqa_plan_t &plan, const gqa_tuning_t &t, const f
     if ((t.combine == 0 && plan.max_pieces <= kNarrowPieces) || prop) {
         const int64_t waves = (int64_t)B * ((rows * (D / 4) + 63) / 64);
         auto go = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, dim3((unsigned)waves), dim3(kNarrowThreads), 0, stream, ca.part_acc,
-                               ca.part_ml, ca.num_splits, ca.G, ca.Hq, ca.D, ca);
+            return launch(kernel, dim3((unsigned)waves), dim3(kNarrowThreads), stream, ca.part_acc, ca.part_ml,
+                          ca.num_splits, ca.G, ca.Hq, ca.D, ca);
         };
-        even ? go(gqa_combine_narrow_kernel<kPartitionEven>) : go(gqa_combine_narrow_kernel<kPartitionFixed>);
-        return hipGetLastError();
+        return even ? go(gqa_combine_narrow_kernel<kPartitionEven>) : go(gqa_combine_narrow_kernel<kPartitionFixed>);
     }
     int ncol = t.combine_cols;
     if (ncol != 2 && ncol != 4 && ncol != 8 && ncol != 16) {
@@ -2208,14 +2255,13 @@ hipError_t launch_combine(const gqa_plan_t &plan, const gqa_tuning_t &t, const f
     while (4 * ncol > D) ncol /= 2;  // a chunk never exceeds the head (head_dim 32: 8 columns)
     const unsigned grid = (unsigned)(heads * (D / (4 * ncol)));
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kCombineThreads), 0, stream, ca.part_acc, ca.part_ml,
-                           ca.num_splits, ca.G, ca.Hq, ca.D, ca);
+        return launch(kernel, dim3(grid), dim3(kCombineThreads), stream, ca.part_acc, ca.part_ml, ca.num_splits, ca.G,
+                      ca.Hq, ca.D, ca);
     };
-    if (ncol == 16) even ? go(gqa_combine_kernel<16, kPartitionEven>) : go(gqa_combine_kernel<16, kPartitionFixed>);
-    else if (ncol == 8) even ? go(gqa_combine_kernel<8, kPartitionEven>) : go(gqa_combine_kernel<8, kPartitionFixed>);
-    else if (ncol == 4) even ? go(gqa_combine_kernel<4, kPartitionEven>) : go(gqa_combine_kernel<4, kPartitionFixed>);
-    else even ? go(gqa_combine_kernel<2, kPartitionEven>) : go(gqa_combine_kernel<2, kPartitionFixed>);
-    return hipGetLastError();
+    if (ncol == 16) return even ? go(gqa_combine_kernel<16, kPartitionEven>) : go(gqa_combine_kernel<16, kPartitionFixed>);
+    if (ncol == 8) return even ? go(gqa_combine_kernel<8, kPartitionEven>) : go(gqa_combine_kernel<8, kPartitionFixed>);
+    if (ncol == 4) return even ? go(gqa_combine_kernel<4, kPartitionEven>) : go(gqa_combine_kernel<4, kPartitionFixed>);
+    return even ? go(gqa_combine_kernel<2, kPartitionEven>) : go(gqa_combine_kernel<2, kPartitionFixed>);
 }
 
 template <int D, int NB, bool PAGED>
@@ -2228,9 +2274,10 @@ hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, int kv, h
         const bool even = plan.partition == kPartitionEven || plan.partition == kPartitionProp;
         const bool nt = plan.streaming != 0;
         const int qpack = a.G | a.M << 5 | a.R << 10 | a.qdiv << 15;  // each field <= 16, qdiv <= 256
+        hipError_t err = hipErrorInvalidValue;  // stays so if no branch below launches
         auto go = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, grid, block, 0, stream, a.seq_lens, a.k, a.v, a.q, a.num_splits, a.Hkv, a.B,
-                               cap, a.split_tokens, qpack, a);
+            err = launch(kernel, grid, block, stream, a.seq_lens, a.k, a.v, a.q, a.num_splits, a.Hkv, a.B, cap,
+                         a.split_tokens, qpack, a);
         };
         if (kv == kKvFp8) {
             // The E4M3 cache always runs the default pipeline (bf16 PV, one register tile);
@@ -2265,7 +2312,7 @@ hipError_t launch_split_nb(const gqa_plan_t &plan, const SplitArgs &a, int kv, h
             even ? go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionEven, 0, kKvBf16>)
                  : go(gqa_split_kernel<D, NB, PAGED, kPvBf16, false, kPartitionFixed, 0, kKvBf16>);
         }
-        return hipGetLastError();
+        return err;
     }
 }
 
@@ -2802,8 +2849,8 @@ gqa_status_t scratch_for_device(hipStream_t stream, void **out) {
     if (g_scratch_ptr[dev] == nullptr) {
         void *ptr = nullptr;
         if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return GQA_ERR_HIP;
-        hipLaunchKernelGGL(clear_counters_kernel, dim3(1), dim3(256), 0, stream, static_cast<unsigned *>(ptr));
-        if (hipGetLastError() != hipSuccess) return GQA_ERR_HIP;
+        if (launch(clear_counters_kernel, dim3(1), dim3(256), stream, static_cast<unsigned *>(ptr)) != hipSuccess)
+            return GQA_ERR_HIP;
         g_scratch_ptr[dev] = ptr;
     }
     *out = g_scratch_ptr[dev];
