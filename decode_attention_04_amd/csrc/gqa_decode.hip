@@ -2028,7 +2028,12 @@ hipError_t function_of(const void *kernel, hipFunction_t *f) {
         return hipSuccess;
     }
     e = hipGetFuncBySymbol(f, kernel);
-    if (e == hipSuccess) g_funcs.emplace(key, *f);
+    if (e == hipSuccess) {
+        try {
+            g_funcs.emplace(key, *f);
+        } catch (...) {  // nothing throws across the C ABI; the handle is still valid
+        }
+    }
     return e;
 }
 

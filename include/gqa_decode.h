@@ -23,9 +23,10 @@
  *     aligned.  bf16 tensors are passed as raw 16-bit patterns (E4M3 caches
  *     as raw bytes, see gqa_decode_fp8).
  *   - Calls only enqueue work on `stream` (0 = the null stream): they never
- *     synchronise and never allocate.  The library keeps no state besides a
- *     cached CU count per device, the process-wide tuning (gqa_tuning_t) and
- *     the static scratch array of gqa_decode_noalloc.  Outputs are ready when
+ *     synchronise and never allocate device memory.  The library keeps no
+ *     state besides a cached CU count and the kernels' function handles per
+ *     device, the process-wide tuning (gqa_tuning_t) and the static scratch
+ *     array of gqa_decode_noalloc.  Outputs are ready when
  *     the stream reaches them.
  *   - Every argument check runs on the host before any launch; a rejected call
  *     launches nothing and returns the status below.  A failed launch returns
